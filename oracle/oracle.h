@@ -1,0 +1,83 @@
+/*
+ * Test infrastructure only: the CPU oracle for the routed-expert MoE layer with
+ * per-expert pre-activation LoRA over a frozen 4-bit fused expert stack.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header, table or helper with the HIP
+ * library; the product never calls it.
+ *
+ * Source pages: "How do I QLoRA-train the fused experts of a MoE" (solution
+ * page, sections "The abstraction that fails, and what replaces it" and "Why it
+ * happens"), and the experts4bit-qlora package README ("The package family").
+ *
+ * Precision: dequantised weights follow the fp32 contract exactly (one fp32
+ * multiply of the code value by its block scale); every other quantity of the
+ * layer (products, sums, activation, gradients) is computed in fp64 and
+ * returned unrounded.
+ */
+#ifndef E4B_ORACLE_H
+#define E4B_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_FMT_NF4 = 0, ORC_FMT_NF4_DQ = 1, ORC_FMT_MXFP4 = 2 };
+
+/* One 4-bit expert stack [E, N, K], K contiguous, as bytes + scales. */
+typedef struct {
+  int32_t fmt;
+  int32_t E, N, K;
+  const uint8_t *codes;   /* [E*N*K/2] */
+  const void *scale;      /* NF4: float[E*N*K/64]; NF4_DQ: uint8[E*N*K/64]; MXFP4: uint8[E*N*K/32] */
+  const float *scale2;    /* NF4_DQ: float[ceil(E*N*K/64/256)]; else unused */
+} orc_qweight;
+
+/* The layer: weights either packed (w_gu/w_dn) or dense fp32 (W1f/W2f, for
+ * identities that need weights outside the 4-bit grid). */
+typedef struct {
+  int32_t E, H, I, T, k;
+  const orc_qweight *w_gu;  /* gate_up_proj [E, 2I, H] */
+  const orc_qweight *w_dn;  /* down_proj    [E, H, I]  */
+  const float *W1f;         /* optional dense [E, 2I, H] (overrides w_gu) */
+  const float *W2f;         /* optional dense [E, H, I]  (overrides w_dn) */
+  const uint16_t *A1, *B1;  /* bf16 [E, r1, H], [E, 2I, r1]; A1 == NULL: no adapter */
+  int32_t r1; double s1;
+  const uint16_t *A2, *B2;  /* bf16 [E, r2, I], [E, H, r2]; A2 == NULL: no adapter */
+  int32_t r2; double s2;
+  const uint16_t *x;        /* bf16 [T, H] */
+  const int32_t *ids;       /* [T, k] */
+  const float *topw;        /* [T, k] */
+  int32_t post_act_delta;   /* test hook: 1 = act(Wx) + delta instead of act(Wx + delta) */
+} orc_layer;
+
+int32_t orc_version(void);
+void orc_nf4_codebook(float out[16]);
+void orc_bf16_round(const float *in, uint16_t *out, int64_t n);
+
+void orc_quant_nf4(const float *w, int64_t n, uint8_t *codes, float *absmax);
+void orc_quant_nf4_dq(const float *w, int64_t n, uint8_t *codes, uint8_t *qabsmax, float *scale2);
+void orc_quant_mxfp4(const float *w, int64_t n, uint8_t *codes, uint8_t *scales);
+/* Dequantise n elements (flat) to fp32 and/or bf16 (either pointer may be NULL). */
+void orc_dequant(int32_t fmt, int64_t n, const uint8_t *codes, const void *scale,
+                 const float *scale2, float *out_f32, uint16_t *out_bf16);
+
+void orc_route(int32_t T, int32_t k, int32_t E, const int32_t *ids,
+               int32_t *cnt, int32_t *off, int32_t *perm, int32_t *inv);
+
+/* Forward.  tok_mask[T] (NULL = all tokens) selects the tokens whose rows are
+ * computed.  y: fp64 [T, H] (unselected tokens get 0).  O (nullable): fp64
+ * per-routed-row expert outputs [T*k, H] in flat (t*k+j) order. Returns 0. */
+int32_t orc_moe_fwd(const orc_layer *L, const uint8_t *tok_mask, double *y, double *O);
+
+/* Backward of sum(dy * y) with the routing held fixed.  dy: bf16 [T, H]; only
+ * masked tokens contribute.  Outputs (any nullable except dx): dx [T, H],
+ * dw [T, k], dA1 [E, r1, H], dB1 [E, 2I, r1], dA2 [E, r2, I], dB2 [E, H, r2]. */
+int32_t orc_moe_bwd(const orc_layer *L, const uint8_t *tok_mask, const uint16_t *dy,
+                    double *dx, double *dw, double *dA1, double *dB1, double *dA2, double *dB2);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,444 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a published
+construction, a closed form evaluated by a library routine, brute force on small
+inputs, an exact special case, or finite differences.  A plausible mistake in the
+oracle (a dropped LoRA term, a wrong scaling, a swapped gate/up half, a transposed
+operand, a wrong nibble order) fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------- NF4 table
+
+def test_codebook_matches_published_table(orc):
+    lit = np.loadtxt(os.path.join(GOLD, "nf4_codebook.txt"), dtype=np.float64)
+    assert np.array_equal(orc.codebook().astype(np.float64), lit.astype(np.float32).astype(np.float64))
+
+
+def test_codebook_matches_quantile_construction(orc):
+    """NF4 = normalised quantiles of N(0,1): 8 positive levels from an even split of
+    [offset, 0.5], 7 negative ones, plus an exact zero (QLoRA paper, NF4 section)."""
+    from scipy.stats import norm
+
+    offset = 1.0 - 0.5 * (1.0 / 32 + 1.0 / 30)
+    pos = norm.ppf(np.linspace(offset, 0.5, 9)[:-1])
+    neg = -norm.ppf(np.linspace(offset, 0.5, 8)[:-1])
+    v = np.sort(np.concatenate([pos, [0.0], neg]))
+    v /= v.max()
+    cb = orc.codebook().astype(np.float64)
+    assert np.abs(cb - v).max() < 5e-7
+
+
+def test_codebook_invariants(orc):
+    cb = orc.codebook()
+    assert np.all(np.diff(cb) > 0)
+    assert cb[0] == -1.0 and cb[7] == 0.0 and cb[15] == 1.0
+    assert (cb < 0).sum() == 7 and (cb > 0).sum() == 8
+
+
+# ----------------------------------------------------------------------------- bf16
+
+def test_bf16_rounding_matches_torch(orc):
+    rng = np.random.default_rng(0)
+    a = rng.standard_normal(100000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 100000)
+    # exact ties: low 16 bits 0x8000 with even and odd kept bits
+    hi = rng.integers(0, 0x7F7F, 2000).astype(np.uint32) | (rng.integers(0, 2, 2000).astype(np.uint32) << 15)
+    ties = (hi << 16 | 0x8000).view(np.float32)  # finite values only: NaN payloads are not compared
+    a = np.concatenate([a.astype(np.float32), ties, np.float32([0.0, -0.0, np.inf, -np.inf, 3.4e38, 1e-45])])
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.bf16_round(a), ref)
+
+
+# ----------------------------------------------------------------------------- NF4 quant/dequant
+
+def _blocks(rng, nblk, scale=0.02):
+    return (rng.standard_normal((1, nblk, 64)) * scale).astype(np.float32)
+
+
+def test_nf4_roundtrip_exact_codes(orc):
+    """A block holding +-a and every code value times a quantises back to those codes."""
+    cb = orc.codebook()
+    rng = np.random.default_rng(1)
+    for a in rng.uniform(1e-4, 10.0, 50).astype(np.float32):
+        idx = rng.integers(0, 16, 64)
+        idx[0] = 15  # guarantees absmax == a
+        w = (cb[idx] * a).astype(np.float32).reshape(1, 1, 64)
+        q = orc.quantize("nf4", w)
+        assert q.scale[0] == a
+        hi, lo = q.codes >> 4, q.codes & 15
+        got = np.stack([hi, lo], axis=1).ravel()
+        assert np.array_equal(got, idx)
+
+
+def test_nf4_quant_bruteforce(orc):
+    rng = np.random.default_rng(2)
+    w = _blocks(rng, 300)
+    w[0, 5] = 0.0  # an all-zero block
+    q = orc.quantize("nf4", w)
+    cb = orc.codebook()
+    blocks = w.reshape(-1, 64)
+    amax = np.abs(blocks).max(axis=1)
+    assert np.array_equal(q.scale, amax)
+    for b in range(blocks.shape[0]):
+        if amax[b] == 0:
+            want = np.full(64, 7)
+        else:
+            v = (blocks[b] / amax[b]).astype(np.float32)
+            want = np.argmin(np.abs(v[:, None] - cb[None, :]).astype(np.float32), axis=1)
+        byte = q.codes[b * 32:(b + 1) * 32]
+        got = np.stack([byte >> 4, byte & 15], axis=1).ravel()  # element 2j -> high nibble
+        assert np.array_equal(got, want), b
+
+
+def test_nf4_dequant_closed_form(orc):
+    """w = fp32(code) * absmax in one fp32 multiply; bf16 by round-to-nearest-even."""
+    rng = np.random.default_rng(3)
+    E, N, K = 2, 8, 128
+    codes = rng.integers(0, 256, E * N * K // 2).astype(np.uint8)
+    absmax = rng.uniform(0, 1, E * N * K // 64).astype(np.float32)
+    q = orc.QWeight("nf4", E, N, K, codes, absmax)
+    f32, b16 = orc.dequant(q)
+    cb = np.loadtxt(os.path.join(GOLD, "nf4_codebook.txt")).astype(np.float32)
+    nib = np.stack([codes >> 4, codes & 15], axis=1).ravel()
+    want = cb[nib] * np.repeat(absmax, 64)
+    assert want.dtype == np.float32
+    assert np.array_equal(f32.ravel().view(np.uint32), want.view(np.uint32))
+    ref16 = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16.ravel(), ref16)
+
+
+def test_nf4_dq_scheme(orc):
+    rng = np.random.default_rng(4)
+    w = (rng.standard_normal((3, 64, 192)) * 0.02).astype(np.float32)  # 576 blocks: 3 groups, ragged tail
+    w[1, :4] *= 7.0
+    q = orc.quantize("nf4_dq", w)
+    codes_p, amax = orc.quantize_flat_nf4(w)
+    assert np.array_equal(q.codes, codes_p)  # 4-bit codes use the undoubled absmax
+    nb = amax.size
+    groups = [amax[g * 256:(g + 1) * 256] for g in range((nb + 255) // 256)]
+    assert np.array_equal(q.scale2, np.array([g.max() for g in groups], np.float32))
+    s2 = np.repeat(q.scale2, 256)[:nb]
+    rec = (q.scale.astype(np.float32) / np.float32(255.0)).astype(np.float32) * s2
+    assert np.all(np.abs(rec - amax) <= s2 / 510.0 * (1 + 1e-6))
+    f32, b16 = orc.dequant(q)
+    cb = orc.codebook()
+    nib = np.stack([q.codes >> 4, q.codes & 15], axis=1).ravel()
+    want = cb[nib] * np.repeat(rec.astype(np.float32), 64)
+    assert np.array_equal(f32.ravel().view(np.uint32), want.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------- MXFP4
+
+E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+
+
+def test_mxfp4_dequant_closed_form(orc):
+    rng = np.random.default_rng(5)
+    E, N, K = 1, 4, 256
+    codes = rng.integers(0, 256, E * N * K // 2).astype(np.uint8)
+    scales = rng.integers(100, 150, E * N * K // 32).astype(np.uint8)
+    q = orc.QWeight("mxfp4", E, N, K, codes, scales)
+    f32, _ = orc.dequant(q)
+    nib = np.stack([codes & 15, codes >> 4], axis=1).ravel()  # element 2j -> low nibble
+    mag = E2M1[nib & 7] * np.where(nib & 8, -1.0, 1.0).astype(np.float32)
+    want = np.ldexp(mag, np.repeat(scales.astype(np.int32) - 127, 32)).astype(np.float32)
+    assert np.array_equal(f32.ravel(), want)
+
+
+def test_mxfp4_quant_bruteforce(orc):
+    rng = np.random.default_rng(6)
+    w = (rng.standard_normal((1, 40, 64)) * 0.02).astype(np.float32)
+    w[0, 0, :32] = 0.0
+    q = orc.quantize("mxfp4", w)
+    blocks = w.reshape(-1, 32)
+    for b, blk in enumerate(blocks):
+        amax = np.abs(blk).max()
+        if amax == 0:
+            assert q.scale[b] == 0
+            continue
+        e = int(np.floor(np.log2(np.float64(amax)))) - 2
+        assert q.scale[b] == e + 127
+        v = np.abs(blk.astype(np.float64)) / 2.0 ** e
+        d = np.abs(v[:, None] - E2M1[None, :].astype(np.float64))
+        best = np.argmin(d, axis=1)
+        # ties -> even code
+        for i in range(32):
+            cand = np.nonzero(d[i] == d[i].min())[0]
+            if cand.size > 1:
+                best[i] = cand[cand % 2 == 0][0]
+        best = np.where(v >= 6.0, 7, best)
+        sign = np.where((blk < 0) & (best != 0), 8, 0)
+        want = best + sign
+        byte = q.codes[b * 16:(b + 1) * 16]
+        got = np.stack([byte & 15, byte >> 4], axis=1).ravel()
+        assert np.array_equal(got, want), b
+
+
+def test_mxfp4_roundtrip_representable(orc):
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        e = int(rng.integers(-12, 4))
+        idx = rng.integers(0, 16, 32)
+        idx[3] = 7  # magnitude 6 sets the shared exponent to e
+        mag = E2M1[idx & 7] * np.where(idx & 8, -1.0, 1.0)
+        w = np.ldexp(mag, e).astype(np.float32).reshape(1, 1, 32)
+        q = orc.quantize("mxfp4", w)
+        f32, _ = orc.dequant(q)
+        assert np.array_equal(f32.ravel(), w.ravel())
+
+
+# ----------------------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("T,k,E", [(0, 2, 4), (1, 2, 8), (37, 3, 5), (200, 8, 128), (64, 1, 1)])
+def test_route_bruteforce(orc, T, k, E):
+    rng = np.random.default_rng(T * 31 + E)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    if T > 3:
+        ids[2, 0] = E + 3  # out of range: dropped
+        ids[3, -1] = -1
+    cnt, off, perm, inv = orc.route(ids, E)
+    flat = ids.ravel().tolist()
+    valid = [f for f in range(T * k) if 0 <= flat[f] < E]
+    order = sorted(valid, key=lambda f: flat[f])  # Python's sort is stable
+    assert perm[:len(order)].tolist() == order
+    assert np.all(perm[len(order):] == -1)
+    assert cnt[:E].tolist() == [flat.count(e) for e in range(E)]
+    assert cnt[E] == T * k - len(valid)
+    assert off.tolist() == [0] + np.cumsum(cnt[:E]).tolist()
+    for p, f in enumerate(order):
+        assert inv[f] == p
+    assert all(inv[f] == -1 for f in range(T * k) if f not in set(valid))
+
+
+# ----------------------------------------------------------------------------- forward
+
+def _small(E=3, H=64, I=64, T=12, k=2, r=4, alpha=8.0, fmt="nf4", seed=11, zero_B=False):
+    s = synth.custom(E, H, I, T, k, r, alpha, fmt)
+    return synth.make_inputs(s, seed=seed, zero_B=zero_B)
+
+
+def _f64(bits):
+    return synth.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _dense_reformulation(inp, W1, W2, lora=True):
+    """All experts for all tokens with dense fp64 torch matmuls, then a one-hot combine."""
+    s = inp.shape
+    X = torch.from_numpy(_f64(inp.x))
+    Y = torch.zeros(s.T, s.H, dtype=torch.float64)
+    C = torch.zeros(s.T, s.E, dtype=torch.float64)
+    for j in range(s.k):
+        C[torch.arange(s.T), torch.from_numpy(inp.ids[:, j].astype(np.int64))] += torch.from_numpy(
+            inp.topw[:, j].astype(np.float64))
+    for e in range(s.E):
+        w1 = torch.from_numpy(W1[e].astype(np.float64))
+        w2 = torch.from_numpy(W2[e].astype(np.float64))
+        G = X @ w1.T
+        if lora:
+            A1, B1 = torch.from_numpy(_f64(inp.A1[e])), torch.from_numpy(_f64(inp.B1[e]))
+            G = G + s.scaling * (X @ A1.T) @ B1.T
+        h = torch.nn.functional.silu(G[:, :s.I]) * G[:, s.I:]
+        o = h @ w2.T
+        if lora:
+            A2, B2 = torch.from_numpy(_f64(inp.A2[e])), torch.from_numpy(_f64(inp.B2[e]))
+            o = o + s.scaling * (h @ A2.T) @ B2.T
+        Y += C[:, e:e + 1] * o
+    return Y.numpy()
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+def test_forward_matches_dense_onehot(orc, fmt):
+    inp = _small(fmt=fmt)
+    q1, q2 = orc.quantize(fmt, inp.W1), orc.quantize(fmt, inp.W2)
+    y = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2))
+    W1, _ = orc.dequant(q1, want_bf16=False)
+    W2, _ = orc.dequant(q2, want_bf16=False)
+    ref = _dense_reformulation(inp, W1, W2)
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_forward_textbook_swiglu(orc):
+    """E=1, k=1, w=1, no adapter: y = W2 (silu(W_gate x) * (W_up x))."""
+    s = synth.custom(1, 64, 128, 5, 1, 4, 8.0)
+    inp = synth.make_inputs(s, seed=3)
+    inp.topw[:] = 1.0
+    y = orc.moe_fwd(orc.layer_from_inputs(inp, dense=True, lora=False))
+    X = torch.from_numpy(_f64(inp.x))
+    w1 = torch.from_numpy(inp.W1[0].astype(np.float64))
+    w2 = torch.from_numpy(inp.W2[0].astype(np.float64))
+    mlp = (torch.nn.functional.silu(X @ w1[:128].T) * (X @ w1[128:].T)) @ w2.T
+    assert np.abs(y - mlp.numpy()).max() <= 1e-12 * np.abs(mlp.numpy()).max()
+
+
+def test_zero_B_is_exactly_base(orc):
+    """B zero-initialised: the delta starts at exactly zero (solution page, component table)."""
+    inp = _small(zero_B=True)
+    q1, q2 = orc.quantize("nf4", inp.W1), orc.quantize("nf4", inp.W2)
+    y_lora = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2, lora=True))
+    y_base = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2, lora=False))
+    assert np.array_equal(y_lora, y_base)
+    g_lora = orc.moe_bwd(orc.layer_from_inputs(inp, q1, q2, lora=True), inp.dy)
+    g_base = orc.moe_bwd(orc.layer_from_inputs(inp, q1, q2, lora=False), inp.dy)
+    assert np.array_equal(g_lora["dx"], g_base["dx"])
+    assert np.all(g_lora["dA1"] == 0) and np.all(g_lora["dA2"] == 0)
+    assert np.abs(g_lora["dB1"]).max() > 0 and np.abs(g_lora["dB2"]).max() > 0
+
+
+def test_lora_merge_identity(orc):
+    """act((W + s B A) x) == act(W x + s B (A x)): the adapter equals a merged weight."""
+    inp = _small(T=9, r=8, alpha=16.0)
+    rng = np.random.default_rng(9)
+    inp.B1[:] = synth.to_bf16_bits(rng.normal(0, 0.1, inp.B1.shape).astype(np.float32))
+    inp.B2[:] = synth.to_bf16_bits(rng.normal(0, 0.1, inp.B2.shape).astype(np.float32))
+    s = inp.shape
+    y = orc.moe_fwd(orc.layer_from_inputs(inp, dense=True))
+    W1m = inp.W1.astype(np.float64) + s.scaling * np.einsum("enr,erh->enh", _f64(inp.B1), _f64(inp.A1))
+    W2m = inp.W2.astype(np.float64) + s.scaling * np.einsum("enr,eri->eni", _f64(inp.B2), _f64(inp.A2))
+    ref = _dense_reformulation(inp, W1m, W2m, lora=False)
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_pre_activation_delta_is_distinguishable(orc):
+    """act(W x + B A x) is not act(W x) + d: a planted post-activation delta must fail the
+    bf16 parity gate (max <= 2e-2 max|ref|, relative L1 <= 5e-3) on the tiny workload."""
+    inp = synth.make_inputs(synth.WORKLOADS["tiny"])
+    q1, q2 = orc.quantize("nf4", inp.W1), orc.quantize("nf4", inp.W2)
+    good = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2))
+    bad = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2, post_act_delta=True))
+    rel_l1 = np.abs(bad - good).sum() / np.abs(good).sum()
+    rel_max = np.abs(bad - good).max() / np.abs(good).max()
+    assert rel_l1 > 5e-3 * 4 or rel_max > 2e-2 * 4
+
+
+def test_combine_order_k2_is_bitwise(orc):
+    inp = _small(k=2)
+    q1, q2 = orc.quantize("nf4", inp.W1), orc.quantize("nf4", inp.W2)
+    y = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2))
+    inp.ids[:] = inp.ids[:, ::-1].copy()
+    inp.topw[:] = inp.topw[:, ::-1].copy()
+    y2 = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2))
+    assert np.array_equal(y, y2)
+
+
+def test_duplicate_and_invalid_ids(orc):
+    inp = _small(E=3, k=2, T=6)
+    inp.ids[0] = [1, 1]          # duplicate: two separate routed rows
+    inp.ids[1] = [2, 7]          # out of range: row dropped
+    q1, q2 = orc.quantize("nf4", inp.W1), orc.quantize("nf4", inp.W2)
+    y, O = orc.moe_fwd(orc.layer_from_inputs(inp, q1, q2), want_O=True)
+    assert np.allclose(y[0], (float(inp.topw[0, 0]) + float(inp.topw[0, 1])) * O[0], rtol=1e-12, atol=0)
+    assert np.array_equal(O[0], O[1])
+    assert np.array_equal(y[1], inp.topw[1, 0] * O[2])
+    assert np.all(O[3] == 0)
+
+
+def test_token_mask_selects_rows(orc):
+    inp = _small(T=10)
+    q1, q2 = orc.quantize("nf4", inp.W1), orc.quantize("nf4", inp.W2)
+    L = orc.layer_from_inputs(inp, q1, q2)
+    full = orc.moe_fwd(L)
+    sub = orc.moe_fwd(L, tokens=[1, 4, 7])
+    assert np.array_equal(sub[[1, 4, 7]], full[[1, 4, 7]])
+    assert np.all(sub[[0, 2, 3, 5, 6, 8, 9]] == 0)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _loss(orc, inp, dy64, **kw):
+    y = orc.moe_fwd(orc.layer_from_inputs(inp, dense=True, **kw))
+    return float((y * dy64).sum())
+
+
+def _bf16_neighbours(bits):
+    up = synth.bf16_bits_to_f32(np.uint16(bits + 1))
+    dn = synth.bf16_bits_to_f32(np.uint16(bits - 1))
+    return np.uint16(bits + 1), np.uint16(bits - 1), float(up) - float(dn)
+
+
+def test_backward_finite_differences(orc):
+    """Central differences over one-ulp bf16 steps (x, A1, B1: nonlinear) and exact
+    differences (top-k weight, B2, A2: the loss is linear in them)."""
+    inp = _small(E=2, H=64, I=64, T=6, k=2, r=4, alpha=8.0, seed=21)
+    rng = np.random.default_rng(21)
+    inp.B1[:] = synth.to_bf16_bits(rng.normal(0, 0.2, inp.B1.shape).astype(np.float32))
+    inp.B2[:] = synth.to_bf16_bits(rng.normal(0, 0.2, inp.B2.shape).astype(np.float32))
+    inp.W1 *= 5.0  # stronger gate nonlinearity
+    dy64 = _f64(inp.dy)
+    g = orc.moe_bwd(orc.layer_from_inputs(inp, dense=True), inp.dy)
+
+    def central(arr, idx):
+        keep = arr[idx]
+        up, dn, step = _bf16_neighbours(keep)
+        arr[idx] = up
+        lp = _loss(orc, inp, dy64)
+        arr[idx] = dn
+        lm = _loss(orc, inp, dy64)
+        arr[idx] = keep
+        return (lp - lm) / step
+
+    scale = {k: np.abs(v).max() for k, v in g.items() if v is not None}
+    for idx in [(0, 3), (4, 10), (5, 63)]:
+        assert abs(central(inp.x, idx) - g["dx"][idx]) <= 2e-3 * scale["dx"]
+    for idx in [(0, 1, 5), (1, 3, 60)]:
+        assert abs(central(inp.A1, idx) - g["dA1"][idx]) <= 2e-3 * scale["dA1"]
+    for idx in [(0, 7, 2), (1, 100, 0), (0, 70, 3)]:
+        assert abs(central(inp.B1, idx) - g["dB1"][idx]) <= 2e-3 * scale["dB1"]
+    # exact differences where the loss is linear
+    base = _loss(orc, inp, dy64)
+    for (t, j) in [(0, 0), (3, 1)]:
+        keep = inp.topw[t, j]
+        inp.topw[t, j] = keep + np.float32(0.25)
+        d = (_loss(orc, inp, dy64) - base) / float(np.float32(keep + np.float32(0.25)) - keep)
+        inp.topw[t, j] = keep
+        assert abs(d - g["dw"][t, j]) <= 1e-9 * max(1.0, abs(d))
+    for name, idxs in [("B2", [(0, 1, 2), (1, 5, 3)]), ("A2", [(0, 1, 2), (1, 3, 50)])]:
+        arr = getattr(inp, name)
+        for idx in idxs:
+            keep = arr[idx]
+            arr[idx] = synth.to_bf16_bits(np.float32([synth.bf16_bits_to_f32(keep) + 0.5]))[0]
+            step = float(synth.bf16_bits_to_f32(arr[idx])) - float(synth.bf16_bits_to_f32(keep))
+            d = (_loss(orc, inp, dy64) - base) / step
+            arr[idx] = keep
+            assert abs(d - g["d" + name][idx]) <= 1e-8 * max(1.0, np.abs(g["d" + name]).max())
+
+
+def test_backward_adjoint_in_B2(orc):
+    """The loss is linear in B2: L(V) - L(0) = <dL/dB2, V> for any V."""
+    inp = _small(E=2, T=8, seed=5)
+    dy64 = _f64(inp.dy)
+    rng = np.random.default_rng(5)
+    V = synth.to_bf16_bits(rng.normal(0, 0.3, inp.B2.shape).astype(np.float32))
+    inp.B2[:] = 0
+    l0 = _loss(orc, inp, dy64)
+    g = orc.moe_bwd(orc.layer_from_inputs(inp, dense=True), inp.dy)
+    inp.B2[:] = V
+    l1 = _loss(orc, inp, dy64)
+    lhs = l1 - l0
+    rhs = float((g["dB2"] * _f64(V)).sum())
+    assert abs(lhs - rhs) <= 1e-10 * abs(rhs)
+
+
+def test_backward_mask_equals_zeroed_dy(orc):
+    """Gradients of a token subset equal full gradients with dy zeroed elsewhere."""
+    inp = _small(T=10, seed=8)
+    q1, q2 = orc.quantize("nf4", inp.W1), orc.quantize("nf4", inp.W2)
+    L = orc.layer_from_inputs(inp, q1, q2)
+    toks = [0, 3, 9]
+    dyz = inp.dy.copy()
+    keep = np.zeros(10, bool)
+    keep[toks] = True
+    dyz[~keep] = 0
+    a = orc.moe_bwd(L, dyz)
+    b = orc.moe_bwd(L, inp.dy, tokens=toks)
+    for k in ["dA1", "dB1", "dA2", "dB2"]:
+        assert np.allclose(a[k], b[k], rtol=1e-12, atol=1e-300)
+    assert np.array_equal(a["dx"][toks], b["dx"][toks])
