@@ -1,0 +1,488 @@
+// C ABI of libe4b: argument validation, workspace layout, the three layer calls
+// (forward, input gradient, LoRA weight gradients) as stream-ordered kernel
+// sequences, and the verification / observability exports.
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "e4b.h"
+#include "kernels.hpp"
+
+namespace e4b {
+
+// ------------------------------------------------------------------ launch bookkeeping
+static std::atomic<int64_t> g_count[FAM_COUNT];
+static std::atomic<int64_t> g_total{0};
+static std::mutex g_tmu;
+static bool g_timing = false;
+struct TimedLaunch {
+  hipEvent_t a, b;
+  int fam;
+};
+static std::vector<TimedLaunch> g_pending;
+static int64_t g_tl[FAM_COUNT];
+static double g_tms[FAM_COUNT];
+
+const char *family_name(int f) {
+  static const char *names[FAM_COUNT] = {"route",          "lora_a",       "gemm_gate_up",
+                                         "gemm_down",      "combine",      "combine_bwd",
+                                         "gemm_down_dgrad", "gemm_gate_up_dgrad", "unpermute",
+                                         "wgrad",          "quant",        "dequant",
+                                         "transpose"};
+  return (f >= 0 && f < FAM_COUNT) ? names[f] : "?";
+}
+
+LaunchScope::LaunchScope(int f, hipStream_t st) : fam(f), s(st), slot(-1) {
+  g_count[f]++;
+  g_total++;
+  if (g_timing) {
+    TimedLaunch t{};
+    t.fam = f;
+    if (hipEventCreate(&t.a) == hipSuccess && hipEventCreate(&t.b) == hipSuccess &&
+        hipEventRecord(t.a, s) == hipSuccess) {
+      std::lock_guard<std::mutex> lk(g_tmu);
+      slot = (int)g_pending.size();
+      g_pending.push_back(t);
+    }
+  }
+}
+
+LaunchScope::~LaunchScope() {
+  if (slot >= 0) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    (void)hipEventRecord(g_pending[slot].b, s);
+  }
+}
+
+bool last_launch_ok() { return hipGetLastError() == hipSuccess; }
+
+// ------------------------------------------------------------------ workspace layout
+struct Layout {
+  size_t cnt, off, perm, inv, z1, z2, G, h, O, dO, u2, dG, u1, dXp, A1T, B1T, A2T, B2T, total;
+};
+static constexpr size_t NONE = ~(size_t)0;
+
+static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
+  Layout L;
+  const size_t M = (size_t)d.T * d.topk, E = d.E, H = d.H, I = d.I;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = (o + bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  const bool train = d.flags & E4B_TRAIN;
+  L.cnt = take((E + 1) * 4);
+  L.off = take((E + 1) * 4);
+  L.perm = take(M * 4);
+  L.inv = take(M * 4);
+  L.z1 = take(M * r1 * 2);
+  L.z2 = take(M * r2 * 2);
+  L.G = train ? take(M * 2 * I * 2) : NONE;
+  L.h = take(M * I * 2);
+  L.O = take(M * H * 4);
+  if (train) {
+    L.dO = take(M * H * 2);
+    L.u2 = take(M * r2 * 2);
+    L.dG = take(M * 2 * I * 2);
+    L.u1 = take(M * r1 * 2);
+    L.dXp = take(M * H * 4);
+    L.A1T = take(E * H * r1 * 2);
+    L.B1T = take(E * r1 * 2 * I * 2);
+    L.A2T = take(E * I * r2 * 2);
+    L.B2T = take(E * r2 * H * 2);
+  } else {
+    L.dO = L.u2 = L.dG = L.u1 = L.dXp = L.A1T = L.B1T = L.A2T = L.B2T = NONE;
+  }
+  L.total = o;
+  return L;
+}
+
+template <class T>
+static T *at(void *ws, size_t off) {
+  return (T *)((char *)ws + off);
+}
+
+// ------------------------------------------------------------------ validation
+static e4b_status check_desc(const e4b_moe_desc *d) {
+  if (!d) return E4B_ERR_INVALID_ARG;
+  if (d->E < 1 || d->E > 1024 || d->topk < 1 || d->topk > d->E || d->T < 0) return E4B_ERR_INVALID_ARG;
+  if (d->H <= 0 || d->I <= 0 || d->H % 64 || d->I % 64) return E4B_ERR_INVALID_ARG;
+  if ((int64_t)d->T * d->topk > (int64_t)1 << 30) return E4B_ERR_INVALID_ARG;
+  if ((int64_t)d->T * d->topk * 2 * d->I >= ((int64_t)1 << 40)) return E4B_ERR_INVALID_ARG;
+  if (d->flags & ~E4B_TRAIN) return E4B_ERR_INVALID_ARG;
+  return E4B_OK;
+}
+
+static e4b_status check_lora(const e4b_lora *l, int *r) {
+  *r = 0;
+  if (!l || !l->A) return (l && l->B) ? E4B_ERR_INVALID_ARG : E4B_OK;
+  if (!l->B) return E4B_ERR_INVALID_ARG;
+  if (l->r < 8 || l->r > 128 || l->r % 8) return E4B_ERR_INVALID_ARG;
+  if (!(l->scaling == l->scaling)) return E4B_ERR_INVALID_ARG;
+  *r = l->r;
+  return E4B_OK;
+}
+
+static e4b_status check_q(const e4b_qweight *q, int E, int N, int K) {
+  if (!q || !q->codes || !q->scale) return E4B_ERR_INVALID_ARG;
+  if (q->fmt < E4B_FMT_NF4 || q->fmt > E4B_FMT_MXFP4) return E4B_ERR_UNSUPPORTED;
+  if (q->fmt == E4B_FMT_NF4_DQ && !q->scale2) return E4B_ERR_INVALID_ARG;
+  if (q->E != E || q->N != N || q->K != K) return E4B_ERR_INVALID_ARG;
+  return E4B_OK;
+}
+
+static QStack qstack(const e4b_qweight *q) {
+  QStack s;
+  s.codes = q->codes;
+  s.scale = q->scale;
+  s.scale2 = q->scale2;
+  s.fmt = q->fmt;
+  s.N = q->N;
+  s.K = q->K;
+  return s;
+}
+
+#define E4B_TRY(x)                       \
+  do {                                   \
+    e4b_status st_ = (x);                \
+    if (st_ != E4B_OK) return st_;       \
+  } while (0)
+#define E4B_LAUNCH(x)                    \
+  do {                                   \
+    if (!(x)) return E4B_ERR_HIP;        \
+  } while (0)
+
+}  // namespace e4b
+
+using namespace e4b;
+
+extern "C" {
+
+int32_t e4b_version(void) { return 100; }
+
+const char *e4b_status_str(int32_t s) {
+  switch (s) {
+    case E4B_OK: return "ok";
+    case E4B_ERR_INVALID_ARG: return "invalid argument";
+    case E4B_ERR_UNSUPPORTED: return "unsupported format";
+    case E4B_ERR_WORKSPACE: return "workspace too small";
+    case E4B_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+e4b_status e4b_moe_workspace_size(const e4b_moe_desc *desc, const e4b_lora *l_gu,
+                                  const e4b_lora *l_dn, size_t *bytes) {
+  int r1, r2;
+  E4B_TRY(check_desc(desc));
+  E4B_TRY(check_lora(l_gu, &r1));
+  E4B_TRY(check_lora(l_dn, &r2));
+  if (!bytes) return E4B_ERR_INVALID_ARG;
+  *bytes = layout(*desc, r1, r2).total;
+  return E4B_OK;
+}
+
+static e4b_status validate_layer(const e4b_moe_desc *d, const e4b_qweight *w_gu,
+                                 const e4b_qweight *w_dn, const e4b_lora *l_gu,
+                                 const e4b_lora *l_dn, int *r1, int *r2) {
+  E4B_TRY(check_desc(d));
+  E4B_TRY(check_q(w_gu, d->E, 2 * d->I, d->H));
+  E4B_TRY(check_q(w_dn, d->E, d->H, d->I));
+  if (w_gu->fmt != w_dn->fmt) return E4B_ERR_UNSUPPORTED;
+  E4B_TRY(check_lora(l_gu, r1));
+  E4B_TRY(check_lora(l_dn, r2));
+  return E4B_OK;
+}
+
+e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
+                       const e4b_lora *l_gu, const e4b_lora *l_dn, const uint16_t *x,
+                       const int32_t *ids, const float *topw, uint16_t *y, void *ws,
+                       size_t ws_bytes, void *stream) {
+  int r1, r2;
+  E4B_TRY(validate_layer(desc, w_gu, w_dn, l_gu, l_dn, &r1, &r2));
+  const e4b_moe_desc &d = *desc;
+  const Layout L = layout(d, r1, r2);
+  if (!ws || ws_bytes < L.total) return E4B_ERR_WORKSPACE;
+  if (d.T > 0 && (!x || !ids || !topw || !y)) return E4B_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int M = d.T * d.topk, E = d.E, H = d.H, I = d.I;
+  int32_t *cnt = at<int32_t>(ws, L.cnt), *off = at<int32_t>(ws, L.off);
+  int32_t *perm = at<int32_t>(ws, L.perm), *inv = at<int32_t>(ws, L.inv);
+  uint16_t *z1 = at<uint16_t>(ws, L.z1), *z2 = at<uint16_t>(ws, L.z2), *h = at<uint16_t>(ws, L.h);
+  float *O = at<float>(ws, L.O);
+  uint16_t *G = L.G == NONE ? nullptr : at<uint16_t>(ws, L.G);
+
+  E4B_LAUNCH(launch_route(ids, M, E, cnt, off, perm, inv, s));
+  if (M == 0) return E4B_OK;
+
+  if (r1) {  // z1 = s1 * A1[e] x
+    GroupedArgs a{};
+    a.off = off; a.E = E; a.M = M; a.N = r1; a.K = H;
+    a.A = x; a.lda = H; a.a_gather = perm; a.a_gdiv = d.topk;
+    a.Bd = l_gu->A; a.b_estride = (int64_t)r1 * H; a.ldb = H;
+    a.C = z1; a.ldc = r1; a.alpha = l_gu->scaling;
+    E4B_LAUNCH(launch_lora_a(a, s));
+  }
+  {  // h = silu(G_gate) * G_up, G = W1 x + B1 z1
+    GroupedArgs a{};
+    a.off = off; a.E = E; a.M = M; a.N = I; a.K = H;
+    a.A = x; a.lda = H; a.a_gather = perm; a.a_gdiv = d.topk;
+    a.q = qstack(w_gu);
+    a.xa = z1; a.ldxa = r1; a.xb = r1 ? l_gu->B : nullptr; a.xb_estride = (int64_t)2 * I * r1;
+    a.ldxb = r1; a.r = r1;
+    a.C = h; a.ldc = I; a.alpha = 1.0f;
+    a.Gout = G; a.ldg = 2 * I; a.I = I;
+    E4B_LAUNCH(launch_gemm_gate_up(a, s));
+  }
+  if (r2) {  // z2 = s2 * A2[e] h
+    GroupedArgs a{};
+    a.off = off; a.E = E; a.M = M; a.N = r2; a.K = I;
+    a.A = h; a.lda = I; a.a_gdiv = 1;
+    a.Bd = l_dn->A; a.b_estride = (int64_t)r2 * I; a.ldb = I;
+    a.C = z2; a.ldc = r2; a.alpha = l_dn->scaling;
+    E4B_LAUNCH(launch_lora_a(a, s));
+  }
+  {  // O = W2 h + B2 z2
+    GroupedArgs a{};
+    a.off = off; a.E = E; a.M = M; a.N = H; a.K = I;
+    a.A = h; a.lda = I; a.a_gdiv = 1;
+    a.q = qstack(w_dn);
+    a.xa = z2; a.ldxa = r2; a.xb = r2 ? l_dn->B : nullptr; a.xb_estride = (int64_t)H * r2;
+    a.ldxb = r2; a.r = r2;
+    a.C = O; a.ldc = H; a.alpha = 1.0f; a.I = I;
+    E4B_LAUNCH(launch_gemm_down(a, s));
+  }
+  E4B_LAUNCH(launch_combine(O, inv, topw, d.T, d.topk, H, y, s));
+  return E4B_OK;
+}
+
+e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
+                         const e4b_lora *l_gu, const e4b_lora *l_dn, const int32_t *ids,
+                         const float *topw, const uint16_t *dy, uint16_t *dx, float *d_topw,
+                         void *ws, size_t ws_bytes, void *stream) {
+  int r1, r2;
+  E4B_TRY(validate_layer(desc, w_gu, w_dn, l_gu, l_dn, &r1, &r2));
+  const e4b_moe_desc &d = *desc;
+  if (!(d.flags & E4B_TRAIN)) return E4B_ERR_INVALID_ARG;
+  const Layout L = layout(d, r1, r2);
+  if (!ws || ws_bytes < L.total) return E4B_ERR_WORKSPACE;
+  if (d.T > 0 && (!ids || !topw || !dy || !dx)) return E4B_ERR_INVALID_ARG;
+  (void)ids;
+  hipStream_t s = (hipStream_t)stream;
+  const int M = d.T * d.topk, E = d.E, H = d.H, I = d.I;
+  if (M == 0) return E4B_OK;
+  int32_t *off = at<int32_t>(ws, L.off), *inv = at<int32_t>(ws, L.inv);
+  uint16_t *G = at<uint16_t>(ws, L.G), *dO = at<uint16_t>(ws, L.dO), *dG = at<uint16_t>(ws, L.dG);
+  uint16_t *u1 = at<uint16_t>(ws, L.u1), *u2 = at<uint16_t>(ws, L.u2);
+  float *O = at<float>(ws, L.O), *dXp = at<float>(ws, L.dXp);
+  uint16_t *A1T = at<uint16_t>(ws, L.A1T), *B1T = at<uint16_t>(ws, L.B1T);
+  uint16_t *A2T = at<uint16_t>(ws, L.A2T), *B2T = at<uint16_t>(ws, L.B2T);
+
+  E4B_LAUNCH(launch_combine_bwd(dy, O, inv, topw, d.T, d.topk, H, dO, d_topw, s));
+  if (r2) {
+    E4B_LAUNCH(launch_transpose(l_dn->B, E, H, r2, B2T, s));  // [E,H,r] -> [E,r,H]
+    E4B_LAUNCH(launch_transpose(l_dn->A, E, r2, I, A2T, s));  // [E,r,I] -> [E,I,r]
+    GroupedArgs a{};  // u2 = s2 * dO B2
+    a.off = off; a.E = E; a.M = M; a.N = r2; a.K = H;
+    a.A = dO; a.lda = H; a.a_gdiv = 1;
+    a.Bd = B2T; a.b_estride = (int64_t)r2 * H; a.ldb = H;
+    a.C = u2; a.ldc = r2; a.alpha = l_dn->scaling;
+    E4B_LAUNCH(launch_lora_a(a, s));
+  }
+  {  // dH = dO W2 + u2 A2 -> SwiGLU backward -> dG
+    GroupedArgs a{};
+    a.off = off; a.E = E; a.M = M; a.N = I; a.K = H;
+    a.A = dO; a.lda = H; a.a_gdiv = 1;
+    a.q = qstack(w_dn);
+    a.xa = u2; a.ldxa = r2; a.xb = r2 ? A2T : nullptr; a.xb_estride = (int64_t)I * r2;
+    a.ldxb = r2; a.r = r2;
+    a.Gin = G; a.Gout = dG; a.ldg = 2 * I; a.I = I;
+    E4B_LAUNCH(launch_gemm_down_dgrad(a, s));
+  }
+  if (r1) {
+    E4B_LAUNCH(launch_transpose(l_gu->B, E, 2 * I, r1, B1T, s));  // [E,2I,r] -> [E,r,2I]
+    E4B_LAUNCH(launch_transpose(l_gu->A, E, r1, H, A1T, s));      // [E,r,H] -> [E,H,r]
+    GroupedArgs a{};  // u1 = s1 * dG B1
+    a.off = off; a.E = E; a.M = M; a.N = r1; a.K = 2 * I;
+    a.A = dG; a.lda = 2 * I; a.a_gdiv = 1;
+    a.Bd = B1T; a.b_estride = (int64_t)r1 * 2 * I; a.ldb = 2 * I;
+    a.C = u1; a.ldc = r1; a.alpha = l_gu->scaling;
+    E4B_LAUNCH(launch_lora_a(a, s));
+  }
+  {  // dXp = dG W1 + u1 A1
+    GroupedArgs a{};
+    a.off = off; a.E = E; a.M = M; a.N = H; a.K = 2 * I;
+    a.A = dG; a.lda = 2 * I; a.a_gdiv = 1;
+    a.q = qstack(w_gu);
+    a.xa = u1; a.ldxa = r1; a.xb = r1 ? A1T : nullptr; a.xb_estride = (int64_t)H * r1;
+    a.ldxb = r1; a.r = r1;
+    a.C = dXp; a.ldc = H; a.alpha = 1.0f; a.I = I;
+    E4B_LAUNCH(launch_gemm_gate_up_dgrad(a, s));
+  }
+  E4B_LAUNCH(launch_unpermute(dXp, inv, d.T, d.topk, H, dx, s));
+  return E4B_OK;
+}
+
+e4b_status e4b_lora_wgrad(const e4b_moe_desc *desc, const e4b_lora *l_gu, const e4b_lora *l_dn,
+                          const uint16_t *x, void *ws, size_t ws_bytes, float *dA_gu, float *dB_gu,
+                          float *dA_dn, float *dB_dn, void *stream) {
+  int r1, r2;
+  E4B_TRY(check_desc(desc));
+  E4B_TRY(check_lora(l_gu, &r1));
+  E4B_TRY(check_lora(l_dn, &r2));
+  const e4b_moe_desc &d = *desc;
+  if (!(d.flags & E4B_TRAIN)) return E4B_ERR_INVALID_ARG;
+  const Layout L = layout(d, r1, r2);
+  if (!ws || ws_bytes < L.total) return E4B_ERR_WORKSPACE;
+  if (r1 && (!dA_gu || !dB_gu || (d.T > 0 && !x))) return E4B_ERR_INVALID_ARG;
+  if (r2 && (!dA_dn || !dB_dn)) return E4B_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int E = d.E, H = d.H, I = d.I;
+  int32_t *off = at<int32_t>(ws, L.off), *perm = at<int32_t>(ws, L.perm);
+  if (r1) {
+    WgradArgs a{};  // dB1[e] = dG_e^T z1_e
+    a.off = off; a.E = E;
+    a.P = at<uint16_t>(ws, L.dG); a.ldp = 2 * I; a.Na = 2 * I; a.p_gdiv = 1;
+    a.Q = at<uint16_t>(ws, L.z1); a.ldq = r1; a.Nb = r1; a.q_gdiv = 1;
+    a.C = dB_gu;
+    E4B_LAUNCH(launch_wgrad(a, s));
+    WgradArgs b{};  // dA1[e] = u1_e^T X_e
+    b.off = off; b.E = E;
+    b.P = at<uint16_t>(ws, L.u1); b.ldp = r1; b.Na = r1; b.p_gdiv = 1;
+    b.Q = x; b.ldq = H; b.Nb = H; b.q_gather = perm; b.q_gdiv = d.topk;
+    b.C = dA_gu;
+    E4B_LAUNCH(launch_wgrad(b, s));
+  }
+  if (r2) {
+    WgradArgs a{};  // dB2[e] = dO_e^T z2_e
+    a.off = off; a.E = E;
+    a.P = at<uint16_t>(ws, L.dO); a.ldp = H; a.Na = H; a.p_gdiv = 1;
+    a.Q = at<uint16_t>(ws, L.z2); a.ldq = r2; a.Nb = r2; a.q_gdiv = 1;
+    a.C = dB_dn;
+    E4B_LAUNCH(launch_wgrad(a, s));
+    WgradArgs b{};  // dA2[e] = u2_e^T h_e
+    b.off = off; b.E = E;
+    b.P = at<uint16_t>(ws, L.u2); b.ldp = r2; b.Na = r2; b.p_gdiv = 1;
+    b.Q = at<uint16_t>(ws, L.h); b.ldq = I; b.Nb = I; b.q_gdiv = 1;
+    b.C = dA_dn;
+    E4B_LAUNCH(launch_wgrad(b, s));
+  }
+  return E4B_OK;
+}
+
+e4b_status e4b_moe_route(const e4b_moe_desc *desc, const int32_t *ids, int32_t *cnt, int32_t *off,
+                         int32_t *perm, int32_t *inv, void *stream) {
+  E4B_TRY(check_desc(desc));
+  const int M = desc->T * desc->topk;
+  if (!cnt || !off || (M > 0 && (!ids || !perm || !inv))) return E4B_ERR_INVALID_ARG;
+  E4B_LAUNCH(launch_route(ids, M, desc->E, cnt, off, perm, inv, (hipStream_t)stream));
+  return E4B_OK;
+}
+
+e4b_status e4b_dequant(const e4b_qweight *w, int32_t expert, float *out_f32, uint16_t *out_bf16,
+                       void *stream) {
+  if (!w || w->E < 1 || w->N < 1 || w->K < 64 || w->K % 64) return E4B_ERR_INVALID_ARG;
+  E4B_TRY(check_q(w, w->E, w->N, w->K));
+  if (expert >= w->E) return E4B_ERR_INVALID_ARG;
+  if (!out_f32 && !out_bf16) return E4B_ERR_INVALID_ARG;
+  const int64_t per = (int64_t)w->N * w->K;
+  const int64_t e0 = expert < 0 ? 0 : expert;
+  const int64_t n = expert < 0 ? per * w->E : per;
+  E4B_LAUNCH(launch_dequant(qstack(w), e0 * per, n, out_f32, out_bf16, (hipStream_t)stream));
+  return E4B_OK;
+}
+
+e4b_status e4b_quantize(int32_t fmt, int32_t E, int32_t N, int32_t K, const float *w, uint8_t *codes,
+                        void *scale, float *scale2, void *stream) {
+  if (fmt < E4B_FMT_NF4 || fmt > E4B_FMT_MXFP4) return E4B_ERR_UNSUPPORTED;
+  if (E < 1 || N < 1 || K < 64 || K % 64) return E4B_ERR_INVALID_ARG;
+  if (!w || !codes || !scale || (fmt == E4B_FMT_NF4_DQ && !scale2)) return E4B_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)E * N * K;
+  E4B_LAUNCH(launch_quantize(fmt, n, w, codes, scale, scale2, (hipStream_t)stream));
+  return E4B_OK;
+}
+
+e4b_status e4b_moe_check(const e4b_moe_desc *desc, const void *ws, void *stream, int32_t *dropped) {
+  E4B_TRY(check_desc(desc));
+  if (!ws || !dropped) return E4B_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return E4B_ERR_HIP;
+  const Layout L = layout(*desc, 0, 0);
+  int32_t v = 0;
+  if (hipMemcpy(&v, (const char *)ws + L.cnt + (size_t)desc->E * 4, 4, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return E4B_ERR_HIP;
+  *dropped = v;
+  return E4B_OK;
+}
+
+e4b_status e4b_get_stats(e4b_stats *out) {
+  if (!out) return E4B_ERR_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->launches_total = g_total.load();
+  out->route = g_count[FAM_ROUTE].load();
+  out->lora_a = g_count[FAM_LORA_A].load();
+  out->gemm_gate_up = g_count[FAM_GATE_UP].load();
+  out->gemm_down = g_count[FAM_DOWN].load();
+  out->combine = g_count[FAM_COMBINE].load();
+  out->combine_bwd = g_count[FAM_COMBINE_BWD].load();
+  out->gemm_down_dgrad = g_count[FAM_DOWN_DGRAD].load();
+  out->gemm_gate_up_dgrad = g_count[FAM_GATE_UP_DGRAD].load();
+  out->unpermute = g_count[FAM_UNPERMUTE].load();
+  out->wgrad = g_count[FAM_WGRAD].load();
+  out->quant = g_count[FAM_QUANT].load();
+  out->dequant = g_count[FAM_DEQUANT].load();
+  out->fallbacks = 0;
+  return E4B_OK;
+}
+
+void e4b_reset_stats(void) {
+  for (int i = 0; i < FAM_COUNT; ++i) g_count[i] = 0;
+  g_total = 0;
+}
+
+e4b_status e4b_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_tmu);
+  g_timing = on != 0;
+  return E4B_OK;
+}
+
+e4b_status e4b_timing_read(int32_t max, char (*names)[32], int64_t *launches, double *ms,
+                           int32_t *n_out) {
+  if (!n_out) return E4B_ERR_INVALID_ARG;
+  std::vector<TimedLaunch> pend;
+  {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    pend.swap(g_pending);
+  }
+  for (auto &t : pend) {
+    float el = 0.0f;
+    if (hipEventSynchronize(t.b) != hipSuccess) return E4B_ERR_HIP;
+    if (hipEventElapsedTime(&el, t.a, t.b) != hipSuccess) return E4B_ERR_HIP;
+    g_tl[t.fam]++;
+    g_tms[t.fam] += el;
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  int n = 0;
+  for (int f = 0; f < FAM_COUNT; ++f) {
+    if (g_tl[f] == 0) continue;
+    if (n < max) {
+      if (names) {
+        std::strncpy(names[n], family_name(f), 31);
+        names[n][31] = 0;
+      }
+      if (launches) launches[n] = g_tl[f];
+      if (ms) ms[n] = g_tms[f];
+    }
+    ++n;
+    g_tl[f] = 0;
+    g_tms[f] = 0.0;
+  }
+  *n_out = n;
+  return E4B_OK;
+}
+
+}  // extern "C"

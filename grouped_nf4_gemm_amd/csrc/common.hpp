@@ -1,0 +1,85 @@
+// Shared device helpers for the gfx950 kernels: bf16 packing, MFMA fragment
+// types, and the 4-bit decode rules of the three frozen-stack formats.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace e4b {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+enum Fmt : int { FMT_NF4 = 0, FMT_NF4_DQ = 1, FMT_MXFP4 = 2 };
+
+// NormalFloat-4 code values (QLoRA), index 0..15.
+#define E4B_NF4_VALUES                                                                    \
+  {-1.0f, -0.6961928009986877f, -0.5250730514526367f, -0.39491748809814453f,              \
+   -0.28444138169288635f, -0.18477343022823334f, -0.09105003625154495f, 0.0f,              \
+   0.07958029955625534f, 0.16093020141124725f, 0.24611230194568634f, 0.33791524171829224f, \
+   0.44070982933044434f, 0.5626170039176941f, 0.7229568362236023f, 1.0f}
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// E8M0 scale byte -> fp32 2^(X-127) (X = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t X) {
+  return X == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(X << 23);
+}
+
+// Decode the 8 NF4 codes of one 32-bit word (bytes in memory order; element 2j
+// in the high nibble of byte j) to 8 bf16 values, w = bf16(fp32(nf4[q]) * absmax).
+// `cb` is the fp32 code table (in LDS).
+__device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, const float *cb) {
+  u32x4 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t byte = (w >> (8 * b)) & 0xffu;
+    float e0 = cb[byte >> 4] * absmax;
+    float e1 = cb[byte & 15u] * absmax;
+    r[b] = pack_bf16x2(e0, e1);
+  }
+  return r;
+}
+
+// Decode the 8 E2M1 codes of one 32-bit word (element 2j in the low nibble of
+// byte j) times 2^(X-127) to 8 bf16 values (exact).
+__device__ __forceinline__ u32x4 mxfp4_word_to_bf16(uint32_t w, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return r;
+}
+
+// A frozen 4-bit stack as the kernels see it.
+struct QStack {
+  const uint8_t *codes;
+  const void *scale;
+  const float *scale2;
+  int fmt;
+  int N, K;  // per-expert matrix [N, K], K contiguous
+};
+
+// Block scale for NF4 / NF4_DQ element block `b` (flat over the whole stack).
+__device__ __forceinline__ float nf4_block_absmax(const QStack &q, int64_t b) {
+  if (q.fmt == FMT_NF4) return ((const float *)q.scale)[b];
+  float t = (float)((const uint8_t *)q.scale)[b] / 255.0f;
+  return t * q.scale2[b >> 8];
+}
+
+}  // namespace e4b

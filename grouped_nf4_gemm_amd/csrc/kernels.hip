@@ -1,0 +1,600 @@
+// gfx950 kernels of the routed-expert MoE layer: routing, the grouped MFMA
+// GEMMs with in-register 4-bit decode, LoRA K-extension and SwiGLU epilogues,
+// the top-k combine and its backward, the unpermute-sum, the segmented LoRA
+// weight-gradient GEMMs, and the quantise / dequantise kernels.
+#include "gemm.hpp"
+#include "kernels.hpp"
+
+namespace e4b {
+
+__constant__ float kNF4[16] = E4B_NF4_VALUES;
+__constant__ float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// =============================================================== routing
+// One workgroup of 8 wave64s.  Wave w owns a contiguous range of flat indices.
+// Pass 1 counts (expert, wave) pairs in LDS; pass 2 turns them into per-wave
+// starting positions (expert-major, wave-minor) and the expert offsets; pass 3
+// walks each range in order, ranking equal expert ids inside a wave64 by the
+// lanes below them (bitwise key match from ballots), which keeps the grouping
+// stable in the flat index t*k + j.
+constexpr int RT_WAVES = 8;
+
+__global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(const int32_t *__restrict__ ids, int M,
+                                                              int E, int32_t *__restrict__ cnt,
+                                                              int32_t *__restrict__ off,
+                                                              int32_t *__restrict__ perm,
+                                                              int32_t *__restrict__ inv) {
+  extern __shared__ int32_t sm[];
+  const int KE = E + 1;  // keys 0..E-1 valid, E = dropped
+  int32_t *wc = sm;                   // [RT_WAVES][KE]
+  int32_t *soff = sm + RT_WAVES * KE;  // [KE]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < RT_WAVES * KE; i += blockDim.x) wc[i] = 0;
+  __syncthreads();
+  const int S = (((M + RT_WAVES - 1) / RT_WAVES) + 63) & ~63;
+  const int f0 = min(M, w * S), f1 = min(M, f0 + S);
+  for (int f = f0 + lane; f < f1; f += 64) {
+    const int e = ids[f];
+    atomicAdd(&wc[w * KE + ((e >= 0 && e < E) ? e : E)], 1);
+  }
+  __syncthreads();
+  for (int key = tid; key < KE; key += blockDim.x) {
+    int run = 0;
+    for (int ww = 0; ww < RT_WAVES; ++ww) {
+      const int c = wc[ww * KE + key];
+      wc[ww * KE + key] = run;
+      run += c;
+    }
+    cnt[key] = run;
+    soff[key] = run;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int base = 0;
+    for (int c = 0; c < E; c += 64) {
+      const int e = c + lane;
+      const int v = e < E ? soff[e] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (lane >= d) incl += u;
+      }
+      if (e < E) soff[e] = base + incl - v;
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) soff[E] = base;
+  }
+  __syncthreads();
+  for (int e = tid; e < KE; e += blockDim.x) off[e] = soff[e];
+  const int nbits = 32 - __clz(E);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = f0; c0 < f1; c0 += 64) {
+    const int f = c0 + lane;
+    const bool act = f < f1;
+    const int e = act ? ids[f] : 0;
+    const bool valid = act && e >= 0 && e < E;
+    const int key = valid ? e : E;
+    uint64_t eq = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      eq &= bit ? m : ~m;
+    }
+    const int rank = __popcll(eq & lt);
+    const int total = __popcll(eq);
+    if (valid) {
+      const int pos = soff[e] + wc[w * KE + e] + rank;
+      perm[pos] = f;
+      inv[f] = pos;
+    } else if (act) {
+      inv[f] = -1;
+    }
+    if (valid && rank == 0) wc[w * KE + e] += total;
+  }
+  for (int p = soff[E] + tid; p < M; p += blockDim.x) perm[p] = -1;
+}
+
+bool launch_route(const int32_t *ids, int M, int E, int32_t *cnt, int32_t *off, int32_t *perm,
+                  int32_t *inv, hipStream_t s) {
+  LaunchScope ls(FAM_ROUTE, s);
+  const size_t shm = (size_t)(RT_WAVES + 1) * (E + 1) * sizeof(int32_t);
+  route_kernel<<<1, RT_WAVES * 64, shm, s>>>(ids, M, E, cnt, off, perm, inv);
+  return last_launch_ok();
+}
+
+// =============================================================== grouped GEMM
+template <int BKIND, int EPI, bool SWIGLU, int BN, int WM, int WN>
+__global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(GroupedArgs g) {
+  constexpr int BMt = 128;
+  __shared__ LdsTile<BMt> As;
+  __shared__ LdsTile<BN> Bs;
+  __shared__ float cb[16];
+  if (threadIdx.x < 16) cb[threadIdx.x] = kNF4[threadIdx.x];
+  TileM tm;
+  if (!find_tile(g.off, g.E, BMt, blockIdx.y, tm)) return;
+  const int e = tm.e;
+  const int n0 = blockIdx.x * (SWIGLU ? BN / 2 : BN);
+  const RowMap map{n0, g.I, SWIGLU};
+  const int Nrows = SWIGLU ? 2 * g.I : g.N;  // B operand rows (weight rows)
+
+  Mma<BMt, BN, WM, WN> mma;
+  mma.zero();
+  RowLoader<BMt> la;
+  QuantNKLoader lq;
+  QuantKNLoader lk;
+  DenseNKLoader<BN> ld;
+
+  const int nmain = g.K / BK;
+  const int next = g.r > 0 ? (g.r + BK - 1) / BK : 0;
+  const int nsl = nmain + next;
+  const uint16_t *Bd_e = g.Bd ? g.Bd + (int64_t)e * g.b_estride : nullptr;
+  const uint16_t *xb_e = g.xb ? g.xb + (int64_t)e * g.xb_estride : nullptr;
+
+  auto fetch = [&](int s) {
+    if (s < nmain) {
+      const int k0 = s * BK;
+      la.fetch(g.A, g.lda, tm.rows, tm.row0, g.a_gather, g.a_gdiv, k0, g.K);
+      if constexpr (BKIND == B_QNK) lq.fetch(g.q, e, map, Nrows, k0);
+      else if constexpr (BKIND == B_QKN) lk.fetch(g.q, e, n0, g.N, k0);
+      else ld.fetch(Bd_e, g.ldb, map, Nrows, k0, g.K);
+    } else {
+      const int k0 = (s - nmain) * BK;
+      la.fetch(g.xa, g.ldxa, tm.rows, tm.row0, nullptr, 1, k0, g.r);
+      ld.fetch(xb_e, g.ldxb, map, Nrows, k0, g.r);
+    }
+  };
+  auto store = [&](int s) {
+    la.store(As);
+    if (s < nmain) {
+      if constexpr (BKIND == B_QNK) lq.store(Bs, g.q.fmt, cb);
+      else if constexpr (BKIND == B_QKN) lk.store(Bs, g.q.fmt, cb);
+      else ld.store(Bs);
+    } else {
+      ld.store(Bs);
+    }
+  };
+
+  if (nsl > 0) fetch(0);
+  for (int s = 0; s < nsl; ++s) {
+    __syncthreads();  // previous slab's MFMAs done with LDS (and cb written)
+    store(s);
+    __syncthreads();
+    if (s + 1 < nsl) fetch(s + 1);
+    const int ksteps = s < nmain ? 4 : min(4, (g.r - (s - nmain) * BK + 15) / 16);
+    mma.step(As, Bs, ksteps);
+  }
+
+  const int lane = threadIdx.x & 63;
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    // wave (wm, wn): tile j=0 = gate, j=1 = up of h columns n0 + wn*32 + lane%32
+    static_assert(Mma<BMt, BN, WM, WN>::TN == 2 && WN == 2, "SwiGLU tile layout");
+    const int wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+    const int col = n0 + wn * 32 + (lane & 31);
+    uint16_t *H = (uint16_t *)g.C;
+#pragma unroll
+    for (int i = 0; i < Mma<BMt, BN, WM, WN>::TM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = (wm * Mma<BMt, BN, WM, WN>::TM + i) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (row < tm.rows) {
+          const int64_t p = tm.row0 + row;
+          const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
+          const float act = gt / (1.0f + expf(-gt));
+          H[p * g.ldc + col] = f2bf(act * up);
+          if (g.Gout) {
+            g.Gout[p * g.ldg + col] = f2bf(gt);
+            g.Gout[p * g.ldg + g.I + col] = f2bf(up);
+          }
+        }
+      }
+  } else {
+    mma.for_each([&](int row, int col, float v) {
+      const int n = n0 + col;
+      if (row >= tm.rows || n >= g.N) return;
+      const int64_t p = tm.row0 + row;
+      if constexpr (EPI == EPI_F32) {
+        ((float *)g.C)[p * g.ldc + n] = g.alpha * v;
+      } else if constexpr (EPI == EPI_BF16) {
+        ((uint16_t *)g.C)[p * g.ldc + n] = f2bf(g.alpha * v);
+      } else {  // EPI_SWIGLU_BWD: v = dh
+        const float gt = bf2f(g.Gin[p * g.ldg + n]), up = bf2f(g.Gin[p * g.ldg + g.I + n]);
+        const float sg = 1.0f / (1.0f + expf(-gt));
+        const float dg = v * up * sg * (1.0f + gt * (1.0f - sg));
+        const float du = v * gt * sg;
+        g.Gout[p * g.ldg + n] = f2bf(dg);
+        g.Gout[p * g.ldg + g.I + n] = f2bf(du);
+      }
+    });
+  }
+}
+
+static inline int m_slots(const GroupedArgs &a, int BMt) { return cdiv(a.M, BMt) + a.E; }
+
+bool launch_gemm_gate_up(const GroupedArgs &a, hipStream_t s) {
+  if (a.M == 0) return true;
+  LaunchScope ls(FAM_GATE_UP, s);
+  dim3 grid(cdiv(a.I, 64), m_slots(a, 128));
+  grouped_gemm_kernel<B_QNK, EPI_SWIGLU_FWD, true, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  return last_launch_ok();
+}
+
+bool launch_gemm_down(const GroupedArgs &a, hipStream_t s) {
+  if (a.M == 0) return true;
+  LaunchScope ls(FAM_DOWN, s);
+  dim3 grid(cdiv(a.N, 128), m_slots(a, 128));
+  grouped_gemm_kernel<B_QNK, EPI_F32, false, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  return last_launch_ok();
+}
+
+bool launch_gemm_down_dgrad(const GroupedArgs &a, hipStream_t s) {
+  if (a.M == 0) return true;
+  LaunchScope ls(FAM_DOWN_DGRAD, s);
+  dim3 grid(cdiv(a.N, 128), m_slots(a, 128));
+  grouped_gemm_kernel<B_QKN, EPI_SWIGLU_BWD, false, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  return last_launch_ok();
+}
+
+bool launch_gemm_gate_up_dgrad(const GroupedArgs &a, hipStream_t s) {
+  if (a.M == 0) return true;
+  LaunchScope ls(FAM_GATE_UP_DGRAD, s);
+  dim3 grid(cdiv(a.N, 128), m_slots(a, 128));
+  grouped_gemm_kernel<B_QKN, EPI_F32, false, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  return last_launch_ok();
+}
+
+bool launch_lora_a(const GroupedArgs &a, hipStream_t s) {
+  if (a.M == 0) return true;
+  LaunchScope ls(FAM_LORA_A, s);
+  dim3 grid(cdiv(a.N, 64), m_slots(a, 128));
+  grouped_gemm_kernel<B_DENSE, EPI_BF16, false, 64, 4, 1><<<grid, NTHREADS, 0, s>>>(a);
+  return last_launch_ok();
+}
+
+// =============================================================== LoRA weight gradients
+// C[e][a][b] = sum over the routed rows m of expert e of P[m][a] * Q[m][b].
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
+  __shared__ LdsTile<BM> As;
+  __shared__ LdsTile<BN> Bs;
+  const int e = blockIdx.z;
+  const int a0 = blockIdx.y * BM, b0 = blockIdx.x * BN;
+  const int row0 = g.off[e], krows = g.off[e + 1] - g.off[e];
+  Mma<BM, BN, WM, WN> mma;
+  mma.zero();
+  KMajorLoader<BM> la;
+  KMajorLoader<BN> lb;
+  const int nsl = (krows + BK - 1) / BK;
+  if (nsl > 0) {
+    la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, 0);
+    lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, 0);
+  }
+  for (int s = 0; s < nsl; ++s) {
+    __syncthreads();
+    la.store(As);
+    lb.store(Bs);
+    __syncthreads();
+    if (s + 1 < nsl) {
+      la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, (s + 1) * BK);
+      lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, (s + 1) * BK);
+    }
+    mma.step(As, Bs, 4);
+  }
+  float *C = g.C + (int64_t)e * g.Na * g.Nb;
+  mma.for_each([&](int row, int col, float v) {
+    const int a = a0 + row, b = b0 + col;
+    if (a < g.Na && b < g.Nb) C[(int64_t)a * g.Nb + b] = v;
+  });
+}
+
+bool launch_wgrad(const WgradArgs &a, hipStream_t s) {
+  if (a.E == 0) return true;
+  LaunchScope ls(FAM_WGRAD, s);
+  if (a.Nb <= 64) {  // tall-skinny: rows = weight rows, cols = rank
+    dim3 grid(cdiv(a.Nb, 64), cdiv(a.Na, 128), a.E);
+    wgrad_kernel<128, 64, 4, 1><<<grid, NTHREADS, 0, s>>>(a);
+  } else {  // short-wide: rows = rank, cols = weight columns
+    dim3 grid(cdiv(a.Nb, 128), cdiv(a.Na, 64), a.E);
+    wgrad_kernel<64, 128, 1, 4><<<grid, NTHREADS, 0, s>>>(a);
+  }
+  return last_launch_ok();
+}
+
+// =============================================================== combine and friends
+// y[t] = bf16(sum_j w[t,j] * O[inv[t*k+j]]), fp32 sum in j order.
+__global__ void combine_kernel(const float *__restrict__ O, const int32_t *__restrict__ inv,
+                               const float *__restrict__ topw, int k, int H,
+                               uint16_t *__restrict__ y) {
+  const int t = blockIdx.x;
+  for (int h = threadIdx.x * 4; h < H; h += blockDim.x * 4) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int p = inv[(int64_t)t * k + j];
+      if (p < 0) continue;
+      const float w = topw[(int64_t)t * k + j];
+      const f32x4 o = *(const f32x4 *)(O + (int64_t)p * H + h);
+      a0 += w * o[0];
+      a1 += w * o[1];
+      a2 += w * o[2];
+      a3 += w * o[3];
+    }
+    u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+    *(u32x2 *)(y + (int64_t)t * H + h) = out;
+  }
+}
+
+bool launch_combine(const float *O, const int32_t *inv, const float *topw, int T, int k, int H,
+                    uint16_t *y, hipStream_t s) {
+  if (T == 0) return true;
+  LaunchScope ls(FAM_COMBINE, s);
+  combine_kernel<<<T, 256, 0, s>>>(O, inv, topw, k, H, y);
+  return last_launch_ok();
+}
+
+// dO[p] = bf16(w * dy[t]); d_topw[t,j] = <dy[t], O[p]>.
+__global__ void combine_bwd_kernel(const uint16_t *__restrict__ dy, const float *__restrict__ O,
+                                   const int32_t *__restrict__ inv, const float *__restrict__ topw,
+                                   int k, int H, uint16_t *__restrict__ dO,
+                                   float *__restrict__ d_topw) {
+  const int64_t f = blockIdx.x;
+  const int t = (int)(f / k);
+  const int p = inv[f];
+  __shared__ float red[4];
+  if (p < 0) {
+    if (d_topw && threadIdx.x == 0) d_topw[f] = 0.0f;
+    return;
+  }
+  const float w = topw[f];
+  float dot = 0.0f;
+  for (int h = threadIdx.x * 4; h < H; h += blockDim.x * 4) {
+    const u32x2 d = *(const u32x2 *)(dy + (int64_t)t * H + h);
+    const float d0 = __uint_as_float(d[0] << 16), d1 = __uint_as_float(d[0] & 0xffff0000u);
+    const float d2 = __uint_as_float(d[1] << 16), d3 = __uint_as_float(d[1] & 0xffff0000u);
+    const f32x4 o = *(const f32x4 *)(O + (int64_t)p * H + h);
+    dot += d0 * o[0] + d1 * o[1] + d2 * o[2] + d3 * o[3];
+    u32x2 out{pack_bf16x2(w * d0, w * d1), pack_bf16x2(w * d2, w * d3)};
+    *(u32x2 *)(dO + (int64_t)p * H + h) = out;
+  }
+  if (d_topw) {
+    for (int d = 32; d > 0; d >>= 1) dot += __shfl_xor(dot, d);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s = 0.0f;
+      for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += red[i];
+      d_topw[f] = s;
+    }
+  }
+}
+
+bool launch_combine_bwd(const uint16_t *dy, const float *O, const int32_t *inv, const float *topw,
+                        int T, int k, int H, uint16_t *dO, float *d_topw, hipStream_t s) {
+  if (T == 0) return true;
+  LaunchScope ls(FAM_COMBINE_BWD, s);
+  combine_bwd_kernel<<<T * k, 256, 0, s>>>(dy, O, inv, topw, k, H, dO, d_topw);
+  return last_launch_ok();
+}
+
+// dx[t] = bf16(sum_j dXp[inv[t*k+j]]).
+__global__ void unpermute_kernel(const float *__restrict__ dXp, const int32_t *__restrict__ inv, int k,
+                                 int H, uint16_t *__restrict__ dx) {
+  const int t = blockIdx.x;
+  for (int h = threadIdx.x * 4; h < H; h += blockDim.x * 4) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int p = inv[(int64_t)t * k + j];
+      if (p < 0) continue;
+      const f32x4 o = *(const f32x4 *)(dXp + (int64_t)p * H + h);
+      a0 += o[0];
+      a1 += o[1];
+      a2 += o[2];
+      a3 += o[3];
+    }
+    u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+    *(u32x2 *)(dx + (int64_t)t * H + h) = out;
+  }
+}
+
+bool launch_unpermute(const float *dXp, const int32_t *inv, int T, int k, int H, uint16_t *dx,
+                      hipStream_t s) {
+  if (T == 0) return true;
+  LaunchScope ls(FAM_UNPERMUTE, s);
+  unpermute_kernel<<<T, 256, 0, s>>>(dXp, inv, k, H, dx);
+  return last_launch_ok();
+}
+
+// out[e][c][r] = in[e][r][c] (bf16), 32x32 tiles through LDS.
+__global__ void transpose_kernel(const uint16_t *__restrict__ in, int R, int C, uint16_t *__restrict__ out) {
+  __shared__ uint16_t t[32][33];
+  const int e = blockIdx.z;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const uint16_t *src = in + (int64_t)e * R * C;
+  uint16_t *dst = out + (int64_t)e * R * C;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 8 rows per pass
+  for (int i = ty; i < 32; i += 8) {
+    const int r = r0 + i, c = c0 + tx;
+    t[i][tx] = (r < R && c < C) ? src[(int64_t)r * C + c] : 0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < R && c < C) dst[(int64_t)c * R + r] = t[tx][i];
+  }
+}
+
+bool launch_transpose(const uint16_t *in, int E, int R, int C, uint16_t *out, hipStream_t s) {
+  if (E == 0 || R == 0 || C == 0) return true;
+  LaunchScope ls(FAM_TRANSPOSE, s);
+  dim3 grid(cdiv(C, 32), cdiv(R, 32), E);
+  transpose_kernel<<<grid, 256, 0, s>>>(in, R, C, out);
+  return last_launch_ok();
+}
+
+// =============================================================== quantise / dequantise
+__device__ __forceinline__ uint32_t nf4_nearest_dev(float v) {
+  uint32_t best = 0;
+  float bestd = fabsf(v - kNF4[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    const float d = fabsf(v - kNF4[i]);
+    if (d < bestd) {
+      bestd = d;
+      best = i;
+    }
+  }
+  return best;
+}
+
+// One wave64 per block of 64 elements (element i of the block on lane i).
+__global__ void quant_nf4_kernel(const float *__restrict__ w, int64_t nblk, uint8_t *__restrict__ codes,
+                                 float *__restrict__ absmax_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (b >= nblk) return;
+  const float v = w[b * 64 + lane];
+  float amax = fabsf(v);
+  for (int d = 32; d > 0; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  const uint32_t q = amax == 0.0f ? 7u : nf4_nearest_dev(v / amax);
+  const uint32_t partner = __shfl_xor(q, 1);
+  if ((lane & 1) == 0) codes[b * 32 + (lane >> 1)] = (uint8_t)((q << 4) | partner);
+  if (lane == 0 && absmax_out) absmax_out[b] = amax;
+}
+
+// Second level of NF4_DQ: one workgroup of 256 threads per group of 256 blocks.
+__global__ void quant_dq_kernel(const float *__restrict__ w, int64_t nblk, uint8_t *__restrict__ qabs,
+                                float *__restrict__ scale2) {
+  __shared__ float red[256];
+  const int64_t g = blockIdx.x;
+  const int64_t b = g * 256 + threadIdx.x;
+  float amax = 0.0f;
+  if (b < nblk) {
+    const float *p = w + b * 64;
+    for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(p[i]));
+  }
+  red[threadIdx.x] = amax;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float s2 = red[0];
+  if (threadIdx.x == 0) scale2[g] = s2;
+  if (b < nblk) {
+    uint8_t c = 0;
+    if (s2 != 0.0f) {
+      float t = amax / s2;
+      t = t * 255.0f;
+      c = (uint8_t)rintf(t);
+    }
+    qabs[b] = c;
+  }
+}
+
+// One wave64 per two MXFP4 blocks of 32 (lanes 0-31 and 32-63).
+__global__ void quant_mxfp4_kernel(const float *__restrict__ w, int64_t nblk, uint8_t *__restrict__ codes,
+                                   uint8_t *__restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = ((int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 2 + (lane >> 5);
+  const bool ok = b < nblk;
+  const float v = ok ? w[b * 32 + (lane & 31)] : 0.0f;
+  float amax = fabsf(v);
+  for (int d = 16; d > 0; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  uint32_t q = 0;
+  int X = 0;
+  if (amax != 0.0f) {
+    int ex;
+    frexpf(amax, &ex);
+    X = min(254, max(0, (ex - 1) - 2 + 127));
+    const float s = ldexpf(v, -(X - 127));
+    const float a = fabsf(s);
+    if (a >= 6.0f) {
+      q = 7;
+    } else {
+      float bestd = a;
+      for (int i = 1; i < 8; ++i) {
+        const float d = fabsf(a - kE2M1[i]);
+        if (d < bestd || (d == bestd && (i & 1) == 0)) {
+          bestd = d;
+          q = i;
+        }
+      }
+    }
+    if (s < 0.0f && q != 0) q |= 8;
+  }
+  const uint32_t partner = __shfl_xor(q, 1);
+  if (ok && (lane & 1) == 0) codes[b * 16 + ((lane & 31) >> 1)] = (uint8_t)(q | (partner << 4));
+  if (ok && (lane & 31) == 0) scales[b] = (uint8_t)X;
+}
+
+bool launch_quantize(int fmt, int64_t n, const float *w, uint8_t *codes, void *scale, float *scale2,
+                     hipStream_t s) {
+  if (n == 0) return true;
+  LaunchScope ls(FAM_QUANT, s);
+  if (fmt == FMT_MXFP4) {
+    const int64_t nblk = n / 32;
+    quant_mxfp4_kernel<<<cdiv(nblk, 8), 256, 0, s>>>(w, nblk, codes, (uint8_t *)scale);
+    return last_launch_ok();
+  }
+  const int64_t nblk = n / 64;
+  quant_nf4_kernel<<<cdiv(nblk, 4), 256, 0, s>>>(w, nblk, codes,
+                                                 fmt == FMT_NF4 ? (float *)scale : nullptr);
+  if (!last_launch_ok()) return false;
+  if (fmt == FMT_NF4_DQ) {
+    quant_dq_kernel<<<cdiv(nblk, 256), 256, 0, s>>>(w, nblk, (uint8_t *)scale, scale2);
+    return last_launch_ok();
+  }
+  return true;
+}
+
+// 8 consecutive elements per thread: elements elem0 + 8*i .. +8 of the flat stack.
+__global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *__restrict__ f32,
+                               uint16_t *__restrict__ b16) {
+  __shared__ float cb[16];
+  if (threadIdx.x < 16) cb[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nwords) return;
+  const int64_t elem = elem0 + i * 8;
+  const uint32_t w = *(const uint32_t *)(q.codes + elem / 2);
+  float vals[8];
+  u32x4 bits;
+  if (q.fmt == FMT_MXFP4) {
+    const uint32_t X = ((const uint8_t *)q.scale)[elem >> 5];
+    const float sc = e8m0_to_f32(X);
+    bits = mxfp4_word_to_bf16(w, sc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t c = (w >> (4 * j)) & 15u;  // element j: byte j/2, low nibble first
+      const float m = (c & 8u) ? -kE2M1[c & 7u] : kE2M1[c & 7u];
+      vals[j] = m * sc;
+    }
+  } else {
+    const float am = nf4_block_absmax(q, elem >> 6);
+    bits = nf4_word_to_bf16(w, am, cb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t byte = (w >> (8 * j)) & 0xffu;
+      vals[2 * j] = cb[byte >> 4] * am;
+      vals[2 * j + 1] = cb[byte & 15u] * am;
+    }
+  }
+  if (f32) {
+    f32x4 a{vals[0], vals[1], vals[2], vals[3]}, b{vals[4], vals[5], vals[6], vals[7]};
+    *(f32x4 *)(f32 + i * 8) = a;
+    *(f32x4 *)(f32 + i * 8 + 4) = b;
+  }
+  if (b16) *(u32x4 *)(b16 + i * 8) = bits;
+}
+
+bool launch_dequant(const QStack &q, int64_t elem0, int64_t n, float *out_f32, uint16_t *out_bf16,
+                    hipStream_t s) {
+  if (n == 0) return true;
+  LaunchScope ls(FAM_DEQUANT, s);
+  const int64_t nwords = n / 8;
+  dequant_kernel<<<cdiv(nwords, 256), 256, 0, s>>>(q, elem0, nwords, out_f32, out_bf16);
+  return last_launch_ok();
+}
+
+}  // namespace e4b

@@ -1,0 +1,117 @@
+// Host-side launch interface of the gfx950 kernels (internal to libe4b).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace e4b {
+
+// Kernel families for launch counting and event timing.
+enum Family : int {
+  FAM_ROUTE = 0,
+  FAM_LORA_A,
+  FAM_GATE_UP,
+  FAM_DOWN,
+  FAM_COMBINE,
+  FAM_COMBINE_BWD,
+  FAM_DOWN_DGRAD,
+  FAM_GATE_UP_DGRAD,
+  FAM_UNPERMUTE,
+  FAM_WGRAD,
+  FAM_QUANT,
+  FAM_DEQUANT,
+  FAM_TRANSPOSE,
+  FAM_COUNT
+};
+const char *family_name(int f);
+
+// Brackets one launch: counts it and, while timing is on, records events.
+struct LaunchScope {
+  int fam;
+  hipStream_t s;
+  int slot;
+  LaunchScope(int fam, hipStream_t s);
+  ~LaunchScope();
+};
+bool last_launch_ok();
+
+// Operands of one grouped GEMM over expert segments (see gemm.hpp).
+struct GroupedArgs {
+  const int32_t *off;
+  int E;
+  int M;   // total routed rows (grid sizing)
+  int N;   // output columns (per expert); for SwiGLU: I (h columns)
+  int K;   // main reduction length, multiple of 64
+  // A operand: row-major bf16, sorted row p -> source row p (or gather[p] / gdiv)
+  const uint16_t *A;
+  int64_t lda;
+  const int32_t *a_gather;
+  int a_gdiv;
+  // B operand
+  QStack q;            // 4-bit stack (NK: [N, K] rows; KN: stored [K, N])
+  const uint16_t *Bd;  // dense bf16 [E][N][ldb]
+  int64_t b_estride, ldb;
+  // LoRA K-extension: xa [M][ldxa] sorted rows, xb [E][N][ldxb]; r = 0 disables
+  const uint16_t *xa;
+  int64_t ldxa;
+  const uint16_t *xb;
+  int64_t xb_estride, ldxb;
+  int r;
+  // epilogue
+  void *C;
+  int64_t ldc;
+  float alpha;
+  uint16_t *Gout;       // SwiGLU fwd: saved pre-activation [M][2I] (nullable); bwd: dG out
+  const uint16_t *Gin;  // SwiGLU bwd: saved pre-activation
+  int64_t ldg;
+  int I;
+};
+
+enum BKind : int { B_QNK = 0, B_QKN = 1, B_DENSE = 2 };
+enum EpiKind : int { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_FWD = 2, EPI_SWIGLU_BWD = 3 };
+
+// Launchers (return false if the launch failed).
+bool launch_route(const int32_t *ids, int M, int E, int32_t *cnt, int32_t *off, int32_t *perm,
+                  int32_t *inv, hipStream_t s);
+// gate_up forward: h = swiglu(X W1^T + z1 B1^T) (+ G saved)
+bool launch_gemm_gate_up(const GroupedArgs &a, hipStream_t s);
+// down forward: O = h W2^T + z2 B2^T (fp32)
+bool launch_gemm_down(const GroupedArgs &a, hipStream_t s);
+// dgrad through down (stored [H, I] reduced over H) + SwiGLU backward -> dG
+bool launch_gemm_down_dgrad(const GroupedArgs &a, hipStream_t s);
+// dgrad through gate_up (stored [2I, H] reduced over 2I) -> dXp (fp32)
+bool launch_gemm_gate_up_dgrad(const GroupedArgs &a, hipStream_t s);
+// small-N dense GEMM: C = alpha * A B^T (bf16 out), B per expert [N][K]
+bool launch_lora_a(const GroupedArgs &a, hipStream_t s);
+
+struct WgradArgs {
+  const int32_t *off;
+  int E;
+  const uint16_t *P;  // rows a: P[row][a]
+  int64_t ldp;
+  int Na;
+  const int32_t *p_gather;
+  int p_gdiv;
+  const uint16_t *Q;  // cols b: Q[row][b]
+  int64_t ldq;
+  int Nb;
+  const int32_t *q_gather;
+  int q_gdiv;
+  float *C;  // [E][Na][Nb]
+};
+bool launch_wgrad(const WgradArgs &a, hipStream_t s);
+
+bool launch_combine(const float *O, const int32_t *inv, const float *topw, int T, int k, int H,
+                    uint16_t *y, hipStream_t s);
+bool launch_combine_bwd(const uint16_t *dy, const float *O, const int32_t *inv, const float *topw,
+                        int T, int k, int H, uint16_t *dO, float *d_topw, hipStream_t s);
+bool launch_unpermute(const float *dXp, const int32_t *inv, int T, int k, int H, uint16_t *dx,
+                      hipStream_t s);
+bool launch_transpose(const uint16_t *in, int E, int R, int C, uint16_t *out, hipStream_t s);
+bool launch_quantize(int fmt, int64_t n, const float *w, uint8_t *codes, void *scale, float *scale2,
+                     hipStream_t s);
+bool launch_dequant(const QStack &q, int64_t elem0, int64_t n, float *out_f32, uint16_t *out_bf16,
+                    hipStream_t s);
+
+}  // namespace e4b

@@ -1,0 +1,103 @@
+"""GPU bit-exact checks: 4-bit decode, quantisers and routing metadata against the
+oracle (integer and byte work must match exactly; the decoded fp32 and bf16
+weights are fixed by the format's closed form)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from grouped_nf4_gemm_amd import QStack, route
+from tests.gpu_helpers import require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _weights(E, N, K, seed, scale=0.02):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((E, N, K)) * scale).astype(np.float32)
+    w[0, 0, :64] = 0.0          # an all-zero block
+    w[-1, -1, :32] *= 50.0      # a block with a large scale
+    return w
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("E,N,K", [(2, 96, 128), (3, 64, 2880), (1, 8, 64 * 300)])
+def test_dequant_bitexact(fmt, E, N, K):
+    print(f"dequant {fmt} {E}x{N}x{K}", flush=True)
+    w = _weights(E, N, K, seed=E * 7 + N)
+    q = oracle.quantize(fmt, w)
+    f_ref, b_ref = oracle.dequant(q)
+    d = QStack.from_host(fmt, E, N, K, q.codes, q.scale, q.scale2)
+    f32, b16 = d.dequant(-1)
+    assert np.array_equal(f32.cpu().numpy().view(np.uint32), f_ref.reshape(E * N, K).view(np.uint32))
+    assert np.array_equal(b16.view(torch.int16).cpu().numpy().view(np.uint16), b_ref.reshape(E * N, K))
+    # one expert at a time
+    f1, b1 = d.dequant(E - 1)
+    assert np.array_equal(f1.cpu().numpy(), f_ref[E - 1])
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+def test_dequant_every_code(fmt):
+    """All 256 code bytes under a spread of block scales."""
+    E, N, K = 1, 64, 512
+    rng = np.random.default_rng(3)
+    codes = np.tile(np.arange(256, dtype=np.uint8), E * N * K // 2 // 256)
+    if fmt == "nf4":
+        scale = rng.uniform(0, 3, E * N * K // 64).astype(np.float32)
+        q = oracle.QWeight(fmt, E, N, K, codes, scale)
+    elif fmt == "nf4_dq":
+        scale = rng.integers(0, 256, E * N * K // 64).astype(np.uint8)
+        scale2 = rng.uniform(0.01, 2, (E * N * K // 64 + 255) // 256).astype(np.float32)
+        q = oracle.QWeight(fmt, E, N, K, codes, scale, scale2)
+    else:
+        scale = rng.integers(90, 160, E * N * K // 32).astype(np.uint8)
+        q = oracle.QWeight(fmt, E, N, K, codes, scale)
+    f_ref, b_ref = oracle.dequant(q)
+    d = QStack.from_host(fmt, E, N, K, q.codes, q.scale, q.scale2)
+    f32, b16 = d.dequant(-1)
+    assert np.array_equal(f32.cpu().numpy().view(np.uint32), f_ref.reshape(N, K).view(np.uint32))
+    assert np.array_equal(b16.view(torch.int16).cpu().numpy().view(np.uint16), b_ref.reshape(N, K))
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+def test_quantize_bitexact(fmt):
+    E, N, K = 3, 80, 2880
+    w = _weights(E, N, K, seed=11)
+    q = oracle.quantize(fmt, w)
+    g = QStack.quantize(fmt, torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(g.codes.cpu().numpy(), q.codes)
+    assert np.array_equal(g.scale.cpu().numpy(), q.scale)
+    if fmt == "nf4_dq":
+        assert np.array_equal(g.scale2.cpu().numpy(), q.scale2)
+
+
+@pytest.mark.parametrize("T,k,E,bad", [(0, 2, 4, False), (1, 2, 8, False), (37, 3, 5, True),
+                                       (4096, 8, 128, True), (16384, 2, 8, False), (300, 1, 1, False),
+                                       (5000, 4, 1024, True)])
+def test_route_bitexact(T, k, E, bad):
+    rng = np.random.default_rng(T + E)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    if bad and T > 3:
+        ids[1, 0] = E
+        ids[3, k - 1] = -5
+    cnt, off, perm, inv = oracle.route(ids, E)
+    g = route(torch.from_numpy(ids).cuda(), E)
+    torch.cuda.synchronize()
+    for name, ref, got in zip(["cnt", "off", "perm", "inv"], [cnt, off, perm, inv], g):
+        assert np.array_equal(got.cpu().numpy(), ref), name
+
+
+def test_route_skewed_loads():
+    s = synth.WORKLOADS["many-small"]
+    inp = synth.make_inputs(s, weights=False)
+    cnt, off, perm, inv = oracle.route(inp.ids, s.E)
+    g = route(torch.from_numpy(inp.ids).cuda(), s.E)
+    for ref, got in zip([cnt, off, perm, inv], g):
+        assert np.array_equal(got.cpu().numpy(), ref)

@@ -1,0 +1,138 @@
+"""GPU parity of the layer (forward, input gradient, LoRA weight gradients)
+against the oracle, element by element, on shapes the oracle finishes in seconds
+but that span several tiles and ragged tails, plus the exact special cases."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from grouped_nf4_gemm_amd import get_stats, reset_stats
+from tests.gpu_helpers import Case, assert_close, bf16_to_np, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _check_all(case: Case, out: dict, tokens=None):
+    L = case.oracle_layer()
+    y_ref = oracle_fwd = None
+    import oracle
+
+    y_ref = oracle.moe_fwd(L, tokens=tokens)
+    g_ref = oracle.moe_bwd(L, case.inp.dy, tokens=tokens) if "dx" in out else None
+    sel = slice(None) if tokens is None else np.asarray(tokens)
+    assert_close(bf16_to_np(out["y"])[sel], y_ref[sel], "y")
+    if g_ref is None:
+        return
+    assert_close(bf16_to_np(out["dx"])[sel], g_ref["dx"][sel], "dx")
+    assert_close(out["dw"].cpu().numpy()[sel], g_ref["dw"][sel], "d_topw")
+    if case.lora and "dA_gu" in out:
+        for k_gpu, k_ref in [("dA_gu", "dA1"), ("dB_gu", "dB1"), ("dA_dn", "dA2"), ("dB_dn", "dB2")]:
+            assert_close(out[k_gpu].cpu().numpy(), g_ref[k_ref], k_gpu)
+    del oracle_fwd
+
+
+SHAPES = [
+    # name, E, H, I, T, k, r, alpha, fmt
+    ("tiny", 4, 64, 128, 32, 2, 8, 16.0, "nf4"),
+    ("ragged", 5, 192, 320, 77, 3, 16, 32.0, "nf4"),
+    ("multi-tile", 3, 256, 448, 300, 2, 64, 128.0, "nf4"),
+    ("dq", 4, 320, 192, 150, 2, 8, 16.0, "nf4_dq"),
+    ("mxfp4", 6, 192, 192, 100, 4, 8, 16.0, "mxfp4"),
+    ("one-expert", 1, 128, 128, 200, 1, 8, 16.0, "nf4"),
+    ("rank128", 2, 128, 256, 40, 2, 128, 256.0, "nf4"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_layer_parity(shape):
+    name, E, H, I, T, k, r, alpha, fmt = shape
+    print(f"layer parity {shape}", flush=True)
+    s = synth.custom(E, H, I, T, k, r, alpha, fmt, name=name)
+    case = Case(synth.make_inputs(s, seed=100 + E + H + T))
+    reset_stats()
+    out = case.run()
+    st = get_stats()
+    assert st["gemm_gate_up"] >= 1 and st["gemm_down"] >= 1
+    assert st["gemm_down_dgrad"] >= 1 and st["gemm_gate_up_dgrad"] >= 1 and st["wgrad"] >= 4
+    assert st["fallbacks"] == 0
+    _check_all(case, out)
+
+
+def test_tiny_workload_both_B():
+    """The tiny workload, once with random B and once with B = 0."""
+    for zero_B in (False, True):
+        inp = synth.make_inputs(synth.WORKLOADS["tiny"], zero_B=zero_B)
+        case = Case(inp)
+        _check_all(case, case.run())
+
+
+def test_zero_B_equals_no_adapter_bitwise():
+    """B = 0: the K-extension adds exact zeros, so the GPU output and input gradient
+    equal the adapter-free call bit for bit; dA = 0 exactly, dB does not vanish."""
+    inp = synth.make_inputs(synth.custom(4, 128, 192, 64, 2, 16, 32.0), seed=5, zero_B=True)
+    a = Case(inp, lora=True).run()
+    b = Case(inp, lora=False).run()
+    assert torch.equal(a["y"].view(torch.int16), b["y"].view(torch.int16))
+    assert torch.equal(a["dx"].view(torch.int16), b["dx"].view(torch.int16))
+    assert torch.count_nonzero(a["dA_gu"]) == 0 and torch.count_nonzero(a["dA_dn"]) == 0
+    assert torch.count_nonzero(a["dB_gu"]) > 0 and torch.count_nonzero(a["dB_dn"]) > 0
+
+
+def test_no_adapter_parity():
+    inp = synth.make_inputs(synth.custom(3, 128, 128, 50, 2, 8, 16.0), seed=9)
+    case = Case(inp, lora=False)
+    _check_all(case, case.run())
+
+
+def test_deterministic_and_duplicate_rows():
+    """Run twice -> identical bits; a token duplicated in the batch gets identical rows."""
+    inp = synth.make_inputs(synth.custom(4, 128, 192, 40, 2, 8, 16.0), seed=13)
+    inp.x[7] = inp.x[3]
+    inp.ids[7] = inp.ids[3]
+    inp.topw[7] = inp.topw[3]
+    inp.dy[7] = inp.dy[3]
+    case = Case(inp)
+    a = case.run()
+    b = case.run()
+    for k in a:
+        assert torch.equal(a[k].view(torch.int32) if a[k].dtype == torch.float32 else a[k].view(torch.int16),
+                           b[k].view(torch.int32) if b[k].dtype == torch.float32 else b[k].view(torch.int16)), k
+    assert torch.equal(a["y"][7].view(torch.int16), a["y"][3].view(torch.int16))
+    assert torch.equal(a["dx"][7].view(torch.int16), a["dx"][3].view(torch.int16))
+
+
+def test_empty_experts_and_skew():
+    """All tokens on one expert of four: the other experts' LoRA grads are exactly 0."""
+    inp = synth.make_inputs(synth.custom(4, 128, 128, 90, 2, 8, 16.0), seed=17)
+    inp.ids[:, 0] = 2
+    inp.ids[:, 1] = 2
+    case = Case(inp)
+    out = case.run()
+    _check_all(case, out)
+    for k in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
+        g = out[k].cpu().numpy()
+        assert np.all(g[[0, 1, 3]] == 0)
+
+
+def test_out_of_range_ids_dropped():
+    inp = synth.make_inputs(synth.custom(4, 128, 128, 20, 2, 8, 16.0), seed=19)
+    inp.ids[2, 1] = 9
+    inp.ids[5, 0] = -1
+    case = Case(inp)
+    out = case.run()
+    assert case.layer.dropped_rows() == 2
+    _check_all(case, out)
+
+
+def test_zero_tokens():
+    inp = synth.make_inputs(synth.custom(4, 64, 64, 0, 2, 8, 16.0), seed=1)
+    case = Case(inp)
+    out = case.run()
+    assert out["y"].shape == (0, 64) and out["dx"].shape == (0, 64)
+    for k in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
+        assert torch.count_nonzero(out[k]) == 0
