@@ -17,7 +17,7 @@ synthetic values in place of real weights):
                                                                    expert bias N(0,0.5)
 Distributions: x, dy ~ N(0,1) (bf16); logits ~ N(0,1) fp32 (+ per-expert bias);
 W ~ N(0, 0.02) fp32; A ~ U(+-1/sqrt(fan_in)) bf16; B ~ N(0, 0.01) bf16 (or 0).
-Seed = 1000 + workload index, one independent stream per tensor.
+Seed = 1000 + workload index, one independent stream per tensor (per expert for W).
 """
 from __future__ import annotations
 
@@ -77,9 +77,26 @@ def bf16_bits_to_f32(a: np.ndarray) -> np.ndarray:
     return (a.astype(np.uint32) << 16).view(np.float32)
 
 
-def _rngs(seed: int) -> dict:
+def _seqs(seed: int) -> dict:
     ss = np.random.SeedSequence(seed)
-    return {name: np.random.Generator(np.random.PCG64(s)) for name, s in zip(_STREAMS, ss.spawn(len(_STREAMS)))}
+    return dict(zip(_STREAMS, ss.spawn(len(_STREAMS))))
+
+
+def _normal_stack(seq: np.random.SeedSequence, shape, std: float) -> np.ndarray:
+    """N(0, std) fp32 stack [E, ...], one child stream per expert, filled in parallel."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    out = np.empty(shape, np.float32)
+    kids = seq.spawn(shape[0])
+
+    def fill(e):
+        g = np.random.Generator(np.random.PCG64(kids[e]))
+        g.standard_normal(out=out[e], dtype=np.float32)
+        out[e] *= np.float32(std)
+
+    with ThreadPoolExecutor(max_workers=min(16, max(1, shape[0]))) as ex:
+        list(ex.map(fill, range(shape[0])))
+    return out
 
 
 def route(logits: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
@@ -111,17 +128,16 @@ def make_inputs(shape: Shape, seed: int | None = None, zero_B: bool = False,
                 weights: bool = True) -> LayerInputs:
     """Draw every tensor of one layer call.  weights=False skips W1/W2 (empty arrays)."""
     s = shape
-    g = _rngs(1000 + s.index if seed is None else seed)
+    seqs = _seqs(1000 + s.index if seed is None else seed)
+    g = {k: np.random.Generator(np.random.PCG64(v)) for k, v in seqs.items()}
     x = to_bf16_bits(g["x"].standard_normal((s.T, s.H), dtype=np.float32))
     logits = g["logits"].standard_normal((s.T, s.E), dtype=np.float32)
     if s.bias_std:
         logits = logits + (g["bias"].standard_normal(s.E, dtype=np.float32) * np.float32(s.bias_std))
     ids, topw = route(logits, s.k)
     if weights:
-        W1 = g["W1"].standard_normal((s.E, 2 * s.I, s.H), dtype=np.float32)
-        W1 *= np.float32(0.02)
-        W2 = g["W2"].standard_normal((s.E, s.H, s.I), dtype=np.float32)
-        W2 *= np.float32(0.02)
+        W1 = _normal_stack(seqs["W1"], (s.E, 2 * s.I, s.H), 0.02)
+        W2 = _normal_stack(seqs["W2"], (s.E, s.H, s.I), 0.02)
     else:
         W1 = np.zeros((0,), np.float32)
         W2 = np.zeros((0,), np.float32)
