@@ -40,17 +40,23 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t X) {
   return X == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(X << 23);
 }
 
-// Decode the 8 NF4 codes of one 32-bit word (bytes in memory order; element 2j
-// in the high nibble of byte j) to 8 bf16 values, w = bf16(fp32(nf4[q]) * absmax).
-// `cb` is the fp32 code table (in LDS).
-__device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, const float *cb) {
+// Per-workgroup decode tables in LDS.
+//  cb2[b]  = {nf4[b >> 4], nf4[b & 15]}: the two NF4 values of code byte b, element 2j
+//            (high nibble) first, so one 8-byte LDS read decodes a byte.
+//  tab8[c] = fp32(c / 255): the 8-bit absmax code of the double-quantised format.
+struct DecodeTables {
+  float2 cb2[256];
+  float tab8[256];
+};
+
+// Decode the 8 NF4 codes of one 32-bit word (bytes in memory order; element 2j in the
+// high nibble of byte j) to 8 bf16 values, w = bf16(fp32(nf4[q]) * absmax).
+__device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, const DecodeTables &t) {
   u32x4 r;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    uint32_t byte = (w >> (8 * b)) & 0xffu;
-    float e0 = cb[byte >> 4] * absmax;
-    float e1 = cb[byte & 15u] * absmax;
-    r[b] = pack_bf16x2(e0, e1);
+    const float2 v = t.cb2[(w >> (8 * b)) & 0xffu];
+    r[b] = pack_bf16x2(v.x * absmax, v.y * absmax);
   }
   return r;
 }
@@ -76,10 +82,9 @@ struct QStack {
 };
 
 // Block scale for NF4 / NF4_DQ element block `b` (flat over the whole stack).
-__device__ __forceinline__ float nf4_block_absmax(const QStack &q, int64_t b) {
+__device__ __forceinline__ float nf4_block_absmax(const QStack &q, int64_t b, const DecodeTables &t) {
   if (q.fmt == FMT_NF4) return ((const float *)q.scale)[b];
-  float t = (float)((const uint8_t *)q.scale)[b] / 255.0f;
-  return t * q.scale2[b >> 8];
+  return t.tab8[((const uint8_t *)q.scale)[b]] * q.scale2[b >> 8];
 }
 
 }  // namespace e4b

@@ -105,109 +105,167 @@ bool launch_route(const int32_t *ids, int M, int E, int32_t *cnt, int32_t *off, 
   return last_launch_ok();
 }
 
-// =============================================================== grouped GEMM
-template <int BKIND, int EPI, bool SWIGLU, int BN, int WM, int WN>
-__global__ __launch_bounds__(NTHREADS) void grouped_gemm_kernel(GroupedArgs g) {
+// Per-workgroup LDS decode tables (see DecodeTables).
+__device__ __forceinline__ void init_decode_tables(DecodeTables &t) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    t.cb2[i] = make_float2(kNF4[i >> 4], kNF4[i & 15]);
+    t.tab8[i] = (float)i / 255.0f;
+  }
+}
+
+// =============================================================== small-tile bf16 GEMM
+// C = alpha * A B^T over expert segments with a dense per-expert B [N][ldb]: the
+// LoRA-A projections (z = s A[e] x and u = s dG B[e]) whose N is the adapter rank.
+template <int BN, int WM, int WN>
+__global__ __launch_bounds__(NTHREADS) void dense_gemm_kernel(GroupedArgs g) {
   constexpr int BMt = 128;
   __shared__ LdsTile<BMt> As;
   __shared__ LdsTile<BN> Bs;
-  __shared__ float cb[16];
-  if (threadIdx.x < 16) cb[threadIdx.x] = kNF4[threadIdx.x];
   TileM tm;
   if (!find_tile(g.off, g.E, BMt, blockIdx.y, tm)) return;
   const int e = tm.e;
-  const int n0 = blockIdx.x * (SWIGLU ? BN / 2 : BN);
-  const RowMap map{n0, g.I, SWIGLU};
-  const int Nrows = SWIGLU ? 2 * g.I : g.N;  // B operand rows (weight rows)
-
+  const int n0 = blockIdx.x * BN;
+  const RowMap map{n0, 0, false};
   Mma<BMt, BN, WM, WN> mma;
   mma.zero();
   RowLoader<BMt> la;
-  QuantNKLoader lq;
-  QuantKNLoader lk;
   DenseNKLoader<BN> ld;
-
-  const int nmain = g.K / BK;
-  const int next = g.r > 0 ? (g.r + BK - 1) / BK : 0;
-  const int nsl = nmain + next;
-  const uint16_t *Bd_e = g.Bd ? g.Bd + (int64_t)e * g.b_estride : nullptr;
-  const uint16_t *xb_e = g.xb ? g.xb + (int64_t)e * g.xb_estride : nullptr;
-
+  const uint16_t *Bd_e = g.Bd + (int64_t)e * g.b_estride;
+  const int nsl = g.K / BK;
   auto fetch = [&](int s) {
-    if (s < nmain) {
-      const int k0 = s * BK;
-      la.fetch(g.A, g.lda, tm.rows, tm.row0, g.a_gather, g.a_gdiv, k0, g.K);
-      if constexpr (BKIND == B_QNK) lq.fetch(g.q, e, map, Nrows, k0);
-      else if constexpr (BKIND == B_QKN) lk.fetch(g.q, e, n0, g.N, k0);
-      else ld.fetch(Bd_e, g.ldb, map, Nrows, k0, g.K);
-    } else {
-      const int k0 = (s - nmain) * BK;
-      la.fetch(g.xa, g.ldxa, tm.rows, tm.row0, nullptr, 1, k0, g.r);
-      ld.fetch(xb_e, g.ldxb, map, Nrows, k0, g.r);
-    }
+    la.fetch(g.A, g.lda, tm.rows, tm.row0, g.a_gather, g.a_gdiv, s * BK, g.K);
+    ld.fetch(Bd_e, g.ldb, map, g.N, s * BK, g.K);
   };
-  auto store = [&](int s) {
-    la.store(As);
-    if (s < nmain) {
-      if constexpr (BKIND == B_QNK) lq.store(Bs, g.q.fmt, cb);
-      else if constexpr (BKIND == B_QKN) lk.store(Bs, g.q.fmt, cb);
-      else ld.store(Bs);
-    } else {
-      ld.store(Bs);
-    }
-  };
-
   if (nsl > 0) fetch(0);
   for (int s = 0; s < nsl; ++s) {
-    __syncthreads();  // previous slab's MFMAs done with LDS (and cb written)
-    store(s);
+    __syncthreads();
+    la.store(As);
+    ld.store(Bs);
     __syncthreads();
     if (s + 1 < nsl) fetch(s + 1);
-    const int ksteps = s < nmain ? 4 : min(4, (g.r - (s - nmain) * BK + 15) / 16);
-    mma.step(As, Bs, ksteps);
+    mma.step(As, Bs, 4);
+  }
+  mma.for_each([&](int row, int col, float v) {
+    const int n = n0 + col;
+    if (row >= tm.rows || n >= g.N) return;
+    ((uint16_t *)g.C)[(int64_t)(tm.row0 + row) * g.ldc + n] = f2bf(g.alpha * v);
+  });
+}
+
+// Large-tile grouped GEMM (256 x 256 per workgroup, 8 waves, double-buffered LDS).
+template <int BKIND, int EPI, bool SWIGLU>
+__global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
+  __shared__ LTile As[2];
+  __shared__ LTile Bs[2];
+  __shared__ DecodeTables tb;
+  init_decode_tables(tb);
+  TileM tm;
+  if (!find_tile(g.off, g.E, L_BM, blockIdx.y, tm)) return;
+  const int e = tm.e;
+  const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
+  const RowMap map{n0, g.I, SWIGLU};
+  const int Nrows = SWIGLU ? 2 * g.I : g.N;
+
+  LMma mma;
+  mma.zero();
+  LRowLoader la;
+  la.init(tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
+  LQuantNK lq;
+  LQuantKN lk;
+  if constexpr (BKIND == B_QNK) lq.init(g.q, e, map, Nrows);
+  else lk.init(g.q, e, n0, g.N);
+
+  auto fetchB = [&](int k0) {
+    if constexpr (BKIND == B_QNK) lq.fetch(g.q, k0, tb);
+    else lk.fetch(g.q, k0, tb);
+  };
+  auto storeB = [&](LTile &t) {
+    if constexpr (BKIND == B_QNK) lq.store(t, g.q.fmt, tb);
+    else lk.store(t, g.q.fmt, tb);
+  };
+
+  const int nmain = g.K / BK;
+  la.fetch(g.A, 0, g.K);
+  fetchB(0);
+  la.store(As[0]);
+  storeB(Bs[0]);
+  __syncthreads();
+  for (int s = 0; s < nmain; ++s) {
+    const int cur = s & 1;
+    const bool more = s + 1 < nmain;
+    if (more) {
+      la.fetch(g.A, (s + 1) * BK, g.K);
+      fetchB((s + 1) * BK);
+    }
+    mma.step(As[cur], Bs[cur], 4);
+    if (more) {
+      la.store(As[cur ^ 1]);
+      storeB(Bs[cur ^ 1]);
+    }
+    __syncthreads();
+  }
+  if (g.r > 0) {  // LoRA rank as a K-extension of the same accumulator
+    LRowLoader lx;
+    lx.init(tm.rows, tm.row0, nullptr, 1, g.ldxa);
+    LDenseNK lb;
+    lb.init(g.xb + (int64_t)e * g.xb_estride, g.ldxb, map, Nrows);
+    for (int k0 = 0; k0 < g.r; k0 += BK) {
+      lx.fetch(g.xa, k0, g.r);
+      lb.fetch(k0, g.r);
+      lx.store(As[0]);
+      lb.store(Bs[0]);
+      __syncthreads();
+      mma.step(As[0], Bs[0], min(4, (g.r - k0 + 15) / 16));
+      __syncthreads();
+    }
   }
 
   const int lane = threadIdx.x & 63;
   if constexpr (EPI == EPI_SWIGLU_FWD) {
-    // wave (wm, wn): tile j=0 = gate, j=1 = up of h columns n0 + wn*32 + lane%32
-    static_assert(Mma<BMt, BN, WM, WN>::TN == 2 && WN == 2, "SwiGLU tile layout");
-    const int wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+    const int wn = (threadIdx.x >> 6) & 3;
     const int col = n0 + wn * 32 + (lane & 31);
-    uint16_t *H = (uint16_t *)g.C;
+    if (col < g.I) {
+      uint16_t *Hout = (uint16_t *)g.C;
 #pragma unroll
-    for (int i = 0; i < Mma<BMt, BN, WM, WN>::TM; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = (wm * Mma<BMt, BN, WM, WN>::TM + i) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        if (row < tm.rows) {
-          const int64_t p = tm.row0 + row;
-          const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
-          const float act = gt / (1.0f + expf(-gt));
-          H[p * g.ldc + col] = f2bf(act * up);
-          if (g.Gout) {
-            g.Gout[p * g.ldg + col] = f2bf(gt);
-            g.Gout[p * g.ldg + g.I + col] = f2bf(up);
+        for (int v = 0; v < 16; ++v) {
+          const int row = LMma::row_of(i, v);
+          if (row < tm.rows) {
+            const int64_t p = tm.row0 + row;
+            const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
+            const float act = gt / (1.0f + expf(-gt));
+            Hout[p * g.ldc + col] = f2bf(act * up);
+            if (g.Gout) {
+              g.Gout[p * g.ldg + col] = f2bf(gt);
+              g.Gout[p * g.ldg + g.I + col] = f2bf(up);
+            }
           }
         }
-      }
+    }
   } else {
-    mma.for_each([&](int row, int col, float v) {
-      const int n = n0 + col;
-      if (row >= tm.rows || n >= g.N) return;
-      const int64_t p = tm.row0 + row;
-      if constexpr (EPI == EPI_F32) {
-        ((float *)g.C)[p * g.ldc + n] = g.alpha * v;
-      } else if constexpr (EPI == EPI_BF16) {
-        ((uint16_t *)g.C)[p * g.ldc + n] = f2bf(g.alpha * v);
-      } else {  // EPI_SWIGLU_BWD: v = dh
-        const float gt = bf2f(g.Gin[p * g.ldg + n]), up = bf2f(g.Gin[p * g.ldg + g.I + n]);
-        const float sg = 1.0f / (1.0f + expf(-gt));
-        const float dg = v * up * sg * (1.0f + gt * (1.0f - sg));
-        const float du = v * gt * sg;
-        g.Gout[p * g.ldg + n] = f2bf(dg);
-        g.Gout[p * g.ldg + g.I + n] = f2bf(du);
-      }
-    });
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + LMma::col_of(j);
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = LMma::row_of(i, v);
+          if (row >= tm.rows) continue;
+          const int64_t p = tm.row0 + row;
+          const float val = mma.acc[i][j][v];
+          if constexpr (EPI == EPI_F32) {
+            ((float *)g.C)[p * g.ldc + n] = g.alpha * val;
+          } else {  // EPI_SWIGLU_BWD: val = dh
+            const float gt = bf2f(g.Gin[p * g.ldg + n]), up = bf2f(g.Gin[p * g.ldg + g.I + n]);
+            const float sg = 1.0f / (1.0f + expf(-gt));
+            g.Gout[p * g.ldg + n] = f2bf(val * up * sg * (1.0f + gt * (1.0f - sg)));
+            g.Gout[p * g.ldg + g.I + n] = f2bf(val * gt * sg);
+          }
+        }
+    }
   }
 }
 
@@ -216,32 +274,32 @@ static inline int m_slots(const GroupedArgs &a, int BMt) { return cdiv(a.M, BMt)
 bool launch_gemm_gate_up(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_GATE_UP, s);
-  dim3 grid(cdiv(a.I, 64), m_slots(a, 128));
-  grouped_gemm_kernel<B_QNK, EPI_SWIGLU_FWD, true, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  dim3 grid(cdiv(a.I, L_BN / 2), m_slots(a, L_BM));
+  gemm_large_kernel<B_QNK, EPI_SWIGLU_FWD, true><<<grid, L_THREADS, 0, s>>>(a);
   return last_launch_ok();
 }
 
 bool launch_gemm_down(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_DOWN, s);
-  dim3 grid(cdiv(a.N, 128), m_slots(a, 128));
-  grouped_gemm_kernel<B_QNK, EPI_F32, false, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
+  gemm_large_kernel<B_QNK, EPI_F32, false><<<grid, L_THREADS, 0, s>>>(a);
   return last_launch_ok();
 }
 
 bool launch_gemm_down_dgrad(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_DOWN_DGRAD, s);
-  dim3 grid(cdiv(a.N, 128), m_slots(a, 128));
-  grouped_gemm_kernel<B_QKN, EPI_SWIGLU_BWD, false, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
+  gemm_large_kernel<B_QKN, EPI_SWIGLU_BWD, false><<<grid, L_THREADS, 0, s>>>(a);
   return last_launch_ok();
 }
 
 bool launch_gemm_gate_up_dgrad(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_GATE_UP_DGRAD, s);
-  dim3 grid(cdiv(a.N, 128), m_slots(a, 128));
-  grouped_gemm_kernel<B_QKN, EPI_F32, false, 128, 2, 2><<<grid, NTHREADS, 0, s>>>(a);
+  dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
+  gemm_large_kernel<B_QKN, EPI_F32, false><<<grid, L_THREADS, 0, s>>>(a);
   return last_launch_ok();
 }
 
@@ -249,7 +307,7 @@ bool launch_lora_a(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_LORA_A, s);
   dim3 grid(cdiv(a.N, 64), m_slots(a, 128));
-  grouped_gemm_kernel<B_DENSE, EPI_BF16, false, 64, 4, 1><<<grid, NTHREADS, 0, s>>>(a);
+  dense_gemm_kernel<64, 4, 1><<<grid, NTHREADS, 0, s>>>(a);
   return last_launch_ok();
 }
 
@@ -551,8 +609,8 @@ bool launch_quantize(int fmt, int64_t n, const float *w, uint8_t *codes, void *s
 // 8 consecutive elements per thread: elements elem0 + 8*i .. +8 of the flat stack.
 __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *__restrict__ f32,
                                uint16_t *__restrict__ b16) {
-  __shared__ float cb[16];
-  if (threadIdx.x < 16) cb[threadIdx.x] = kNF4[threadIdx.x];
+  __shared__ DecodeTables tb;
+  init_decode_tables(tb);
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nwords) return;
@@ -571,13 +629,13 @@ __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *_
       vals[j] = m * sc;
     }
   } else {
-    const float am = nf4_block_absmax(q, elem >> 6);
-    bits = nf4_word_to_bf16(w, am, cb);
+    const float am = nf4_block_absmax(q, elem >> 6, tb);
+    bits = nf4_word_to_bf16(w, am, tb);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t byte = (w >> (8 * j)) & 0xffu;
-      vals[2 * j] = cb[byte >> 4] * am;
-      vals[2 * j + 1] = cb[byte & 15u] * am;
+      vals[2 * j] = kNF4[byte >> 4] * am;
+      vals[2 * j + 1] = kNF4[byte & 15u] * am;
     }
   }
   if (f32) {
