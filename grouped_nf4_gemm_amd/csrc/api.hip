@@ -105,12 +105,18 @@ static T *at(void *ws, size_t off) {
 }
 
 // ------------------------------------------------------------------ validation
+// Activations and stacks that the 4-bit GEMMs stream with buffer loads must each stay
+// below 2 GiB (32-bit per-lane byte offsets).
+static constexpr int64_t BUF_LIMIT = ((int64_t)1 << 31) - 1;
+
 static e4b_status check_desc(const e4b_moe_desc *d) {
   if (!d) return E4B_ERR_INVALID_ARG;
   if (d->E < 1 || d->E > 1024 || d->topk < 1 || d->topk > d->E || d->T < 0) return E4B_ERR_INVALID_ARG;
   if (d->H <= 0 || d->I <= 0 || d->H % 64 || d->I % 64) return E4B_ERR_INVALID_ARG;
   if ((int64_t)d->T * d->topk > (int64_t)1 << 30) return E4B_ERR_INVALID_ARG;
-  if ((int64_t)d->T * d->topk * 2 * d->I >= ((int64_t)1 << 40)) return E4B_ERR_INVALID_ARG;
+  const int64_t M = (int64_t)d->T * d->topk;
+  if ((int64_t)d->T * d->H * 2 > BUF_LIMIT || M * d->H * 4 > BUF_LIMIT || M * 2 * d->I * 2 > BUF_LIMIT)
+    return E4B_ERR_INVALID_ARG;
   if (d->flags & ~E4B_TRAIN) return E4B_ERR_INVALID_ARG;
   return E4B_OK;
 }
@@ -130,6 +136,7 @@ static e4b_status check_q(const e4b_qweight *q, int E, int N, int K) {
   if (q->fmt < E4B_FMT_NF4 || q->fmt > E4B_FMT_MXFP4) return E4B_ERR_UNSUPPORTED;
   if (q->fmt == E4B_FMT_NF4_DQ && !q->scale2) return E4B_ERR_INVALID_ARG;
   if (q->E != E || q->N != N || q->K != K) return E4B_ERR_INVALID_ARG;
+  if ((int64_t)E * N * K / 2 > BUF_LIMIT) return E4B_ERR_INVALID_ARG;
   return E4B_OK;
 }
 
@@ -141,6 +148,10 @@ static QStack qstack(const e4b_qweight *q) {
   s.fmt = q->fmt;
   s.N = q->N;
   s.K = q->K;
+  const int64_t n = (int64_t)q->E * q->N * q->K;
+  s.codes_bytes = (uint32_t)(n / 2);
+  s.scale_bytes = (uint32_t)(q->fmt == E4B_FMT_NF4 ? n / 64 * 4 : q->fmt == E4B_FMT_NF4_DQ ? n / 64 : n / 32);
+  s.scale2_bytes = q->fmt == E4B_FMT_NF4_DQ ? (uint32_t)((n / 64 + 255) / 256 * 4) : 0;
   return s;
 }
 
@@ -229,6 +240,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     GroupedArgs a{};
     a.off = off; a.E = E; a.M = M; a.N = I; a.K = H;
     a.A = x; a.lda = H; a.a_gather = perm; a.a_gdiv = d.topk;
+    a.a_bytes = (uint32_t)((int64_t)d.T * H * 2);
     a.q = qstack(w_gu);
     a.xa = z1; a.ldxa = r1; a.xb = r1 ? l_gu->B : nullptr; a.xb_estride = (int64_t)2 * I * r1;
     a.ldxb = r1; a.r = r1;
@@ -248,6 +260,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     GroupedArgs a{};
     a.off = off; a.E = E; a.M = M; a.N = H; a.K = I;
     a.A = h; a.lda = I; a.a_gdiv = 1;
+    a.a_bytes = (uint32_t)((int64_t)M * I * 2);
     a.q = qstack(w_dn);
     a.xa = z2; a.ldxa = r2; a.xb = r2 ? l_dn->B : nullptr; a.xb_estride = (int64_t)H * r2;
     a.ldxb = r2; a.r = r2;
@@ -295,6 +308,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     GroupedArgs a{};
     a.off = off; a.E = E; a.M = M; a.N = I; a.K = H;
     a.A = dO; a.lda = H; a.a_gdiv = 1;
+    a.a_bytes = (uint32_t)((int64_t)M * H * 2);
     a.q = qstack(w_dn);
     a.xa = u2; a.ldxa = r2; a.xb = r2 ? A2T : nullptr; a.xb_estride = (int64_t)I * r2;
     a.ldxb = r2; a.r = r2;
@@ -315,6 +329,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     GroupedArgs a{};
     a.off = off; a.E = E; a.M = M; a.N = H; a.K = 2 * I;
     a.A = dG; a.lda = 2 * I; a.a_gdiv = 1;
+    a.a_bytes = (uint32_t)((int64_t)M * 2 * I * 2);
     a.q = qstack(w_gu);
     a.xa = u1; a.ldxa = r1; a.xb = r1 ? A1T : nullptr; a.xb_estride = (int64_t)H * r1;
     a.ldxb = r1; a.r = r1;

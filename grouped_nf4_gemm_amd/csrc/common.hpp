@@ -79,6 +79,7 @@ struct QStack {
   const float *scale2;
   int fmt;
   int N, K;  // per-expert matrix [N, K], K contiguous
+  uint32_t codes_bytes, scale_bytes, scale2_bytes;  // extents (buffer range checks)
 };
 
 // Block scale for NF4 / NF4_DQ element block `b` (flat over the whole stack).

@@ -26,8 +26,8 @@ struct TileM {
 };
 
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ off, int E, int BMt, int slot,
-                                          TileM &t) {
-  __shared__ int s_e, s_row0, s_rows;
+                                          TileM &t, int *sh /* 3 ints of LDS */) {
+  int &s_e = sh[0], &s_row0 = sh[1], &s_rows = sh[2];
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     if (lane == 0) s_e = -1;
@@ -237,190 +237,322 @@ struct Mma {
 }  // namespace e4b
 
 // =====================================================================================
-// Large-tile variant: 256 x 256 output per workgroup, 512 threads = 8 wave64s laid out
-// 2 (M) x 4 (N), each wave owning 128 x 64 as 4 x 2 tiles of 32x32x16 MFMAs.  A and the
-// decoded B operand are double-buffered in LDS (2 x 2 x 36 KB), so each K slab of 64
-// needs one barrier: while the MFMAs consume slab s, the next slab's global loads are
-// in flight and are then decoded and written into the other buffer.
+// Large-tile variant: 256 x 256 output per workgroup, 256 threads = 4 wave64s laid out
+// 2 x 2, each wave owning 128 x 128 as 4 x 4 tiles of 32x32x16 MFMAs (256 accumulator
+// registers; one wave per SIMD).  Software pipeline over K slabs of 64: A rows arrive by
+// direct-to-LDS buffer loads, the 4-bit B operand by buffer loads into registers two
+// slabs ahead; it is decoded and written into LDS between the MFMA k-steps of the slab
+// before it is used.  Buffer loads keep a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane offset (the slab step goes in the scalar offset), and rows past the end of a
+// segment read as zero through the buffer's range check.
 // =====================================================================================
 namespace e4b {
 
-constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
+constexpr int L_BM = 256, L_BN = 256, L_THREADS = 256;
+constexpr int KN_STRIDE = L_BN + 32;  // [k][n] B tile row: 288 bf16 (576 bytes)
+constexpr uint32_t OOB = 0x80000000u;  // per-lane offset that reads as zero
 
-struct LTile {
-  uint16_t v[L_BM][LDS_STRIDE];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
+// A tile written by direct-to-LDS buffer loads: 256 rows of 64 bf16 (128 bytes, no
+// padding) whose eight 16-byte chunks are XOR-swizzled by (row & 7), which keeps both
+// the DMA writes (lane t -> bytes 16t of a 1 KB block) and the MFMA fragment reads free
+// of bank conflicts.
+struct ATile {
+  uint16_t v[L_BM * BK];
+};
+__device__ __forceinline__ int aswz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+struct LTile {  // [256 n][64 (+8) k] bf16, k contiguous
+  uint16_t v[L_BN][LDS_STRIDE];
+};
+struct LTileKN {  // [64 k][256 (+32) n] bf16, n contiguous
+  uint16_t v[BK][KN_STRIDE];
+};
+static_assert(sizeof(LTile) == sizeof(LTileKN), "B tile layouts share one buffer");
+
+// Shared memory of the large tile.  The decode tables come first so their LDS address is
+// zero and a table index is directly an LDS address.
+struct LargeSmem {
+  DecodeTables tb;
+  ATile A0, A1;
+  LTile B0, B1;
+  int tile[4];
 };
 
-// A: 256 rows x 64 k, row-major source (optionally gathered).  Thread -> rows
-// tid/8 + 64*i (i < 4), 16-byte chunk tid%8: each load instruction of a wave covers 8
-// full 128-byte row segments.
-struct LRowLoader {
-  u32x4 buf[4];
-  int64_t src[4];
-  bool ok[4];
+// A: 256 rows x 64 k of a row-major bf16 matrix (optionally gathered rows) loaded
+// straight into LDS.  Wave w, instruction i fills the 1 KB block of rows 8*(8w+i) ..
+// +7: lane l reads row 8*(8w+i) + l/8, logical chunk (l%8) ^ (l/8).
+struct LDirectA {
+  uint32_t voff[8];
   __device__ __forceinline__ void init(int rows, int64_t row0, const int32_t *__restrict__ gather,
                                        int gdiv, int64_t ld) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (threadIdx.x >> 3) + 64 * i;
-      ok[i] = r < rows;
-      int64_t s = 0;
-      if (ok[i]) s = gather ? (int64_t)(gather[row0 + r] / gdiv) : row0 + r;
-      src[i] = s * ld + (threadIdx.x & 7) * 8;
-    }
-  }
-  __device__ __forceinline__ void fetch(const uint16_t *__restrict__ base, int k0, int kbound) {
-    const int kk = k0 + (threadIdx.x & 7) * 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      buf[i] = (ok[i] && kk < kbound) ? *(const u32x4 *)(base + src[i] + k0) : u32x4{0, 0, 0, 0};
-  }
-  __device__ __forceinline__ void store(LTile &t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st_lds16(&t.v[(threadIdx.x >> 3) + 64 * i][(threadIdx.x & 7) * 8], buf[i]);
-  }
-};
-
-// B from a 4-bit stack stored [N, K] (K contiguous): thread -> (tile row tid/2, 32-k half).
-struct LQuantNK {
-  u32x4 codes;
-  float scale;
-  int64_t elem;  // flat element index of this thread's first element at k0 = 0
-  bool ok;
-  __device__ __forceinline__ void init(const QStack &q, int e, const RowMap &map, int Nrows) {
-    const int n = map(threadIdx.x >> 1);
-    ok = n < Nrows;
-    elem = ((int64_t)e * q.N + (ok ? n : 0)) * q.K + (threadIdx.x & 1) * 32;
-  }
-  __device__ __forceinline__ void fetch(const QStack &q, int k0, const DecodeTables &tb) {
-    if (ok) {
-      const int64_t el = elem + k0;
-      codes = *(const u32x4 *)(q.codes + el / 2);
-      scale = q.fmt == FMT_MXFP4 ? e8m0_to_f32(((const uint8_t *)q.scale)[el >> 5])
-                                 : nf4_block_absmax(q, el >> 6, tb);
-    } else {
-      codes = u32x4{0, 0, 0, 0};
-      scale = 0.0f;
-    }
-  }
-  __device__ __forceinline__ void store(LTile &t, int fmt, const DecodeTables &tb) {
-    uint16_t *dst = &t.v[threadIdx.x >> 1][(threadIdx.x & 1) * 32];
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      st_lds16(dst + w * 8, fmt == FMT_MXFP4 ? mxfp4_word_to_bf16(codes[w], scale)
-                                             : nf4_word_to_bf16(codes[w], scale, tb));
-  }
-};
-
-// B from a 4-bit stack reduced over its STORED row axis: tile rows = 256 output columns
-// (stored columns n0..n0+255), k = 64 stored rows.  Thread -> 2 stored rows x 16 stored
-// columns (one 8-byte code load and one block scale per row), decoded, then each
-// column's two k values are packed into one dword and written transposed.
-struct LQuantKN {
-  u32x2 w[2];
-  float scale[2];
-  int64_t elem;  // flat element index of (stored row 2*kb, column n) at k0 = 0
-  bool ok;
-  __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout) {
-    const int kb = threadIdx.x >> 4, nb = threadIdx.x & 15;
-    const int n = n0 + nb * 16;
-    ok = n < Nout;
-    elem = ((int64_t)e * q.N + kb * 2) * q.K + (ok ? n : 0);
-  }
-  __device__ __forceinline__ void fetch(const QStack &q, int k0, const DecodeTables &tb) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (ok) {
-        const int64_t el = elem + (int64_t)(k0 + i) * q.K;
-        w[i] = *(const u32x2 *)(q.codes + el / 2);
-        scale[i] = q.fmt == FMT_MXFP4 ? e8m0_to_f32(((const uint8_t *)q.scale)[el >> 5])
-                                      : nf4_block_absmax(q, el >> 6, tb);
+    for (int i = 0; i < 8; ++i) {
+      const int r = (w * 8 + i) * 8 + (l >> 3);
+      const int lc = (l & 7) ^ (l >> 3);
+      if (r < rows) {
+        const int64_t s = gather ? (int64_t)(gather[row0 + r] / gdiv) : row0 + r;
+        voff[i] = (uint32_t)((s * ld + lc * 8) * 2);
       } else {
-        w[i] = u32x2{0, 0};
-        scale[i] = 0.0f;
+        voff[i] = OOB;
       }
     }
   }
-  __device__ __forceinline__ void store(LTile &t, int fmt, const DecodeTables &tb) {
-    const int kb = threadIdx.x >> 4, nb = threadIdx.x & 15;
-    u32x4 d[2][2];  // [row][word]: 8 bf16 of columns word*8 .. +8
+  // soff: byte offset of the slab's first column (OOB: the slab reads as zero)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, ATile &t, uint32_t soff) {
+    const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void *)&t.v[(w * 8 + i) * 8 * BK], 16, voff[i], soff, 0, 0);
+  }
+};
+
+// Register-staged A rows for the LoRA extension (rows of ld elements, zero past kbound),
+// written into the same swizzled layout.
+struct LRegA {
+  u32x4 buf[8];
+  __device__ __forceinline__ void load(const uint16_t *__restrict__ base, int64_t ld, int rows, int64_t row0,
+                                       int k0, int kbound) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        d[i][h] = fmt == FMT_MXFP4 ? mxfp4_word_to_bf16(w[i][h], scale[i])
-                                   : nf4_word_to_bf16(w[i][h], scale[i], tb);
+    for (int i = 0; i < 8; ++i) {
+      const int r = (w * 8 + i) * 8 + (l >> 3);
+      const int kk = k0 + ((l & 7) ^ (l >> 3)) * 8;
+      buf[i] = (r < rows && kk < kbound) ? *(const u32x4 *)(base + (row0 + r) * ld + kk) : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(ATile &t) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      const uint32_t pk = __builtin_amdgcn_perm(d[1][c >> 3][(c & 7) >> 1], d[0][c >> 3][(c & 7) >> 1], sel);
-      *(uint32_t *)&t.v[nb * 16 + c][kb * 2] = pk;
+    for (int i = 0; i < 8; ++i) st_lds16(&t.v[(w * 8 + i) * 8 * BK + l * 8], buf[i]);
+  }
+};
+
+// Block scale of one code group from its raw fetched value.
+template <int FMT>
+__device__ __forceinline__ float group_scale(uint32_t raw, float s2, const DecodeTables &tb) {
+  if constexpr (FMT == FMT_NF4) return __uint_as_float(raw);
+  else if constexpr (FMT == FMT_NF4_DQ) return tb.tab8[raw] * s2;
+  else return e8m0_to_f32(raw);
+}
+template <int FMT>
+__device__ __forceinline__ u32x4 decode_word(uint32_t w, float sc, const DecodeTables &tb) {
+  if constexpr (FMT == FMT_MXFP4) return mxfp4_word_to_bf16(w, sc);
+  else return nf4_word_to_bf16(w, sc, tb);
+}
+// Raw scale fetch of one group: NF4 fp32 absmax, NF4_DQ 8-bit code (+ its second-level
+// scale, through buffer rs2), MXFP4 E8M0 byte.  `live` = 0 turns the loads into zero reads.
+template <int FMT>
+__device__ __forceinline__ void fetch_scale(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs2, uint32_t voff,
+                                            uint32_t soff, int64_t blk, uint32_t dead, uint32_t &raw,
+                                            float &s2) {
+  if constexpr (FMT == FMT_NF4) {
+    raw = bload32(rs, voff, soff | dead);
+  } else {
+    raw = bload8(rs, voff, soff | dead);
+    if constexpr (FMT == FMT_NF4_DQ) s2 = __uint_as_float(bload32(rs2, (uint32_t)(blk >> 8) * 4, dead));
+  }
+}
+
+// B from a 4-bit stack stored [N, K] (K contiguous): thread -> tile row tid (one weight
+// row), all 64 k of the slab: two 16-byte code loads and one block scale (two for
+// MXFP4).  Stored as eight 16-byte LDS pieces, two per k-step part.
+template <int FMT>
+struct LQuantNK {
+  u32x4 codes[2];
+  uint32_t sraw[2];
+  float s2, sc[2];
+  uint32_t cvoff, svoff;  // byte offsets at k0 = 0
+  int64_t blk0;
+  __device__ __forceinline__ void init(const QStack &q, int e, const RowMap &map, int Nrows) {
+    const int n = map(threadIdx.x);
+    if (n < Nrows) {
+      const int64_t el = ((int64_t)e * q.N + n) * q.K;
+      cvoff = (uint32_t)(el / 2);
+      blk0 = el >> 6;
+      svoff = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blk0 : (uint32_t)(el >> 5);
+    } else {
+      cvoff = svoff = OOB;
+      blk0 = 0;
+    }
+  }
+  // dead = OOB for a slab past the end (every load then reads zero), else 0
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                        __amdgpu_buffer_rsrc_t rs2, int k0, uint32_t dead) {
+    codes[0] = bload128(rc, cvoff, ((uint32_t)k0 / 2) | dead);
+    codes[1] = bload128(rc, cvoff, ((uint32_t)k0 / 2 + 16) | dead);
+    if constexpr (FMT == FMT_MXFP4) {
+      sraw[0] = bload8(rs, svoff, ((uint32_t)(k0 / 32)) | dead);
+      sraw[1] = bload8(rs, svoff, ((uint32_t)(k0 / 32) + 1) | dead);
+    } else {
+      fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)(k0 / 64) * (FMT == FMT_NF4 ? 4 : 1), blk0 + k0 / 64, dead,
+                       sraw[0], s2);
+    }
+  }
+  __device__ __forceinline__ void prepare(const DecodeTables &tb) {
+    sc[0] = group_scale<FMT>(sraw[0], s2, tb);
+    sc[1] = FMT == FMT_MXFP4 ? group_scale<FMT>(sraw[1], s2, tb) : sc[0];
+  }
+  __device__ __forceinline__ void store_part(LTile &t, int part, const DecodeTables &tb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int wi = part * 2 + h;  // code word 0..7 = k 8*wi .. +8
+      st_lds16(&t.v[threadIdx.x][wi * 8], decode_word<FMT>(codes[wi >> 2][wi & 3], sc[wi >> 2], tb));
     }
   }
 };
 
-// Dense bf16 B rows (LoRA K-extension): tile row lr = tid/2 -> weight row map(lr),
-// 32-element half tid%2, zero past kbound.
+// B from a 4-bit stack reduced over its STORED row axis: LDS tile [64 k][256 n], k =
+// stored rows k0..k0+63, n = stored columns n0..n0+255.  Thread -> 2 stored rows x 32
+// stored columns (one 16-byte code load and one block scale per row: 32 aligned columns
+// lie in one NF4 block of 64 and in exactly one MXFP4 block of 32), decoded and written as 16-byte row pieces; the MFMA fragments are read with the
+// transposing LDS load.
+template <int FMT>
+struct LQuantKN {
+  u32x4 w[2];
+  uint32_t sraw[2];
+  float s2[2], sc[2];
+  uint32_t cvoff, svoff, crow, srow;  // offsets at k0 = 0 of stored row 2*kb; per-row steps
+  int64_t blk0, blkrow;
+  __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout) {
+    const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
+    const int n = n0 + nb * 32;
+    crow = (uint32_t)(q.K / 2);
+    blkrow = q.K / 64;
+    srow = FMT == FMT_NF4 ? (uint32_t)(blkrow * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blkrow : (uint32_t)(q.K / 32);
+    if (n < Nout) {
+      const int64_t el = ((int64_t)e * q.N + kb * 2) * q.K + n;
+      cvoff = (uint32_t)(el / 2);
+      blk0 = el >> 6;
+      svoff = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blk0 : (uint32_t)(el >> 5);
+    } else {
+      cvoff = svoff = OOB;
+      blk0 = 0;
+    }
+  }
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                        __amdgpu_buffer_rsrc_t rs2, int k0, uint32_t dead) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t cv = cvoff == OOB ? OOB : cvoff + i * crow;
+      const uint32_t sv = svoff == OOB ? OOB : svoff + i * srow;
+      w[i] = bload128(rc, cv, ((uint32_t)k0 * crow) | dead);
+      fetch_scale<FMT>(rs, rs2, sv, (uint32_t)k0 * srow, blk0 + (int64_t)(k0 + i) * blkrow, dead, sraw[i], s2[i]);
+    }
+  }
+  __device__ __forceinline__ void prepare(const DecodeTables &tb) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sc[i] = group_scale<FMT>(sraw[i], s2[i], tb);
+  }
+  __device__ __forceinline__ void store_part(LTileKN &t, int part, const DecodeTables &tb) {
+    const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
+    const int i = part >> 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int wi = (part & 1) * 2 + h;  // code word 0..3 = columns 8*wi .. +8
+      st_lds16(&t.v[kb * 2 + i][nb * 32 + wi * 8], decode_word<FMT>(w[i][wi], sc[i], tb));
+    }
+  }
+};
+
+// Dense bf16 B rows (LoRA K-extension): tile row tid -> weight row map(tid), zero past
+// kbound.  Always written in the [n][k] layout.
 struct LDenseNK {
-  u32x4 buf[4];
+  u32x4 buf[8];
   const uint16_t *row;
   bool ok;
   __device__ __forceinline__ void init(const uint16_t *__restrict__ base, int64_t ld, const RowMap &map,
                                        int Nrows) {
-    const int n = map(threadIdx.x >> 1);
+    const int n = map(threadIdx.x);
     ok = n < Nrows;
-    row = base + (int64_t)(ok ? n : 0) * ld + (threadIdx.x & 1) * 32;
+    row = base + (int64_t)(ok ? n : 0) * ld;
   }
   __device__ __forceinline__ void fetch(int k0, int kbound) {
-    const int kk = k0 + (threadIdx.x & 1) * 32;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      buf[v] = (ok && kk + 8 * v < kbound) ? *(const u32x4 *)(row + k0 + 8 * v) : u32x4{0, 0, 0, 0};
+    for (int v = 0; v < 8; ++v)
+      buf[v] = (ok && k0 + 8 * v < kbound) ? *(const u32x4 *)(row + k0 + 8 * v) : u32x4{0, 0, 0, 0};
   }
   __device__ __forceinline__ void store(LTile &t) {
-    uint16_t *dst = &t.v[threadIdx.x >> 1][(threadIdx.x & 1) * 32];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) st_lds16(dst + 8 * v, buf[v]);
+    for (int v = 0; v < 8; ++v) st_lds16(&t.v[threadIdx.x][8 * v], buf[v]);
   }
 };
 
-// MFMA core of the large tile: wave (wm, wn) owns rows wm*128.., cols wn*64..
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// MFMA core of the large tile: wave (wm, wn) owns rows wm*128.., cols wn*128..
 struct LMma {
-  f32x16 acc[4][2];
+  f32x16 acc[4][4];
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   }
-  __device__ __forceinline__ void step(const LTile &A, const LTile &B, int ksteps) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
-    const int r = lane & 31, kg = (lane >> 5) * 8;
-    for (int ks = 0; ks < ksteps; ++ks) {
-      bf16x8 a[4], b[2];
+  // B fragments from an [n][k] tile (ds_read_b128).
+  __device__ __forceinline__ static bf16x8 bfrag_nk(const LTile &B, int j, int ks) {
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+    return *(const bf16x8 *)&B.v[wn * 128 + j * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8];
+  }
+  // B fragments from a [k][n] tile with the transposing LDS read: within each 16-lane
+  // group, lane i receives element i%4 of the 8-byte pieces addressed by lanes 4j + i/4,
+  // so lane (4*kr + c) addresses row kr, columns 4c..4c+3 of the group's 16 columns.
+  __device__ __forceinline__ static bf16x8 bfrag_kn(const LTileKN &B, int j, int ks) {
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+    const int G = lane >> 4, i = lane & 15;
+    const int row = ks * 16 + (G >> 1) * 8 + (i >> 2);
+    const int col = wn * 128 + j * 32 + (G & 1) * 16 + (i & 3) * 4;
+    typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row][col]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row + 4][col]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+  }
+  template <bool KN, class BT>
+  __device__ __forceinline__ void kstep(const ATile &A, const BT &B, int ks) {
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    const int r = lane & 31, kc = ks * 2 + (lane >> 5);
+    bf16x8 a[4], b[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8 *)&B.v[wn * 64 + j * 32 + r][ks * 16 + kg];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8 *)&A.v[wm * 128 + i * 32 + r][ks * 16 + kg];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (KN) b[j] = bfrag_kn(B, j, ks);
+      else b[j] = bfrag_nk(B, j, ks);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8 *)&A.v[aswz(wm * 128 + i * 32 + r, kc)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+  template <bool KN, class BT>
+  __device__ __forceinline__ void step(const ATile &A, const BT &B, int ksteps) {
+    for (int ks = 0; ks < ksteps; ++ks) kstep<KN>(A, B, ks);
   }
   // tile-local (row, col) of accumulator element (i, j, v) for this lane
   __device__ __forceinline__ static int row_of(int i, int v) {
-    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 2;
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
     return wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
   }
   __device__ __forceinline__ static int col_of(int j) {
-    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 3;
-    return wn * 64 + j * 32 + (lane & 31);
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+    return wn * 128 + j * 32 + (lane & 31);
   }
 };
 

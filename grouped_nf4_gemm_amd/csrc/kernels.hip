@@ -2,6 +2,8 @@
 // GEMMs with in-register 4-bit decode, LoRA K-extension and SwiGLU epilogues,
 // the top-k combine and its backward, the unpermute-sum, the segmented LoRA
 // weight-gradient GEMMs, and the quantise / dequantise kernels.
+#include <type_traits>
+
 #include "gemm.hpp"
 #include "kernels.hpp"
 
@@ -121,8 +123,9 @@ __global__ __launch_bounds__(NTHREADS) void dense_gemm_kernel(GroupedArgs g) {
   constexpr int BMt = 128;
   __shared__ LdsTile<BMt> As;
   __shared__ LdsTile<BN> Bs;
+  __shared__ int tile_sh[4];
   TileM tm;
-  if (!find_tile(g.off, g.E, BMt, blockIdx.y, tm)) return;
+  if (!find_tile(g.off, g.E, BMt, blockIdx.y, tm, tile_sh)) return;
   const int e = tm.e;
   const int n0 = blockIdx.x * BN;
   const RowMap map{n0, 0, false};
@@ -153,79 +156,174 @@ __global__ __launch_bounds__(NTHREADS) void dense_gemm_kernel(GroupedArgs g) {
 }
 
 // Large-tile grouped GEMM (256 x 256 per workgroup, 8 waves, double-buffered LDS).
-template <int BKIND, int EPI, bool SWIGLU>
+// Software pipeline over K slabs of 64: while the MFMAs consume slab s from LDS buffer
+// s&1, the registers of slab s+1 (loaded one slab earlier) are decoded and written into
+// the other buffer piece by piece between the MFMA k-steps, and the global loads of slab
+// s+2 are in flight.  One barrier per slab.
+// Direct-to-LDS loads count in vmcnt and are not covered by the barrier: every wave
+// waits for its own before the workgroup barrier that publishes them.  vmcnt(n) waits
+// until at most n vector-memory loads of this wave are outstanding (loads retire in
+// order), so the B loads issued after the A loads can stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // expcnt/lgkmcnt at their maximum: no wait
+}
+__device__ __forceinline__ void wait_lds_dma() { wait_vmcnt<0>(); }
+
+// Workgroup barrier after this wave's LDS stores (lgkmcnt(0)) and all but its last N
+// vector-memory loads (vmcnt(N): the direct-to-LDS A loads, issued first) completed.
+// A fenced __syncthreads() would drain every outstanding load, including the B loads
+// prefetched two slabs ahead; the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void slab_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Vector-memory loads one B fetch issues per thread (see LQuantNK / LQuantKN::fetch).
+template <bool KN, int FMT>
+constexpr int b_fetch_loads() {
+  return KN ? 2 * (2 + (FMT == FMT_NF4_DQ ? 1 : 0)) : 2 + (FMT == FMT_MXFP4 ? 2 : FMT == FMT_NF4_DQ ? 2 : 1);
+  // NK: 2 code loads + (MXFP4: 2 scale bytes | NF4_DQ: code byte + second-level scale | NF4: 1)
+  // KN: per row 1 code load + 1 scale (+ 1 second-level scale for NF4_DQ)
+}
+
+template <int BKIND, int FMT>
+struct LargePipe {
+  static constexpr bool KN = BKIND == B_QKN;
+  using BLoader = typename std::conditional<KN, LQuantKN<FMT>, LQuantNK<FMT>>::type;
+  using BTile = typename std::conditional<KN, LTileKN, LTile>::type;
+  DecodeTables &tb;
+  ATile &A0, &A1;
+  LTile &B0, &B1;
+  const GroupedArgs &g;
+  __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
+  LDirectA la;
+  BLoader lb[2];
+  LMma mma;
+
+  // Members are set here, never zero-filled as an aggregate: a memset over the buffer
+  // resources would keep them in memory and make every buffer load a per-lane loop.
+  __device__ __forceinline__ LargePipe(DecodeTables &tb_, ATile &a0, ATile &a1, LTile &b0, LTile &b1,
+                                       const GroupedArgs &g_)
+      : tb(tb_), A0(a0), A1(a1), B0(b0), B1(b1), g(g_),
+        ra(make_rsrc(g_.A, g_.a_bytes)),
+        rc(make_rsrc(g_.q.codes, g_.q.codes_bytes)),
+        rs(make_rsrc(g_.q.scale, g_.q.scale_bytes)),
+        rs2(make_rsrc(g_.q.scale2, g_.q.scale2_bytes)) {}
+
+  template <int P>
+  __device__ __forceinline__ ATile &atile() {
+    if constexpr (P == 0) return A0;
+    else return A1;
+  }
+  template <int P>
+  __device__ __forceinline__ BTile &btile() {
+    if constexpr (P == 0) return *reinterpret_cast<BTile *>(&B0);
+    else return *reinterpret_cast<BTile *>(&B1);
+  }
+  // Loads of a slab past the end read zero (scalar offset pushed out of range), so every
+  // load is issued unconditionally and the loop body is straight-line code.
+  __device__ __forceinline__ static uint32_t dead(int slab, int nmain) { return slab < nmain ? 0u : OOB; }
+  __device__ __forceinline__ void fetch_b(int stage, int slab, int nmain) {
+    lb[stage].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
+  }
+  __device__ __forceinline__ void issue_a(ATile &t, int slab, int nmain) {
+    la.issue(ra, t, (uint32_t)(slab * BK * 2) | dead(slab, nmain));
+  }
+  // Slab s computes from buffers P while slab s+1 is completed into buffers P^1: its A
+  // rows by direct loads issued now, its B from registers P^1 decoded between the
+  // k-steps; the B loads of slab s+2 go into registers P.  Every body runs its MFMAs, so
+  // the accumulators follow one path; a slab past the end has zero A and B.
+  template <int P>
+  __device__ __forceinline__ void body(int s, int nmain) {
+    // The scheduler keeps the issue order: the A rows first, then the B loads, whose
+    // count is the vmcnt the closing barrier leaves outstanding.
+    issue_a(atile<P ^ 1>(), s + 1, nmain);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_b(P, s + 2, nmain);
+    __builtin_amdgcn_sched_barrier(0);
+    lb[P ^ 1].prepare(tb);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      mma.template kstep<KN>(atile<P>(), btile<P>(), ks);
+      lb[P ^ 1].store_part(btile<P ^ 1>(), ks, tb);
+    }
+    slab_barrier<b_fetch_loads<KN, FMT>()>();  // the A rows of slab s+1 have landed
+  }
+  __device__ __forceinline__ void run(int nmain) {
+    issue_a(A0, 0, nmain);
+    fetch_b(0, 0, nmain);
+    fetch_b(1, 1, nmain);
+    lb[0].prepare(tb);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lb[0].store_part(btile<0>(), p, tb);
+    wait_lds_dma();
+    __syncthreads();
+    for (int s = 0; s < nmain; s += 2) {
+      body<0>(s, nmain);
+      body<1>(s + 1, nmain);
+    }
+  }
+};
+
+template <int BKIND, int EPI, bool SWIGLU, int FMT>
 __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
-  __shared__ LTile As[2];
-  __shared__ LTile Bs[2];
+  // separate LDS objects, so the compiler can tell the A tiles that direct loads fill
+  // from the B tiles and tables that ordinary LDS stores write
   __shared__ DecodeTables tb;
+  __shared__ ATile A0, A1;
+  __shared__ LTile B0, B1;
+  __shared__ int tile_sh[4];
   init_decode_tables(tb);
   TileM tm;
-  if (!find_tile(g.off, g.E, L_BM, blockIdx.y, tm)) return;
+  if (!find_tile(g.off, g.E, L_BM, blockIdx.y, tm, tile_sh)) return;
   const int e = tm.e;
   const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
   const RowMap map{n0, g.I, SWIGLU};
   const int Nrows = SWIGLU ? 2 * g.I : g.N;
 
-  LMma mma;
-  mma.zero();
-  LRowLoader la;
-  la.init(tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
-  LQuantNK lq;
-  LQuantKN lk;
-  if constexpr (BKIND == B_QNK) lq.init(g.q, e, map, Nrows);
-  else lk.init(g.q, e, n0, g.N);
+  LargePipe<BKIND, FMT> pipe(tb, A0, A1, B0, B1, g);
+  pipe.mma.zero();
+  pipe.la.init(tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
+  if constexpr (BKIND == B_QKN) pipe.lb[0].init(g.q, e, n0, g.N);
+  else pipe.lb[0].init(g.q, e, map, Nrows);
+  pipe.lb[1] = pipe.lb[0];
+  pipe.run(g.K / BK);
+  LMma &mma = pipe.mma;
 
-  auto fetchB = [&](int k0) {
-    if constexpr (BKIND == B_QNK) lq.fetch(g.q, k0, tb);
-    else lk.fetch(g.q, k0, tb);
-  };
-  auto storeB = [&](LTile &t) {
-    if constexpr (BKIND == B_QNK) lq.store(t, g.q.fmt, tb);
-    else lk.store(t, g.q.fmt, tb);
-  };
-
-  const int nmain = g.K / BK;
-  la.fetch(g.A, 0, g.K);
-  fetchB(0);
-  la.store(As[0]);
-  storeB(Bs[0]);
-  __syncthreads();
-  for (int s = 0; s < nmain; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nmain;
-    if (more) {
-      la.fetch(g.A, (s + 1) * BK, g.K);
-      fetchB((s + 1) * BK);
-    }
-    mma.step(As[cur], Bs[cur], 4);
-    if (more) {
-      la.store(As[cur ^ 1]);
-      storeB(Bs[cur ^ 1]);
-    }
-    __syncthreads();
-  }
   if (g.r > 0) {  // LoRA rank as a K-extension of the same accumulator
-    LRowLoader lx;
-    lx.init(tm.rows, tm.row0, nullptr, 1, g.ldxa);
-    LDenseNK lb;
-    lb.init(g.xb + (int64_t)e * g.xb_estride, g.ldxb, map, Nrows);
+    LRegA lx;
+    LDenseNK lbd;
+    lbd.init(g.xb + (int64_t)e * g.xb_estride, g.ldxb, map, Nrows);
     for (int k0 = 0; k0 < g.r; k0 += BK) {
-      lx.fetch(g.xa, k0, g.r);
-      lb.fetch(k0, g.r);
-      lx.store(As[0]);
-      lb.store(Bs[0]);
+      lx.load(g.xa, g.ldxa, tm.rows, tm.row0, k0, g.r);
+      lbd.fetch(k0, g.r);
+      lx.store(A0);
+      lbd.store(B0);
       __syncthreads();
-      mma.step(As[0], Bs[0], min(4, (g.r - k0 + 15) / 16));
+      mma.step<false>(A0, B0, min(4, (g.r - k0 + 15) / 16));
       __syncthreads();
     }
   }
 
   const int lane = threadIdx.x & 63;
   if constexpr (EPI == EPI_SWIGLU_FWD) {
-    const int wn = (threadIdx.x >> 6) & 3;
-    const int col = n0 + wn * 32 + (lane & 31);
-    if (col < g.I) {
-      uint16_t *Hout = (uint16_t *)g.C;
+    // tile rows interleave 32 gate and 32 up weight rows: pair (2jj, 2jj+1) holds gate and
+    // up of h columns n0 + wn*64 + jj*32 + lane%32
+    const int wn = (threadIdx.x >> 6) & 1;
+    uint16_t *Hout = (uint16_t *)g.C;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = n0 + wn * 64 + jj * 32 + (lane & 31);
+      if (col >= g.I) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -233,7 +331,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
           const int row = LMma::row_of(i, v);
           if (row < tm.rows) {
             const int64_t p = tm.row0 + row;
-            const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
+            const float gt = mma.acc[i][2 * jj][v], up = mma.acc[i][2 * jj + 1][v];
             const float act = gt / (1.0f + expf(-gt));
             Hout[p * g.ldc + col] = f2bf(act * up);
             if (g.Gout) {
@@ -245,7 +343,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int n = n0 + LMma::col_of(j);
       if (n >= g.N) continue;
 #pragma unroll
@@ -269,13 +367,22 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
   }
 }
 
+template <int BKIND, int EPI, bool SWIGLU>
+static void launch_large(const GroupedArgs &a, dim3 grid, hipStream_t s) {
+  switch (a.q.fmt) {
+    case FMT_NF4: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_NF4><<<grid, L_THREADS, 0, s>>>(a); break;
+    case FMT_NF4_DQ: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_NF4_DQ><<<grid, L_THREADS, 0, s>>>(a); break;
+    default: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_MXFP4><<<grid, L_THREADS, 0, s>>>(a); break;
+  }
+}
+
 static inline int m_slots(const GroupedArgs &a, int BMt) { return cdiv(a.M, BMt) + a.E; }
 
 bool launch_gemm_gate_up(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_GATE_UP, s);
   dim3 grid(cdiv(a.I, L_BN / 2), m_slots(a, L_BM));
-  gemm_large_kernel<B_QNK, EPI_SWIGLU_FWD, true><<<grid, L_THREADS, 0, s>>>(a);
+  launch_large<B_QNK, EPI_SWIGLU_FWD, true>(a, grid, s);
   return last_launch_ok();
 }
 
@@ -283,7 +390,7 @@ bool launch_gemm_down(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_DOWN, s);
   dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
-  gemm_large_kernel<B_QNK, EPI_F32, false><<<grid, L_THREADS, 0, s>>>(a);
+  launch_large<B_QNK, EPI_F32, false>(a, grid, s);
   return last_launch_ok();
 }
 
@@ -291,7 +398,7 @@ bool launch_gemm_down_dgrad(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_DOWN_DGRAD, s);
   dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
-  gemm_large_kernel<B_QKN, EPI_SWIGLU_BWD, false><<<grid, L_THREADS, 0, s>>>(a);
+  launch_large<B_QKN, EPI_SWIGLU_BWD, false>(a, grid, s);
   return last_launch_ok();
 }
 
@@ -299,7 +406,7 @@ bool launch_gemm_gate_up_dgrad(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_GATE_UP_DGRAD, s);
   dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
-  gemm_large_kernel<B_QKN, EPI_F32, false><<<grid, L_THREADS, 0, s>>>(a);
+  launch_large<B_QKN, EPI_F32, false>(a, grid, s);
   return last_launch_ok();
 }
 

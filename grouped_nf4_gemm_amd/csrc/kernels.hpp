@@ -48,6 +48,7 @@ struct GroupedArgs {
   int64_t lda;
   const int32_t *a_gather;
   int a_gdiv;
+  uint32_t a_bytes;  // extent of A (large-tile buffer loads)
   // B operand
   QStack q;            // 4-bit stack (NK: [N, K] rows; KN: stored [K, N])
   const uint16_t *Bd;  // dense bf16 [E][N][ldb]
