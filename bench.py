@@ -169,10 +169,10 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str, command: str) -
 
 # kernel family (as the library's event timing names it) -> kernel symbol fragment
 FAMILY_SYMBOL = {
-    "gemm_gate_up": "grouped_gemm_kernel<0, 2,",
-    "gemm_down": "grouped_gemm_kernel<0, 0,",
-    "gemm_down_dgrad": "grouped_gemm_kernel<1, 3,",
-    "gemm_gate_up_dgrad": "grouped_gemm_kernel<1, 0,",
+    "gemm_gate_up": "gemm_large_kernel<0, 2,",
+    "gemm_down": "gemm_large_kernel<0, 0,",
+    "gemm_down_dgrad": "gemm_large_kernel<1, 3,",
+    "gemm_gate_up_dgrad": "gemm_large_kernel<1, 0,",
 }
 
 
@@ -288,7 +288,7 @@ def main():
         else "routed tokens/s (NF4+LoRA grouped MoE layer, forward)",
         "value": value, "unit": "routed tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 MFMA (fp32 accumulate) over " + s.fmt + " weights", "data": "synthetic",
+        "dtype": "bf16", "data": "synthetic (seeded; random-init weights quantised to " + s.fmt + ")",
         "config": {"workload": s.name, "E": s.E, "H": s.H, "I": s.I, "T": s.T, "topk": s.k, "r": s.r,
                    "alpha": s.alpha, "weights": s.fmt, "global_batch": s.T, "parallelism": "none (1 GPU)"},
         "step_tflops": step_flops(s, with_bwd) / (ms / 1e3) / 1e12,
@@ -300,7 +300,7 @@ def main():
     del layer, w_gu, w_dn
     torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
-        n_tok = a.cpu_sample_tokens or (64 if with_bwd else 16)
+        n_tok = a.cpu_sample_tokens or (320 if with_bwd else 16)
         out["cpu_baseline"] = cpu_baseline(s, inp, n_tok)
         out["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]
     print(json.dumps(out), flush=True)

@@ -248,7 +248,10 @@ struct Mma {
 // =====================================================================================
 namespace e4b {
 
-constexpr int L_BM = 256, L_BN = 256, L_THREADS = 256;
+// Large tile: 256 x 256 outputs per workgroup of eight waves, two per SIMD, so one wave's
+// decode and address work issues while the other wave's MFMAs run.  Wave w owns rows
+// (w >> 2) * 128 .. +127 and columns (w & 3) * 64 .. +63 of the tile.
+constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
 constexpr int KN_STRIDE = L_BN + 32;  // [k][n] B tile row: 288 bf16 (576 bytes)
 constexpr uint32_t OOB = 0x80000000u;  // per-lane offset that reads as zero
 
@@ -291,16 +294,16 @@ struct LargeSmem {
 };
 
 // A: 256 rows x 64 k of a row-major bf16 matrix (optionally gathered rows) loaded
-// straight into LDS.  Wave w, instruction i fills the 1 KB block of rows 8*(8w+i) ..
-// +7: lane l reads row 8*(8w+i) + l/8, logical chunk (l%8) ^ (l/8).
+// straight into LDS.  Wave w, instruction i fills the 1 KB block of rows 8*(4w+i) ..
+// +7: lane l reads row 8*(4w+i) + l/8, logical chunk (l%8) ^ (l/8).
 struct LDirectA {
-  uint32_t voff[8];
+  uint32_t voff[4];
   __device__ __forceinline__ void init(int rows, int64_t row0, const int32_t *__restrict__ gather,
                                        int gdiv, int64_t ld) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (w * 8 + i) * 8 + (l >> 3);
+    for (int i = 0; i < 4; ++i) {
+      const int r = (w * 4 + i) * 8 + (l >> 3);
       const int lc = (l & 7) ^ (l >> 3);
       if (r < rows) {
         const int64_t s = gather ? (int64_t)(gather[row0 + r] / gdiv) : row0 + r;
@@ -314,22 +317,22 @@ struct LDirectA {
   __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, ATile &t, uint32_t soff) {
     const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void *)&t.v[(w * 8 + i) * 8 * BK], 16, voff[i], soff, 0, 0);
+          r, (__attribute__((address_space(3))) void *)&t.v[(w * 4 + i) * 8 * BK], 16, voff[i], soff, 0, 0);
   }
 };
 
 // Register-staged A rows for the LoRA extension (rows of ld elements, zero past kbound),
 // written into the same swizzled layout.
 struct LRegA {
-  u32x4 buf[8];
+  u32x4 buf[4];
   __device__ __forceinline__ void load(const uint16_t *__restrict__ base, int64_t ld, int rows, int64_t row0,
                                        int k0, int kbound) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (w * 8 + i) * 8 + (l >> 3);
+    for (int i = 0; i < 4; ++i) {
+      const int r = (w * 4 + i) * 8 + (l >> 3);
       const int kk = k0 + ((l & 7) ^ (l >> 3)) * 8;
       buf[i] = (r < rows && kk < kbound) ? *(const u32x4 *)(base + (row0 + r) * ld + kk) : u32x4{0, 0, 0, 0};
     }
@@ -337,7 +340,7 @@ struct LRegA {
   __device__ __forceinline__ void store(ATile &t) {
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st_lds16(&t.v[(w * 8 + i) * 8 * BK + l * 8], buf[i]);
+    for (int i = 0; i < 4; ++i) st_lds16(&t.v[(w * 4 + i) * 8 * BK + l * 8], buf[i]);
   }
 };
 
@@ -354,7 +357,7 @@ __device__ __forceinline__ u32x4 decode_word(uint32_t w, float sc, const DecodeT
   else return nf4_word_to_bf16(w, sc, tb);
 }
 // Raw scale fetch of one group: NF4 fp32 absmax, NF4_DQ 8-bit code (+ its second-level
-// scale, through buffer rs2), MXFP4 E8M0 byte.  `live` = 0 turns the loads into zero reads.
+// scale, through buffer rs2), MXFP4 E8M0 byte.  `dead` = OOB turns the loads into zero reads.
 template <int FMT>
 __device__ __forceinline__ void fetch_scale(__amdgpu_buffer_rsrc_t rs, __amdgpu_buffer_rsrc_t rs2, uint32_t voff,
                                             uint32_t soff, int64_t blk, uint32_t dead, uint32_t &raw,
@@ -367,23 +370,24 @@ __device__ __forceinline__ void fetch_scale(__amdgpu_buffer_rsrc_t rs, __amdgpu_
   }
 }
 
-// B from a 4-bit stack stored [N, K] (K contiguous): thread -> tile row tid (one weight
-// row), all 64 k of the slab: two 16-byte code loads and one block scale (two for
-// MXFP4).  Stored as eight 16-byte LDS pieces, two per k-step part.
+// B from a 4-bit stack stored [N, K] (K contiguous): thread -> tile row tid % 256 (one
+// weight row) and half tid / 256 of the slab (32 k): one 16-byte code load and one block
+// scale (an NF4 block of 64 spans both halves; an MXFP4 block of 32 is exactly one half).
+// Stored as four 16-byte LDS pieces, one per k-step part.
 template <int FMT>
 struct LQuantNK {
-  u32x4 codes[2];
-  uint32_t sraw[2];
-  float s2, sc[2];
+  u32x4 codes;
+  uint32_t sraw;
+  float s2, sc;
   uint32_t cvoff, svoff;  // byte offsets at k0 = 0
   int64_t blk0;
   __device__ __forceinline__ void init(const QStack &q, int e, const RowMap &map, int Nrows) {
-    const int n = map(threadIdx.x);
+    const int n = map(threadIdx.x & 255), hh = threadIdx.x >> 8;
     if (n < Nrows) {
       const int64_t el = ((int64_t)e * q.N + n) * q.K;
-      cvoff = (uint32_t)(el / 2);
+      cvoff = (uint32_t)(el / 2) + 16 * hh;
       blk0 = el >> 6;
-      svoff = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blk0 : (uint32_t)(el >> 5);
+      svoff = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blk0 : (uint32_t)(el >> 5) + hh;
     } else {
       cvoff = svoff = OOB;
       blk0 = 0;
@@ -392,40 +396,29 @@ struct LQuantNK {
   // dead = OOB for a slab past the end (every load then reads zero), else 0
   __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
                                         __amdgpu_buffer_rsrc_t rs2, int k0, uint32_t dead) {
-    codes[0] = bload128(rc, cvoff, ((uint32_t)k0 / 2) | dead);
-    codes[1] = bload128(rc, cvoff, ((uint32_t)k0 / 2 + 16) | dead);
-    if constexpr (FMT == FMT_MXFP4) {
-      sraw[0] = bload8(rs, svoff, ((uint32_t)(k0 / 32)) | dead);
-      sraw[1] = bload8(rs, svoff, ((uint32_t)(k0 / 32) + 1) | dead);
-    } else {
-      fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)(k0 / 64) * (FMT == FMT_NF4 ? 4 : 1), blk0 + k0 / 64, dead,
-                       sraw[0], s2);
-    }
+    codes = bload128(rc, cvoff, ((uint32_t)k0 / 2) | dead);
+    const uint32_t soff = FMT == FMT_NF4 ? (uint32_t)(k0 / 64) * 4 : FMT == FMT_NF4_DQ ? (uint32_t)(k0 / 64)
+                                                                                       : (uint32_t)(k0 / 32);
+    fetch_scale<FMT>(rs, rs2, svoff, soff, blk0 + k0 / 64, dead, sraw, s2);
   }
-  __device__ __forceinline__ void prepare(const DecodeTables &tb) {
-    sc[0] = group_scale<FMT>(sraw[0], s2, tb);
-    sc[1] = FMT == FMT_MXFP4 ? group_scale<FMT>(sraw[1], s2, tb) : sc[0];
-  }
+  __device__ __forceinline__ void prepare(const DecodeTables &tb) { sc = group_scale<FMT>(sraw, s2, tb); }
   __device__ __forceinline__ void store_part(LTile &t, int part, const DecodeTables &tb) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int wi = part * 2 + h;  // code word 0..7 = k 8*wi .. +8
-      st_lds16(&t.v[threadIdx.x][wi * 8], decode_word<FMT>(codes[wi >> 2][wi & 3], sc[wi >> 2], tb));
-    }
+    st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + part * 8], decode_word<FMT>(codes[part], sc, tb));
   }
 };
 
 // B from a 4-bit stack reduced over its STORED row axis: LDS tile [64 k][256 n], k =
-// stored rows k0..k0+63, n = stored columns n0..n0+255.  Thread -> 2 stored rows x 32
-// stored columns (one 16-byte code load and one block scale per row: 32 aligned columns
-// lie in one NF4 block of 64 and in exactly one MXFP4 block of 32), decoded and written as 16-byte row pieces; the MFMA fragments are read with the
-// transposing LDS load.
+// stored rows k0..k0+63, n = stored columns n0..n0+255.  Thread -> stored row tid / 8 and
+// 32 stored columns (tid % 8): one 16-byte code load and one block scale (32 aligned
+// columns lie in one NF4 block of 64 and in exactly one MXFP4 block of 32), decoded and
+// written as four 16-byte row pieces; the MFMA fragments are read with the transposing
+// LDS load.
 template <int FMT>
 struct LQuantKN {
-  u32x4 w[2];
-  uint32_t sraw[2];
-  float s2[2], sc[2];
-  uint32_t cvoff, svoff, crow, srow;  // offsets at k0 = 0 of stored row 2*kb; per-row steps
+  u32x4 w;
+  uint32_t sraw;
+  float s2, sc;
+  uint32_t cvoff, svoff, crow, srow;  // offsets at k0 = 0 of this thread's stored row; per-row steps
   int64_t blk0, blkrow;
   __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout) {
     const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
@@ -434,7 +427,7 @@ struct LQuantKN {
     blkrow = q.K / 64;
     srow = FMT == FMT_NF4 ? (uint32_t)(blkrow * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blkrow : (uint32_t)(q.K / 32);
     if (n < Nout) {
-      const int64_t el = ((int64_t)e * q.N + kb * 2) * q.K + n;
+      const int64_t el = ((int64_t)e * q.N + kb) * q.K + n;
       cvoff = (uint32_t)(el / 2);
       blk0 = el >> 6;
       svoff = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blk0 : (uint32_t)(el >> 5);
@@ -445,78 +438,70 @@ struct LQuantKN {
   }
   __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
                                         __amdgpu_buffer_rsrc_t rs2, int k0, uint32_t dead) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t cv = cvoff == OOB ? OOB : cvoff + i * crow;
-      const uint32_t sv = svoff == OOB ? OOB : svoff + i * srow;
-      w[i] = bload128(rc, cv, ((uint32_t)k0 * crow) | dead);
-      fetch_scale<FMT>(rs, rs2, sv, (uint32_t)k0 * srow, blk0 + (int64_t)(k0 + i) * blkrow, dead, sraw[i], s2[i]);
-    }
+    w = bload128(rc, cvoff, ((uint32_t)k0 * crow) | dead);
+    fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)k0 * srow, blk0 + (int64_t)k0 * blkrow, dead, sraw, s2);
   }
-  __device__ __forceinline__ void prepare(const DecodeTables &tb) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) sc[i] = group_scale<FMT>(sraw[i], s2[i], tb);
-  }
+  __device__ __forceinline__ void prepare(const DecodeTables &tb) { sc = group_scale<FMT>(sraw, s2, tb); }
   __device__ __forceinline__ void store_part(LTileKN &t, int part, const DecodeTables &tb) {
     const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
-    const int i = part >> 1;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int wi = (part & 1) * 2 + h;  // code word 0..3 = columns 8*wi .. +8
-      st_lds16(&t.v[kb * 2 + i][nb * 32 + wi * 8], decode_word<FMT>(w[i][wi], sc[i], tb));
-    }
+    st_lds16(&t.v[kb][nb * 32 + part * 8], decode_word<FMT>(w[part], sc, tb));
   }
 };
 
 // Dense bf16 B rows (LoRA K-extension): tile row tid -> weight row map(tid), zero past
 // kbound.  Always written in the [n][k] layout.
 struct LDenseNK {
-  u32x4 buf[8];
+  u32x4 buf[4];
   const uint16_t *row;
   bool ok;
   __device__ __forceinline__ void init(const uint16_t *__restrict__ base, int64_t ld, const RowMap &map,
                                        int Nrows) {
-    const int n = map(threadIdx.x);
+    const int n = map(threadIdx.x & 255);
     ok = n < Nrows;
-    row = base + (int64_t)(ok ? n : 0) * ld;
+    row = base + (int64_t)(ok ? n : 0) * ld + (threadIdx.x >> 8) * 32;
   }
+  // this thread's half of the slab: k0 + 32 * (tid / 256) + 8v
   __device__ __forceinline__ void fetch(int k0, int kbound) {
+    const int kh = k0 + (threadIdx.x >> 8) * 32;
 #pragma unroll
-    for (int v = 0; v < 8; ++v)
-      buf[v] = (ok && k0 + 8 * v < kbound) ? *(const u32x4 *)(row + k0 + 8 * v) : u32x4{0, 0, 0, 0};
+    for (int v = 0; v < 4; ++v)
+      buf[v] = (ok && kh + 8 * v < kbound) ? *(const u32x4 *)(row + k0 + 8 * v) : u32x4{0, 0, 0, 0};
   }
   __device__ __forceinline__ void store(LTile &t) {
 #pragma unroll
-    for (int v = 0; v < 8; ++v) st_lds16(&t.v[threadIdx.x][8 * v], buf[v]);
+    for (int v = 0; v < 4; ++v) st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + 8 * v], buf[v]);
   }
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// MFMA core of the large tile: wave (wm, wn) owns rows wm*128.., cols wn*128..
+// MFMA core of the large tile: wave (wm, wn) = (w / 4, w % 4) owns rows wm*128 .. +127
+// and columns wn*64 .. +63: four 32-row by two 32-column accumulator tiles.
 struct LMma {
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
+  __device__ __forceinline__ static int wm() { return threadIdx.x >> 8; }
+  __device__ __forceinline__ static int wn() { return (threadIdx.x >> 6) & 3; }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
   }
   // B fragments from an [n][k] tile (ds_read_b128).
   __device__ __forceinline__ static bf16x8 bfrag_nk(const LTile &B, int j, int ks) {
-    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-    return *(const bf16x8 *)&B.v[wn * 128 + j * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8];
+    const int lane = threadIdx.x & 63;
+    return *(const bf16x8 *)&B.v[wn() * 64 + j * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8];
   }
   // B fragments from a [k][n] tile with the transposing LDS read: within each 16-lane
   // group, lane i receives element i%4 of the 8-byte pieces addressed by lanes 4j + i/4,
   // so lane (4*kr + c) addresses row kr, columns 4c..4c+3 of the group's 16 columns.
   __device__ __forceinline__ static bf16x8 bfrag_kn(const LTileKN &B, int j, int ks) {
-    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+    const int lane = threadIdx.x & 63;
     const int G = lane >> 4, i = lane & 15;
     const int row = ks * 16 + (G >> 1) * 8 + (i >> 2);
-    const int col = wn * 128 + j * 32 + (G & 1) * 16 + (i & 3) * 4;
+    const int col = wn() * 64 + j * 32 + (G & 1) * 16 + (i & 3) * 4;
     typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row][col]));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row + 4][col]));
@@ -525,20 +510,20 @@ struct LMma {
   }
   template <bool KN, class BT>
   __device__ __forceinline__ void kstep(const ATile &A, const BT &B, int ks) {
-    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    const int lane = threadIdx.x & 63;
     const int r = lane & 31, kc = ks * 2 + (lane >> 5);
-    bf16x8 a[4], b[4];
+    bf16x8 a[4], b[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       if constexpr (KN) b[j] = bfrag_kn(B, j, ks);
       else b[j] = bfrag_nk(B, j, ks);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8 *)&A.v[aswz(wm * 128 + i * 32 + r, kc)];
+    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8 *)&A.v[aswz(wm() * 128 + i * 32 + r, kc)];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
   template <bool KN, class BT>
@@ -547,12 +532,12 @@ struct LMma {
   }
   // tile-local (row, col) of accumulator element (i, j, v) for this lane
   __device__ __forceinline__ static int row_of(int i, int v) {
-    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    return wm * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+    const int lane = threadIdx.x & 63;
+    return wm() * 128 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
   }
   __device__ __forceinline__ static int col_of(int j) {
-    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-    return wn * 128 + j * 32 + (lane & 31);
+    const int lane = threadIdx.x & 63;
+    return wn() * 64 + j * 32 + (lane & 31);
   }
 };
 

@@ -190,9 +190,8 @@ __device__ __forceinline__ void slab_barrier() {
 // Vector-memory loads one B fetch issues per thread (see LQuantNK / LQuantKN::fetch).
 template <bool KN, int FMT>
 constexpr int b_fetch_loads() {
-  return KN ? 2 * (2 + (FMT == FMT_NF4_DQ ? 1 : 0)) : 2 + (FMT == FMT_MXFP4 ? 2 : FMT == FMT_NF4_DQ ? 2 : 1);
-  // NK: 2 code loads + (MXFP4: 2 scale bytes | NF4_DQ: code byte + second-level scale | NF4: 1)
-  // KN: per row 1 code load + 1 scale (+ 1 second-level scale for NF4_DQ)
+  // one code load + one scale load (+ the second-level scale for NF4_DQ), NK and KN alike
+  return FMT == FMT_NF4_DQ ? 3 : 2;
 }
 
 template <int BKIND, int FMT>
@@ -316,14 +315,11 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
 
   const int lane = threadIdx.x & 63;
   if constexpr (EPI == EPI_SWIGLU_FWD) {
-    // tile rows interleave 32 gate and 32 up weight rows: pair (2jj, 2jj+1) holds gate and
-    // up of h columns n0 + wn*64 + jj*32 + lane%32
-    const int wn = (threadIdx.x >> 6) & 1;
+    // tile rows interleave 32 gate and 32 up weight rows: the wave's pair (0, 1) holds gate
+    // and up of h columns n0 + wn*32 + lane%32
     uint16_t *Hout = (uint16_t *)g.C;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int col = n0 + wn * 64 + jj * 32 + (lane & 31);
-      if (col >= g.I) continue;
+    const int col = n0 + LMma::wn() * 32 + (lane & 31);
+    if (col < g.I) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -331,7 +327,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
           const int row = LMma::row_of(i, v);
           if (row < tm.rows) {
             const int64_t p = tm.row0 + row;
-            const float gt = mma.acc[i][2 * jj][v], up = mma.acc[i][2 * jj + 1][v];
+            const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
             const float act = gt / (1.0f + expf(-gt));
             Hout[p * g.ldc + col] = f2bf(act * up);
             if (g.Gout) {
@@ -343,7 +339,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int n = n0 + LMma::col_of(j);
       if (n >= g.N) continue;
 #pragma unroll
