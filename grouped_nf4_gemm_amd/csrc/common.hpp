@@ -42,23 +42,35 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t X) {
 
 // Per-workgroup decode tables in LDS.
 //  cb2[b]  = {nf4[b >> 4], nf4[b & 15]}: the two NF4 values of code byte b, element 2j
-//            (high nibble) first, so one 8-byte LDS read decodes a byte.
+//            (high nibble) first, so one 8-byte LDS read serves two codes.
 //  tab8[c] = fp32(c / 255): the 8-bit absmax code of the double-quantised format.
 struct DecodeTables {
   float2 cb2[256];
   float tab8[256];
 };
 
-// Decode the 8 NF4 codes of one 32-bit word (bytes in memory order; element 2j in the
-// high nibble of byte j) to 8 bf16 values, w = bf16(fp32(nf4[q]) * absmax).
-__device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, const DecodeTables &t) {
-  u32x4 r;
+// The NF4 values of the 8 codes of one 32-bit word (bytes in memory order; element 2j in
+// the high nibble of byte j).
+__device__ __forceinline__ void nf4_lookup(uint32_t w, const DecodeTables &t, float (&v)[8]) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const float2 v = t.cb2[(w >> (8 * b)) & 0xffu];
-    r[b] = pack_bf16x2(v.x * absmax, v.y * absmax);
+    const float2 x = t.cb2[(w >> (8 * b)) & 0xffu];
+    v[2 * b] = x.x;
+    v[2 * b + 1] = x.y;
   }
+}
+// w = bf16(fp32(nf4[q]) * absmax), packed in pairs.
+__device__ __forceinline__ u32x4 nf4_scale_pack(const float (&v)[8], float absmax) {
+  u32x4 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) r[b] = pack_bf16x2(v[2 * b] * absmax, v[2 * b + 1] * absmax);
   return r;
+}
+// Decode the 8 NF4 codes of one 32-bit word to 8 bf16 values.
+__device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, const DecodeTables &t) {
+  float v[8];
+  nf4_lookup(w, t, v);
+  return nf4_scale_pack(v, absmax);
 }
 
 // Decode the 8 E2M1 codes of one 32-bit word (element 2j in the low nibble of

@@ -252,7 +252,7 @@ namespace e4b {
 // decode and address work issues while the other wave's MFMAs run.  Wave w owns rows
 // (w >> 2) * 128 .. +127 and columns (w & 3) * 64 .. +63 of the tile.
 constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
-constexpr int KN_STRIDE = L_BN + 32;  // [k][n] B tile row: 288 bf16 (576 bytes)
+constexpr int KN_STRIDE = L_BN + 16;  // [k][n] B tile row: 272 bf16 (544 bytes = 32 mod 128)
 constexpr uint32_t OOB = 0x80000000u;  // per-lane offset that reads as zero
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
@@ -279,10 +279,19 @@ __device__ __forceinline__ int aswz(int row, int chunk) { return row * BK + ((ch
 struct LTile {  // [256 n][64 (+8) k] bf16, k contiguous
   uint16_t v[L_BN][LDS_STRIDE];
 };
-struct LTileKN {  // [64 k][256 (+32) n] bf16, n contiguous
+// [64 k][256 (+16) n] bf16, n contiguous, whose 16-byte chunks c (8 columns) sit at
+// c ^ ((c >> 3) & 3) within the row.  With the row stride of 32 mod 128 bytes this keeps
+// both access patterns free of bank conflicts: the decode stores (8 lanes write chunks
+// 4m + p, m = 0..7, of one row) and the transposing fragment reads (16 lanes read two
+// adjacent chunks in each of 4 consecutive rows).
+struct LTileKN {
   uint16_t v[BK][KN_STRIDE];
 };
-static_assert(sizeof(LTile) == sizeof(LTileKN), "B tile layouts share one buffer");
+__device__ __forceinline__ int knswz(int col) {
+  const int c = col >> 3;
+  return ((c ^ ((c >> 3) & 3)) << 3) | (col & 7);
+}
+static_assert(sizeof(LTileKN) <= sizeof(LTile), "B tile layouts share one buffer");
 
 // Shared memory of the large tile.  The decode tables come first so their LDS address is
 // zero and a table index is directly an LDS address.
@@ -351,10 +360,16 @@ __device__ __forceinline__ float group_scale(uint32_t raw, float s2, const Decod
   else if constexpr (FMT == FMT_NF4_DQ) return tb.tab8[raw] * s2;
   else return e8m0_to_f32(raw);
 }
+// Decode in two steps, so the table reads can be issued ahead of the MFMAs that hide
+// their latency: lookup (NF4 formats: 8 LDS reads; MXFP4: nothing) and finish.
 template <int FMT>
-__device__ __forceinline__ u32x4 decode_word(uint32_t w, float sc, const DecodeTables &tb) {
+__device__ __forceinline__ void decode_lookup(uint32_t w, const DecodeTables &tb, float (&v)[8]) {
+  if constexpr (FMT != FMT_MXFP4) nf4_lookup(w, tb, v);
+}
+template <int FMT>
+__device__ __forceinline__ u32x4 decode_finish(uint32_t w, float sc, const float (&v)[8]) {
   if constexpr (FMT == FMT_MXFP4) return mxfp4_word_to_bf16(w, sc);
-  else return nf4_word_to_bf16(w, sc, tb);
+  else return nf4_scale_pack(v, sc);
 }
 // Raw scale fetch of one group: NF4 fp32 absmax, NF4_DQ 8-bit code (+ its second-level
 // scale, through buffer rs2), MXFP4 E8M0 byte.  `dead` = OOB turns the loads into zero reads.
@@ -402,8 +417,11 @@ struct LQuantNK {
     fetch_scale<FMT>(rs, rs2, svoff, soff, blk0 + k0 / 64, dead, sraw, s2);
   }
   __device__ __forceinline__ void prepare(const DecodeTables &tb) { sc = group_scale<FMT>(sraw, s2, tb); }
-  __device__ __forceinline__ void store_part(LTile &t, int part, const DecodeTables &tb) {
-    st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + part * 8], decode_word<FMT>(codes[part], sc, tb));
+  __device__ __forceinline__ void lookup(int part, const DecodeTables &tb, float (&v)[8]) const {
+    decode_lookup<FMT>(codes[part], tb, v);
+  }
+  __device__ __forceinline__ void finish(LTile &t, int part, const float (&v)[8]) const {
+    st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + part * 8], decode_finish<FMT>(codes[part], sc, v));
   }
 };
 
@@ -442,9 +460,12 @@ struct LQuantKN {
     fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)k0 * srow, blk0 + (int64_t)k0 * blkrow, dead, sraw, s2);
   }
   __device__ __forceinline__ void prepare(const DecodeTables &tb) { sc = group_scale<FMT>(sraw, s2, tb); }
-  __device__ __forceinline__ void store_part(LTileKN &t, int part, const DecodeTables &tb) {
+  __device__ __forceinline__ void lookup(int part, const DecodeTables &tb, float (&v)[8]) const {
+    decode_lookup<FMT>(w[part], tb, v);
+  }
+  __device__ __forceinline__ void finish(LTileKN &t, int part, const float (&v)[8]) const {
     const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
-    st_lds16(&t.v[kb][nb * 32 + part * 8], decode_word<FMT>(w[part], sc, tb));
+    st_lds16(&t.v[kb][knswz(nb * 32 + part * 8)], decode_finish<FMT>(w[part], sc, v));
   }
 };
 
@@ -503,28 +524,40 @@ struct LMma {
     const int row = ks * 16 + (G >> 1) * 8 + (i >> 2);
     const int col = wn() * 64 + j * 32 + (G & 1) * 16 + (i & 3) * 4;
     typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row][col]));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row + 4][col]));
+    const int pc = knswz(col);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row][pc]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row + 4][pc]));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
   }
+  // The operand fragments of one k-step (16 k) for this wave.
+  struct Frag {
+    bf16x8 a[4], b[2];
+  };
   template <bool KN, class BT>
-  __device__ __forceinline__ void kstep(const ATile &A, const BT &B, int ks) {
+  __device__ __forceinline__ static void load(const ATile &A, const BT &B, int ks, Frag &f) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, kc = ks * 2 + (lane >> 5);
-    bf16x8 a[4], b[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      if constexpr (KN) b[j] = bfrag_kn(B, j, ks);
-      else b[j] = bfrag_nk(B, j, ks);
+      if constexpr (KN) f.b[j] = bfrag_kn(B, j, ks);
+      else f.b[j] = bfrag_nk(B, j, ks);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8 *)&A.v[aswz(wm() * 128 + i * 32 + r, kc)];
+    for (int i = 0; i < 4; ++i) f.a[i] = *(const bf16x8 *)&A.v[aswz(wm() * 128 + i * 32 + r, kc)];
+  }
+  __device__ __forceinline__ void mma(const Frag &f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  }
+  template <bool KN, class BT>
+  __device__ __forceinline__ void kstep(const ATile &A, const BT &B, int ks) {
+    Frag f;
+    load<KN>(A, B, ks, f);
+    mma(f);
   }
   template <bool KN, class BT>
   __device__ __forceinline__ void step(const ATile &A, const BT &B, int ksteps) {

@@ -253,7 +253,9 @@ struct LargePipe {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       mma.template kstep<KN>(atile<P>(), btile<P>(), ks);
-      lb[P ^ 1].store_part(btile<P ^ 1>(), ks, tb);
+      float v[8];
+      lb[P ^ 1].lookup(ks, tb, v);
+      lb[P ^ 1].finish(btile<P ^ 1>(), ks, v);
     }
     slab_barrier<b_fetch_loads<KN, FMT>()>();  // the A rows of slab s+1 have landed
   }
@@ -263,7 +265,11 @@ struct LargePipe {
     fetch_b(1, 1, nmain);
     lb[0].prepare(tb);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) lb[0].store_part(btile<0>(), p, tb);
+    for (int p = 0; p < 4; ++p) {
+      float v[8];
+      lb[0].lookup(p, tb, v);
+      lb[0].finish(btile<0>(), p, v);
+    }
     wait_lds_dma();
     __syncthreads();
     for (int s = 0; s < nmain; s += 2) {
@@ -277,6 +283,8 @@ template <int BKIND, int EPI, bool SWIGLU, int FMT>
 __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
   // separate LDS objects, so the compiler can tell the A tiles that direct loads fill
   // from the B tiles and tables that ordinary LDS stores write
+  // (the largest alignment places the tables at LDS address 0, so table offsets fit the
+  // 16-bit immediate of the LDS reads)
   __shared__ DecodeTables tb;
   __shared__ ATile A0, A1;
   __shared__ LTile B0, B1;
