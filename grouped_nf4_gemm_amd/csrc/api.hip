@@ -81,7 +81,8 @@ static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
   L.z2 = take(M * r2 * 2);
   L.G = train ? take(M * 2 * I * 2) : NONE;
   L.h = take(M * I * 2);
-  L.O = take(M * H * 4);
+  // the decode-shaped forward keeps up to SMALL_MAX_SPLITS partial sums of O (inference only)
+  L.O = take((M <= (size_t)SMALL_M_MAX && !train ? SMALL_MAX_SPLITS : 1) * M * H * 4);
   if (train) {
     L.dO = take(M * H * 2);
     L.u2 = take(M * r2 * 2);
@@ -227,6 +228,10 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
 
   E4B_LAUNCH(launch_route(ids, M, E, cnt, off, perm, inv, s));
   if (M == 0) return E4B_OK;
+  // few routed rows: weight-streaming kernels (small.hip); otherwise the large tiles
+  const bool small = M <= SMALL_M_MAX;
+  const bool train = d.flags & E4B_TRAIN;
+  auto lora_a = [&](const GroupedArgs &a) { return small ? launch_small_lora_a(a, s) : launch_lora_a(a, s); };
 
   if (r1) {  // z1 = s1 * A1[e] x
     GroupedArgs a{};
@@ -234,7 +239,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.A = x; a.lda = H; a.a_gather = perm; a.a_gdiv = d.topk;
     a.Bd = l_gu->A; a.b_estride = (int64_t)r1 * H; a.ldb = H;
     a.C = z1; a.ldc = r1; a.alpha = l_gu->scaling;
-    E4B_LAUNCH(launch_lora_a(a, s));
+    E4B_LAUNCH(lora_a(a));
   }
   {  // h = silu(G_gate) * G_up, G = W1 x + B1 z1
     GroupedArgs a{};
@@ -246,7 +251,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.ldxb = r1; a.r = r1;
     a.C = h; a.ldc = I; a.alpha = 1.0f;
     a.Gout = G; a.ldg = 2 * I; a.I = I;
-    E4B_LAUNCH(launch_gemm_gate_up(a, s));
+    E4B_LAUNCH(small ? launch_small_gate_up(a, s) : launch_gemm_gate_up(a, s));
   }
   if (r2) {  // z2 = s2 * A2[e] h
     GroupedArgs a{};
@@ -254,8 +259,9 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.A = h; a.lda = I; a.a_gdiv = 1;
     a.Bd = l_dn->A; a.b_estride = (int64_t)r2 * I; a.ldb = I;
     a.C = z2; a.ldc = r2; a.alpha = l_dn->scaling;
-    E4B_LAUNCH(launch_lora_a(a, s));
+    E4B_LAUNCH(lora_a(a));
   }
+  int nsplit = 1;
   {  // O = W2 h + B2 z2
     GroupedArgs a{};
     a.off = off; a.E = E; a.M = M; a.N = H; a.K = I;
@@ -265,9 +271,14 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.xa = z2; a.ldxa = r2; a.xb = r2 ? l_dn->B : nullptr; a.xb_estride = (int64_t)H * r2;
     a.ldxb = r2; a.r = r2;
     a.C = O; a.ldc = H; a.alpha = 1.0f; a.I = I;
-    E4B_LAUNCH(launch_gemm_down(a, s));
+    if (small) {
+      nsplit = train ? 1 : small_down_splits(M, E, H, I);
+      E4B_LAUNCH(launch_small_down(a, nsplit, s));
+    } else {
+      E4B_LAUNCH(launch_gemm_down(a, s));
+    }
   }
-  E4B_LAUNCH(launch_combine(O, inv, topw, d.T, d.topk, H, y, s));
+  E4B_LAUNCH(launch_combine(O, nsplit, (int64_t)M * H, inv, topw, d.T, d.topk, H, y, s));
   return E4B_OK;
 }
 

@@ -24,6 +24,16 @@ enum Fmt : int { FMT_NF4 = 0, FMT_NF4_DQ = 1, FMT_MXFP4 = 2 };
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
+// nf4[q] without a memory access (a select chain over the literal values), for building
+// the per-workgroup LDS tables at kernel start without a global-memory round trip.
+__device__ __forceinline__ float nf4_value(uint32_t q) {
+  constexpr float v[16] = E4B_NF4_VALUES;
+  float r = v[15];
+#pragma unroll
+  for (int i = 14; i >= 0; --i) r = q == (uint32_t)i ? v[i] : r;
+  return r;
+}
+
 // Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;

@@ -12,7 +12,6 @@ namespace e4b {
 __constant__ float kNF4[16] = E4B_NF4_VALUES;
 __constant__ float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 
-static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // =============================================================== routing
 // One workgroup of 8 wave64s.  Wave w owns a contiguous range of flat indices.
@@ -110,7 +109,7 @@ bool launch_route(const int32_t *ids, int M, int E, int32_t *cnt, int32_t *off, 
 // Per-workgroup LDS decode tables (see DecodeTables).
 __device__ __forceinline__ void init_decode_tables(DecodeTables &t) {
   for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-    t.cb2[i] = make_float2(kNF4[i >> 4], kNF4[i & 15]);
+    t.cb2[i] = make_float2(nf4_value(i >> 4), nf4_value(i & 15));
     t.tab8[i] = (float)i / 255.0f;
   }
 }
@@ -473,32 +472,34 @@ bool launch_wgrad(const WgradArgs &a, hipStream_t s) {
 
 // =============================================================== combine and friends
 // y[t] = bf16(sum_j w[t,j] * O[inv[t*k+j]]), fp32 sum in j order.
-__global__ void combine_kernel(const float *__restrict__ O, const int32_t *__restrict__ inv,
-                               const float *__restrict__ topw, int k, int H,
-                               uint16_t *__restrict__ y) {
+__global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t split_stride,
+                               const int32_t *__restrict__ inv, const float *__restrict__ topw, int k,
+                               int H, uint16_t *__restrict__ y) {
+  // block (t, chunk of 1024 columns); thread -> 4 columns
   const int t = blockIdx.x;
-  for (int h = threadIdx.x * 4; h < H; h += blockDim.x * 4) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int p = inv[(int64_t)t * k + j];
-      if (p < 0) continue;
-      const float w = topw[(int64_t)t * k + j];
-      const f32x4 o = *(const f32x4 *)(O + (int64_t)p * H + h);
-      a0 += w * o[0];
-      a1 += w * o[1];
-      a2 += w * o[2];
-      a3 += w * o[3];
-    }
-    u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-    *(u32x2 *)(y + (int64_t)t * H + h) = out;
+  const int h = blockIdx.y * 1024 + threadIdx.x * 4;
+  if (h >= H) return;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int p = inv[(int64_t)t * k + j];
+    if (p < 0) continue;
+    const float w = topw[(int64_t)t * k + j];
+    f32x4 o = *(const f32x4 *)(O + (int64_t)p * H + h);
+    for (int c = 1; c < nsplit; ++c) o += *(const f32x4 *)(O + c * split_stride + (int64_t)p * H + h);
+    a0 += w * o[0];
+    a1 += w * o[1];
+    a2 += w * o[2];
+    a3 += w * o[3];
   }
+  u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+  *(u32x2 *)(y + (int64_t)t * H + h) = out;
 }
 
-bool launch_combine(const float *O, const int32_t *inv, const float *topw, int T, int k, int H,
-                    uint16_t *y, hipStream_t s) {
+bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int32_t *inv, const float *topw,
+                    int T, int k, int H, uint16_t *y, hipStream_t s) {
   if (T == 0) return true;
   LaunchScope ls(FAM_COMBINE, s);
-  combine_kernel<<<T, 256, 0, s>>>(O, inv, topw, k, H, y);
+  combine_kernel<<<dim3(T, cdiv(H, 1024)), 256, 0, s>>>(O, nsplit, split_stride, inv, topw, k, H, y);
   return last_launch_ok();
 }
 

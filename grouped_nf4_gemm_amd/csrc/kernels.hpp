@@ -7,6 +7,8 @@
 
 namespace e4b {
 
+static inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
 // Kernel families for launch counting and event timing.
 enum Family : int {
   FAM_ROUTE = 0,
@@ -103,8 +105,19 @@ struct WgradArgs {
 };
 bool launch_wgrad(const WgradArgs &a, hipStream_t s);
 
-bool launch_combine(const float *O, const int32_t *inv, const float *topw, int T, int k, int H,
-                    uint16_t *y, hipStream_t s);
+// y[t] = bf16(sum_j w[t,j] * O[inv[t,j]]); O holds `nsplit` partial sums, split_stride
+// floats apart, that are added in split order first.
+bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int32_t *inv, const float *topw,
+                    int T, int k, int H, uint16_t *y, hipStream_t s);
+
+// Decode-shaped forward (few routed rows per expert), see small.hip.  Used when the routed
+// rows of a call are at most SMALL_M_MAX.
+constexpr int SMALL_M_MAX = 256;
+constexpr int SMALL_MAX_SPLITS = 8;
+bool launch_small_lora_a(const GroupedArgs &a, hipStream_t s);
+bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s);
+int small_down_splits(int M, int E, int N, int K);
+bool launch_small_down(const GroupedArgs &a, int splits, hipStream_t s);
 bool launch_combine_bwd(const uint16_t *dy, const float *O, const int32_t *inv, const float *topw,
                         int T, int k, int H, uint16_t *dO, float *d_topw, hipStream_t s);
 bool launch_unpermute(const float *dXp, const int32_t *inv, int T, int k, int H, uint16_t *dx,
