@@ -57,22 +57,54 @@ __device__ __forceinline__ bf16x8 nf4_codes_bf16(uint32_t w, uint32_t l4, const 
   return __builtin_bit_cast(bf16x8, r);
 }
 
-constexpr int SM_THREADS = 256;  // four waves
-constexpr int SM_BMT = 32;       // tokens per workgroup slot
+constexpr int SM_WAVES = 8, SM_THREADS = 64 * SM_WAVES;
+constexpr int SM_BMT = 32;                  // tokens per workgroup slot
+constexpr int SM_CB = 4;                    // 64-wide blocks per chunk
+constexpr int SM_XSTRIDE = SM_CB * 64 + 8;  // staged activation row: 256 bf16 + 16 bytes
 
-template <int FMT>
-struct SmallScale {
-  uint32_t raw;
-  float s2;
+// Activations of one chunk for the slot's tokens, double-buffered: row t = token t of the
+// slot (zero past its rows).  The 16-byte row padding spreads the 32 fragment reads of a
+// k column over all banks.
+struct SmallX {
+  uint16_t v[2][SM_BMT][SM_XSTRIDE];
 };
 
-template <int FMT, int SPW, int EPI, int D>
+__device__ __forceinline__ uint32_t byte_at(const u32x4 &r, uint32_t o) {
+  const uint32_t w = o < 4 ? r[0] : o < 8 ? r[1] : o < 12 ? r[2] : r[3];
+  return (w >> (8 * (o & 3))) & 0xffu;
+}
+
+// Raw scales of one chunk (4 blocks) of one weight row, read as one 16-byte window that
+// starts `sh` bytes before them (the window is moved back to stay inside the scale
+// array): NF4: 4 fp32 absmax at sh + 4b; NF4_DQ: 4 absmax codes at sh + b, plus the
+// second-level scales of the chunk's first and last block; MXFP4: this lane's E8M0 byte
+// of block b at sh + 2b.
+struct ChunkScale {
+  u32x4 raw;
+  uint32_t sh;
+  float s2a, s2b;
+};
+
+// LDS barrier that leaves vector-memory loads in flight: waits for this wave's LDS
+// accesses only (vmcnt and expcnt at their maximum, lgkmcnt(0)).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int FMT, int SPW, int EPI, int DC>
 __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, int kb_per_split,
                                                                  int64_t split_stride) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
-  // the table lives in dynamic LDS, sized at launch: NF4 formats only
+  constexpr int R = DC + 1;  // chunk slots of the register ring
+  // the code table lives in dynamic LDS, sized at launch (NF4 formats only)
   extern __shared__ __attribute__((aligned(16))) uint32_t small_lds[];
   SmallTables &tb = *reinterpret_cast<SmallTables *>(small_lds);
+  __shared__ SmallX xs;
   __shared__ int tile_sh[4];
   if constexpr (NF4ISH) init_small_tables(tb);
   TileM tm;
@@ -83,19 +115,22 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   const uint32_t l4 = (uint32_t)lane * 4;
   const int N = g.q.N, K = g.q.K, KB = K / 64;
   const int kb0 = blockIdx.z * kb_per_split, kb1 = min(KB, kb0 + kb_per_split);
+  const int nchunks = max(0, (kb1 - kb0 + SM_CB - 1) / SM_CB);
 
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.q.codes, g.q.codes_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.q.scale, g.q.scale_bytes);
   const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(g.q.scale2, g.q.scale2_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(g.A, g.a_bytes);
+  // last 4-byte aligned start of a 16-byte scale window inside the scale array
+  const uint32_t slast = g.q.scale_bytes >= 16 ? (g.q.scale_bytes - 16) & ~3u : 0u;
 
-  // this lane's weight row in each strip, its code and scale offsets at block 0
+  // this lane's weight row in each strip; code and scale offsets at block kb0
   int row[SPW];
-  uint32_t cbase[SPW], sbase[SPW];
+  uint32_t cbase[SPW], sbase[SPW], ssh[SPW];
   int64_t blk0[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
-    const int st = (blockIdx.x * 4 + w) * SPW + s;
+    const int st = (blockIdx.x * SM_WAVES + w) * SPW + s;
     bool ok;
     if constexpr (EPI == EPI_SWIGLU_FWD) {
       const int i = st * 16 + (n & 15);
@@ -106,102 +141,144 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
       ok = row[s] < N;
     }
     const int64_t el = ((int64_t)e * N + row[s]) * K;
-    blk0[s] = el >> 6;
-    cbase[s] = ok ? (uint32_t)(el / 2) + 16 * hh : OOB;
-    sbase[s] = !ok ? OOB
-               : FMT == FMT_NF4 ? (uint32_t)(blk0[s] * 4)
-               : FMT == FMT_NF4_DQ ? (uint32_t)blk0[s]
-                                   : (uint32_t)(el >> 5) + hh;
+    blk0[s] = (el >> 6) + kb0;
+    cbase[s] = ok ? (uint32_t)(el / 2) + (uint32_t)kb0 * 32 + 16 * hh : OOB;
+    // scale windows: NF4 byte 4*blk; NF4_DQ byte blk; MXFP4 byte (el >> 5) + 2 kb + h,
+    // each read from the 4-byte aligned address at or below it
+    const uint32_t sb = FMT == FMT_NF4 ? (uint32_t)(blk0[s] * 4)
+                        : FMT == FMT_NF4_DQ ? (uint32_t)blk0[s]
+                                            : (uint32_t)(el >> 5) + 2u * kb0 + hh;
+    ssh[s] = sb & 3u;
+    sbase[s] = ok ? (sb & ~3u) : OOB;
     if (!ok) row[s] = -1;
   }
-  // activation row of this lane (token n of the slot)
-  const int tok = n;
-  uint32_t avoff = OOB;
-  if (tok < tm.rows) {
-    const int64_t p = tm.row0 + tok;
+  // activation staging: thread -> token row t / 16, 16 elements at 16 * (t % 16) of a chunk
+  const int xrow = threadIdx.x >> 4, xpiece = threadIdx.x & 15;
+  uint32_t xoff = OOB;
+  if (xrow < tm.rows) {
+    const int64_t p = tm.row0 + xrow;
     const int64_t src = g.a_gather ? (int64_t)(g.a_gather[p] / g.a_gdiv) : p;
-    avoff = (uint32_t)((src * g.lda + 32 * hh) * 2);
+    xoff = (uint32_t)((src * g.lda + (int64_t)kb0 * 64 + 16 * xpiece) * 2);
   }
 
-  constexpr int R = D + 1;  // ring slots
-  u32x4 cw[R][SPW];
-  SmallScale<FMT> sr[R][SPW];
-  bf16x8 av[R][4];
+  u32x4 cw[R][SPW][SM_CB];
+  ChunkScale cs[R][SPW];
+  u32x4 xr[2];
   f32x16 acc[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[s][v] = 0.0f;
 
-  auto load_b = [&](int slot, int kb) {
-    const uint32_t dead = kb < kb1 ? 0u : OOB;
+  auto load_x = [&](int c) {
+    const uint32_t dead = c < nchunks ? 0u : OOB;
+    xr[0] = bload128(ra, xoff, ((uint32_t)c * SM_CB * 128) | dead);
+    xr[1] = bload128(ra, xoff, ((uint32_t)c * SM_CB * 128 + 16) | dead);
+  };
+  auto store_x = [&](int c) {
+    uint16_t *dst = &xs.v[c & 1][xrow][16 * xpiece];
+    *(u32x4 *)dst = xr[0];
+    *(u32x4 *)(dst + 8) = xr[1];
+  };
+  auto load_w = [&](int slot, int c) {
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
-      cw[slot][s] = bload128(rc, cbase[s], ((uint32_t)kb * 32) | dead);
-      if constexpr (FMT == FMT_NF4) {
-        sr[slot][s].raw = bload32(rs, sbase[s], ((uint32_t)kb * 4) | dead);
-      } else if constexpr (FMT == FMT_NF4_DQ) {
-        sr[slot][s].raw = bload8(rs, sbase[s], (uint32_t)kb | dead);
-        const uint32_t s2off = sbase[s] == OOB ? OOB : (uint32_t)((blk0[s] + kb) >> 8) * 4;
-        sr[slot][s].s2 = __uint_as_float(bload32(rs2, s2off, dead));
-      } else {
-        sr[slot][s].raw = bload8(rs, sbase[s], ((uint32_t)kb * 2) | dead);
+#pragma unroll
+      for (int b = 0; b < SM_CB; ++b) {
+        const int kb = kb0 + c * SM_CB + b;
+        cw[slot][s][b] = bload128(rc, cbase[s], ((uint32_t)(c * SM_CB + b) * 32) | (kb < kb1 ? 0u : OOB));
+      }
+      const uint32_t dead = c < nchunks ? 0u : OOB;
+      const uint32_t step = FMT == FMT_NF4 ? SM_CB * 4 : FMT == FMT_NF4_DQ ? SM_CB : SM_CB * 2;
+      uint32_t win = OOB, sh = 0;
+      if (sbase[s] != OOB) {
+        const uint32_t at = sbase[s] + (uint32_t)c * step;
+        win = min(at, slast);
+        sh = ssh[s] + (at - win);
+      }
+      cs[slot][s].raw = bload128(rs, win, dead);
+      cs[slot][s].sh = sh;
+      if constexpr (FMT == FMT_NF4_DQ) {
+        const uint32_t s2off = sbase[s] == OOB ? OOB : (uint32_t)((blk0[s] + c * SM_CB) >> 8) * 4;
+        const uint32_t s2offb = sbase[s] == OOB ? OOB : (uint32_t)((blk0[s] + c * SM_CB + SM_CB - 1) >> 8) * 4;
+        cs[slot][s].s2a = __uint_as_float(bload32(rs2, s2off, dead));
+        cs[slot][s].s2b = __uint_as_float(bload32(rs2, s2offb, dead));
       }
     }
   };
-  auto load_a = [&](int slot, int kb) {
-    const uint32_t dead = kb < kb1 ? 0u : OOB;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
-      av[slot][s4] = __builtin_bit_cast(bf16x8, bload128(ra, avoff, ((uint32_t)kb * 128 + s4 * 16) | dead));
+  // scale of block b of the chunk in `slot` for strip s
+  auto scale_of = [&](int slot, int s, int b, int c) -> float {
+    if constexpr (FMT == FMT_NF4) {
+      const uint32_t o = cs[slot][s].sh + 4 * b;  // a multiple of 4
+      const u32x4 &r = cs[slot][s].raw;
+      return __uint_as_float(o < 4 ? r[0] : o < 8 ? r[1] : o < 12 ? r[2] : r[3]);
+    } else if constexpr (FMT == FMT_NF4_DQ) {
+      const uint32_t code = byte_at(cs[slot][s].raw, cs[slot][s].sh + b);
+      const bool second = ((blk0[s] + c * SM_CB + b) >> 8) != ((blk0[s] + c * SM_CB) >> 8);
+      return ((float)code / 255.0f) * (second ? cs[slot][s].s2b : cs[slot][s].s2a);
+    } else {
+      return e8m0_to_f32(byte_at(cs[slot][s].raw, cs[slot][s].sh + 2 * b));
+    }
   };
 
-  // prologue: the first D blocks
+  // prologue: activations of chunk 0 (waited for at once, so issued first), then the
+  // weights of chunks 0 .. DC-1 in slot order
+  __builtin_amdgcn_sched_barrier(0);
+  load_x(0);
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    __builtin_amdgcn_sched_barrier(0);  // in slot order, as in the loop
-    load_a(d, kb0 + d);
-    load_b(d, kb0 + d);
+  for (int d = 0; d < DC; ++d) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(d, d);
   }
   __builtin_amdgcn_sched_barrier(0);
+  store_x(0);
+  lds_barrier();
 
-  // The body is straight-line: a block past kb1 has zero codes, scales and activations
-  // (out-of-range loads) and adds nothing, and the exact wait counts survive.
-  for (int kb = kb0; kb < kb1; kb += R) {
+  for (int cb = 0; cb < nchunks; cb += R) {
 #pragma unroll
     for (int d = 0; d < R; ++d) {
-      const int k = kb + d;  // block k sits in slot d
-      {
-        __builtin_amdgcn_sched_barrier(0);
-        load_a((d + D) % R, k + D);
-        load_b((d + D) % R, k + D);
-        __builtin_amdgcn_sched_barrier(0);
+      const int c = cb + d;  // chunk c sits in slot d; its activations in xs.v[c & 1]
+      // loads: activations of chunk c+1 first (needed at the end of this step), then
+      // the weights of chunk c+DC into the slot the previous step freed
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(c + 1);
+      load_w((d + DC) % R, c + DC);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t *xb = &xs.v[c & 1][n][32 * hh];
+#pragma unroll
+      for (int b = 0; b < SM_CB; ++b) {
+        bf16x8 af[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) af[s4] = *(const bf16x8 *)(xb + 64 * b + 8 * s4);
+        // a block past kb1 reads zero codes, which are nf4 code 0 (-1), against staged
+        // activations that are not zero: its scale is set to zero instead
+        const bool live = kb0 + c * SM_CB + b < kb1;
 #pragma unroll
         for (int s = 0; s < SPW; ++s) {
+          const float sc = live ? scale_of(d, s, b, c) : 0.0f;
           if constexpr (NF4ISH) {
-            float sc;
-            if constexpr (FMT == FMT_NF4) sc = __uint_as_float(sr[d][s].raw);
-            else sc = ((float)sr[d][s].raw / 255.0f) * sr[d][s].s2;
             f32x16 blk = {};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4)
-              blk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[d][s4], nf4_codes_bf16(cw[d][s][s4], l4, tb),
-                                                            blk, 0, 0, 0);
+              blk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s4], nf4_codes_bf16(cw[d][s][b][s4], l4, tb), blk,
+                                                            0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[s][v] += sc * blk[v];
           } else {
-            const float sc = e8m0_to_f32(sr[d][s].raw);
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4)
-              acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[d][s4], __builtin_bit_cast(bf16x8,
-                           mxfp4_word_to_bf16(cw[d][s][s4], sc)), acc[s], 0, 0, 0);
+              acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  af[s4], __builtin_bit_cast(bf16x8, mxfp4_word_to_bf16(cw[d][s][b][s4], sc)), acc[s], 0, 0, 0);
           }
         }
       }
+      store_x(c + 1);
+      lds_barrier();
     }
   }
 
   // LoRA K-extension (first split only): acc += z . B[e]^T over the adapter rank
+  const int tok = n;
   if (g.r > 0 && blockIdx.z == 0) {
     for (int kk = 0; kk < g.r; kk += 16) {
       const int kc = kk + 8 * hh;
@@ -221,7 +298,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     if constexpr (EPI == EPI_SWIGLU_FWD) {
-      const int i = ((blockIdx.x * 4 + w) * SPW + s) * 16 + (n & 15);
+      const int i = ((blockIdx.x * SM_WAVES + w) * SPW + s) * 16 + (n & 15);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float mine = acc[s][v];
@@ -250,24 +327,263 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   }
 }
 
-// Strips per wave: the largest of 4, 2, 1 that still gives about two waves per SIMD.
-static int pick_spw(int64_t strips) {
-  if (strips / 4 >= 2048) return 4;
-  if (strips / 2 >= 2048) return 2;
-  return 1;
+// Variant for few tokens per expert: workgroup slots of at most XMAX tokens, whose
+// activation rows over the whole K range of the split are staged in LDS once; the lanes
+// of the other token rows read a zero line (one address for all of them, a broadcast),
+// so the loop streams only codes and scales: one 16-byte code load per block and one
+// scale window per 4 blocks, in a ring of 8 block slots loaded 7 blocks ahead.  The
+// operands of block j+1 (activation fragments, table reads, scale) are read while the
+// MFMAs of block j run.  Eight waves per workgroup, one strip each.
+constexpr int XMAX = 8;
+constexpr int XPT = 8;  // staged 16-byte activation pieces per thread: rows x blocks <= 512
+
+template <int FMT, int EPI>
+__global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g, int kb_per_split,
+                                                                   int64_t split_stride) {
+  constexpr bool NF4ISH = FMT != FMT_MXFP4;
+  constexpr int D = 7, R = 8;
+  // dynamic LDS: the code table (NF4 formats), then the staged activation rows
+  // [rows][blocks of the split][64]
+  extern __shared__ __attribute__((aligned(16))) uint32_t small_lds[];
+  SmallTables &tb = *reinterpret_cast<SmallTables *>(small_lds);
+  uint16_t *xs = (uint16_t *)(small_lds + (NF4ISH ? sizeof(SmallTables) / 4 : 0));
+  __shared__ __attribute__((aligned(16))) uint16_t xzero[64];
+  __shared__ int tile_sh[4];
+  if (threadIdx.x < 8) *(u32x4 *)&xzero[threadIdx.x * 8] = u32x4{0, 0, 0, 0};
+  TileM tm;
+  if (!find_tile(g.off, g.E, XMAX, blockIdx.y, tm, tile_sh)) return;  // (synchronises)
+  const int e = tm.e;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const uint32_t l4 = (uint32_t)lane * 4;
+  const int N = g.q.N, K = g.q.K, KB = K / 64;
+  const int kb0 = blockIdx.z * kb_per_split, kb1 = min(KB, kb0 + kb_per_split);
+  const int nblk = max(0, kb1 - kb0);
+
+  const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.q.codes, g.q.codes_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.q.scale, g.q.scale_bytes);
+  const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(g.q.scale2, g.q.scale2_bytes);
+  const uint32_t slast = g.q.scale_bytes >= 16 ? (g.q.scale_bytes - 16) & ~3u : 0u;
+
+  int row;
+  bool ok;
+  {
+    const int st = blockIdx.x * SM_WAVES + w;
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      const int i = st * 16 + (n & 15);
+      ok = i < g.I;
+      row = n < 16 ? i : g.I + i;
+    } else {
+      row = st * 32 + n;
+      ok = row < N;
+    }
+  }
+  const int64_t el = ((int64_t)e * N + row) * K;
+  const int64_t blk0 = (el >> 6) + kb0;
+  const uint32_t cbase = ok ? (uint32_t)(el / 2) + (uint32_t)kb0 * 32 + 16 * hh : OOB;
+  const uint32_t sb = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4)
+                      : FMT == FMT_NF4_DQ ? (uint32_t)blk0
+                                          : (uint32_t)(el >> 5) + 2u * kb0 + hh;
+  const uint32_t ssh = sb & 3u, sbase = ok ? (sb & ~3u) : OOB;
+  if (!ok) row = -1;
+
+  {
+    const int t0 = 0, xrows = tm.rows;
+    const int xrow_len = nblk * 64;  // staged elements per token row
+    // Start-up latency is overlapped: the activation pieces are loaded first, then the
+    // first D blocks of codes, then the table is built, and only then do the pieces go
+    // to LDS (waiting for them does not wait for the younger code loads).
+    u32x4 xp[XPT];
+    const int npieces = xrows * nblk * 8;
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int i = threadIdx.x + u * SM_THREADS;
+      xp[u] = u32x4{0, 0, 0, 0};
+      if (i < npieces) {
+        const int xr = i / (nblk * 8), piece = i - xr * (nblk * 8);
+        const int64_t p = tm.row0 + xr;
+        const int64_t src = g.a_gather ? (int64_t)(g.a_gather[p] / g.a_gdiv) : p;
+        xp[u] = *(const u32x4 *)(g.A + src * g.lda + (int64_t)kb0 * 64 + piece * 8);
+      }
+    }
+    const int tok = n;
+    const bool xlane = tok >= t0 && tok < t0 + xrows;
+    // fragment source of this lane: its token row, or the zero line (stride 0)
+    const uint16_t *xsrc = xlane ? xs + (tok - t0) * xrow_len + 32 * hh : xzero;
+    const int xstep = xlane ? 1 : 0;
+
+    u32x4 cw[R];
+    ChunkScale sq[R / 4], cur;
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+
+    auto load_blk = [&](int slot, int j) {
+      const uint32_t dead = j < nblk ? 0u : OOB;
+      cw[slot] = bload128(rc, cbase, ((uint32_t)j * 32) | dead);
+      if (slot % 4 == 0) {  // the scales of blocks j .. j+3
+        const uint32_t step = FMT == FMT_NF4 ? 16u : FMT == FMT_NF4_DQ ? 4u : 8u;
+        ChunkScale &q = sq[slot / 4];
+        uint32_t win = OOB, sh = 0;
+        if (sbase != OOB) {
+          const uint32_t at = sbase + (uint32_t)(j / 4) * step;
+          win = min(at, slast);
+          sh = ssh + (at - win);
+        }
+        q.raw = bload128(rs, win, dead);
+        q.sh = sh;
+        if constexpr (FMT == FMT_NF4_DQ) {
+          q.s2a = __uint_as_float(bload32(rs2, sbase == OOB ? OOB : (uint32_t)((blk0 + j) >> 8) * 4, dead));
+          q.s2b = __uint_as_float(bload32(rs2, sbase == OOB ? OOB : (uint32_t)((blk0 + j + 3) >> 8) * 4, dead));
+        }
+      }
+    };
+    // scale of block j (slot d) from the quad window `q`, block b = j % 4 of it
+    auto scale_in = [&](const ChunkScale &q, int b, int j) -> float {
+      if constexpr (FMT == FMT_NF4) {
+        const uint32_t o = q.sh + 4 * b;
+        return __uint_as_float(o < 4 ? q.raw[0] : o < 8 ? q.raw[1] : o < 12 ? q.raw[2] : q.raw[3]);
+      } else if constexpr (FMT == FMT_NF4_DQ) {
+        const uint32_t code = byte_at(q.raw, q.sh + b);
+        const bool second = ((blk0 + j) >> 8) != ((blk0 + j - b) >> 8);
+        return ((float)code / 255.0f) * (second ? q.s2b : q.s2a);
+      } else {
+        return e8m0_to_f32(byte_at(q.raw, q.sh + 2 * b));
+      }
+    };
+    // operands of block j in slot d: activation fragments, B fragments, scale
+    struct Ops {
+      bf16x8 a[4], b[4];
+      float sc;
+    };
+    auto prepare = [&](int d, int j, Ops &o) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      // only the lanes of real tokens read activations (the others hold zeros), so the
+      // LDS traffic of the fragments scales with the tokens, not with the 32 MFMA rows
+      if (xlane) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xsrc + 64 * j + 8 * s4);
+      }
+      // the quad of block j: in the slot's own window if j starts it, else in `cur`
+      const float sc = d % 4 == 0 ? scale_in(sq[d / 4], 0, j) : scale_in(cur, d % 4, j);
+      // a block past the range has zero codes (nf4 code 0 = -1): zero its scale
+      o.sc = j < nblk ? sc : 0.0f;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        if constexpr (NF4ISH) o.b[s4] = nf4_codes_bf16(cw[d][s4], l4, tb);
+        else o.b[s4] = __builtin_bit_cast(bf16x8, mxfp4_word_to_bf16(cw[d][s4], o.sc));
+      }
+    };
+    auto compute = [&](const Ops &o) {
+      if constexpr (NF4ISH) {
+        f32x16 blk = {};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) blk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[s4], o.b[s4], blk, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] += o.sc * blk[v];
+      } else {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[s4], o.b[s4], acc, 0, 0, 0);
+      }
+    };
+
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_blk(d, d);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NF4ISH) init_small_tables(tb);
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+      const int i = threadIdx.x + u * SM_THREADS;
+      if (i < npieces) *(u32x4 *)(xs + i * 8) = xp[u];  // piece i = row i / (8 nblk), same order
+    }
+    lds_barrier();
+
+    Ops ops[2];
+    prepare(0, 0, ops[0]);
+    for (int jb = 0; jb < nblk; jb += R) {
+#pragma unroll
+      for (int d = 0; d < R; ++d) {
+        const int j = jb + d;  // block j sits in slot d; its operands are in ops[d & 1]
+        __builtin_amdgcn_sched_barrier(0);
+        if (d % 4 == 0) cur = sq[d / 4];  // before the next step refills the slot holding it
+        load_blk((d + D) % R, j + D);
+        __builtin_amdgcn_sched_barrier(0);
+        prepare((d + 1) % R, j + 1, ops[(d + 1) & 1]);
+        compute(ops[d & 1]);
+      }
+    }
+
+    if (g.r > 0 && blockIdx.z == 0) {
+      for (int kk = 0; kk < g.r; kk += 16) {
+        const int kc = kk + 8 * hh;
+        u32x4 za = {0, 0, 0, 0}, zb = {0, 0, 0, 0};
+        if (xlane && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
+        if (row >= 0 && kc < g.r) zb = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + kc);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, za), __builtin_bit_cast(bf16x8, zb),
+                                                      acc, 0, 0, 0);
+      }
+    }
+    // accumulator rows are the slot's tokens: write those of this pass
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      const int i = (blockIdx.x * SM_WAVES + w) * 16 + (n & 15);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float mine = acc[v];
+        const float other = __shfl_xor(mine, 16);
+        const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (n < 16 && i < g.I && t >= t0 && t < t0 + xrows) {
+          const int64_t p = tm.row0 + t;
+          const float gt = mine, up = other;
+          const float act = gt / (1.0f + expf(-gt));
+          ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(act * up);
+          if (g.Gout) {
+            g.Gout[p * g.ldg + i] = f2bf(gt);
+            g.Gout[p * g.ldg + g.I + i] = f2bf(up);
+          }
+        }
+      }
+    } else if (row >= 0) {
+      float *out = (float *)g.C + blockIdx.z * split_stride;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (t >= t0 && t < t0 + xrows) out[(tm.row0 + t) * g.ldc + row] = acc[v];
+      }
+    }
+  }
+}
+
+// Strips (32 weight rows) per wave.  One: a second strip would double the register ring
+// and spill.
+static int pick_spw(int64_t) { return 1; }
+
+// Upper bound on the workgroup slots of bmt tokens over the experts' row segments.
+static int small_slots(int M, int E, int bmt) { return cdiv(M, bmt) + min(E, M); }
+
+// Few tokens per touched expert (at most 2 on average) and staged activations that fit
+// the per-thread pieces: the direct variant.
+static int direct_rows(const GroupedArgs &a) { return min(XMAX, a.M); }
+static bool use_direct(const GroupedArgs &a, int kbs) {
+  return a.M <= 2 * min(a.E, a.M) && direct_rows(a) * kbs * 8 <= XPT * SM_THREADS;
 }
 
 template <int FMT, int EPI>
 static void launch_small_fmt(const GroupedArgs &a, int spw, int strips_per_expert, int slots, int splits,
                              int kbs, int64_t split_stride, hipStream_t s) {
-  // codes in flight per wave: D blocks of SPW strips
-  const int per_wg = 4 * spw;
-  const dim3 grid(cdiv(strips_per_expert, per_wg), slots, splits);
   const size_t lds = FMT == FMT_MXFP4 ? 0 : sizeof(SmallTables);
-  switch (spw) {
-    case 4: small_gemm_kernel<FMT, 4, EPI, 2><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride); break;
-    case 2: small_gemm_kernel<FMT, 2, EPI, 4><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride); break;
-    default: small_gemm_kernel<FMT, 1, EPI, 6><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride); break;
+  (void)spw;
+  (void)slots;
+  if (use_direct(a, kbs)) {
+    const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, XMAX), splits);
+    const size_t xlds = (size_t)direct_rows(a) * kbs * 64 * 2;
+    small_direct_kernel<FMT, EPI><<<grid, SM_THREADS, lds + xlds, s>>>(a, kbs, split_stride);
+  } else {
+    const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, SM_BMT), splits);
+    small_gemm_kernel<FMT, 1, EPI, 2><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride);
   }
 }
 
@@ -281,7 +597,6 @@ static void launch_small(const GroupedArgs &a, int spw, int strips_per_expert, i
   }
 }
 
-static int small_slots(int M, int E) { return cdiv(M, SM_BMT) + min(E, M); }
 
 bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
@@ -289,16 +604,17 @@ bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s) {
   const int strips_per_expert = cdiv(a.I, 16);
   const int64_t strips = (int64_t)strips_per_expert * min(a.E, a.M);
   const int KB = a.K / 64;
-  launch_small<EPI_SWIGLU_FWD>(a, pick_spw(strips), strips_per_expert, small_slots(a.M, a.E), 1, KB, 0, s);
+  launch_small<EPI_SWIGLU_FWD>(a, pick_spw(strips), strips_per_expert, 0, 1, KB, 0, s);
   return last_launch_ok();
 }
 
+// K splits of down: enough waves for the device, each split a whole number of chunks.
 int small_down_splits(int M, int E, int N, int K) {
   const int64_t strips = (int64_t)cdiv(N, 32) * min(E, M);
-  const int spw = pick_spw(strips);
-  const int64_t waves = strips / spw;
+  const int64_t waves = strips / pick_spw(strips);
   int splits = (int)((2048 + waves - 1) / waves);
-  splits = max(1, min(splits, min(SMALL_MAX_SPLITS, K / 64 / 8)));
+  const int chunks = cdiv(K / 64, SM_CB);
+  splits = max(1, min(splits, min(SMALL_MAX_SPLITS, chunks / 4)));
   return splits;
 }
 
@@ -308,9 +624,8 @@ bool launch_small_down(const GroupedArgs &a, int splits, hipStream_t s) {
   const int strips_per_expert = cdiv(a.N, 32);
   const int64_t strips = (int64_t)strips_per_expert * min(a.E, a.M);
   const int KB = a.K / 64;
-  const int kbs = cdiv(KB, splits);
-  launch_small<EPI_F32>(a, pick_spw(strips), strips_per_expert, small_slots(a.M, a.E), splits, kbs,
-                        (int64_t)a.M * a.ldc, s);
+  const int kbs = cdiv(cdiv(KB, splits), SM_CB) * SM_CB;
+  launch_small<EPI_F32>(a, pick_spw(strips), strips_per_expert, 0, splits, kbs, (int64_t)a.M * a.ldc, s);
   return last_launch_ok();
 }
 
