@@ -34,6 +34,12 @@ __device__ __forceinline__ float nf4_value(uint32_t q) {
   return r;
 }
 
+// Logistic sigmoid 1 / (1 + e^-x) from the hardware base-2 exponential and reciprocal
+// (each within about one ulp); saturates to 0 and 1 for large |x|.
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
 // Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;
@@ -81,6 +87,43 @@ __device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, cons
   float v[8];
   nf4_lookup(w, t, v);
   return nf4_scale_pack(v, absmax);
+}
+
+// Register-resident decode table of one NF4 block: the sixteen values e[q] = bf16(nf4[q] *
+// absmax) (the same rounding as nf4_scale_pack) split into byte planes, pl[i] = low bytes of
+// e[4i .. 4i+3] and pl[4 + i] = their high bytes (i < 4), so that byte permutes can look up
+// four codes at a time without touching LDS.
+__device__ __forceinline__ void nf4_planes(float absmax, uint32_t (&pl)[8]) {
+  constexpr float v[16] = E4B_NF4_VALUES;
+  uint32_t e[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) e[k] = pack_bf16x2(v[2 * k] * absmax, v[2 * k + 1] * absmax);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pl[i] = __builtin_amdgcn_perm(e[2 * i + 1], e[2 * i], 0x06040200u);
+    pl[4 + i] = __builtin_amdgcn_perm(e[2 * i + 1], e[2 * i], 0x07050301u);
+  }
+}
+// The 8 codes of one 32-bit word (element 2j in the high nibble of byte j) to 8 bf16 values
+// through the planes of nf4_planes.  v_perm_b32 picks byte s (0..7) of the pair {S0:S1}, so a
+// code q reads entry q & 7 of planes 0-1 or of planes 2-3, chosen per byte by q >= 8.  For the
+// choice, q + 0x78 has bit 7 set exactly when q >= 8, and the selectors 8..11 of v_perm_b32
+// replicate bit 7 of bytes 1, 3, 5, 7 of the pair into a whole byte.
+__device__ __forceinline__ u32x4 nf4_decode_planes(uint32_t w, const uint32_t (&pl)[8]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 2j+1, codes 2j
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t q = __builtin_amdgcn_perm(lo, hi, p == 0 ? 0x05010400u : 0x07030602u);  // codes 4p..4p+3
+    const uint32_t x = q + 0x78787878u;
+    const uint32_t m = __builtin_amdgcn_perm(x, x << 8, 0x0B090A08u);  // 0xFF in bytes with q >= 8
+    const uint32_t s = q & 0x07070707u;
+    const uint32_t L = (__builtin_amdgcn_perm(pl[3], pl[2], s) & m) | (__builtin_amdgcn_perm(pl[1], pl[0], s) & ~m);
+    const uint32_t H = (__builtin_amdgcn_perm(pl[7], pl[6], s) & m) | (__builtin_amdgcn_perm(pl[5], pl[4], s) & ~m);
+    out[2 * p] = __builtin_amdgcn_perm(H, L, 0x05010400u);
+    out[2 * p + 1] = __builtin_amdgcn_perm(H, L, 0x07030602u);
+  }
+  return out;
 }
 
 // Decode the 8 E2M1 codes of one 32-bit word (element 2j in the low nibble of

@@ -293,15 +293,6 @@ __device__ __forceinline__ int knswz(int col) {
 }
 static_assert(sizeof(LTileKN) <= sizeof(LTile), "B tile layouts share one buffer");
 
-// Shared memory of the large tile.  The decode tables come first so their LDS address is
-// zero and a table index is directly an LDS address.
-struct LargeSmem {
-  DecodeTables tb;
-  ATile A0, A1;
-  LTile B0, B1;
-  int tile[4];
-};
-
 // A: 256 rows x 64 k of a row-major bf16 matrix (optionally gathered rows) loaded
 // straight into LDS.  Wave w, instruction i fills the 1 KB block of rows 8*(4w+i) ..
 // +7: lane l reads row 8*(4w+i) + l/8, logical chunk (l%8) ^ (l/8).
@@ -360,17 +351,21 @@ __device__ __forceinline__ float group_scale(uint32_t raw, float s2, const Decod
   else if constexpr (FMT == FMT_NF4_DQ) return tb.tab8[raw] * s2;
   else return e8m0_to_f32(raw);
 }
-// Decode in two steps, so the table reads can be issued ahead of the MFMAs that hide
-// their latency: lookup (NF4 formats: 8 LDS reads; MXFP4: nothing) and finish.
+// Per-slab decode state: the block scale, and for the NF4 formats the byte planes of the
+// sixteen scaled values (the 4-bit codes are then decoded with byte permutes, no LDS reads).
 template <int FMT>
-__device__ __forceinline__ void decode_lookup(uint32_t w, const DecodeTables &tb, float (&v)[8]) {
-  if constexpr (FMT != FMT_MXFP4) nf4_lookup(w, tb, v);
-}
-template <int FMT>
-__device__ __forceinline__ u32x4 decode_finish(uint32_t w, float sc, const float (&v)[8]) {
-  if constexpr (FMT == FMT_MXFP4) return mxfp4_word_to_bf16(w, sc);
-  else return nf4_scale_pack(v, sc);
-}
+struct GroupDecoder {
+  float sc;
+  uint32_t pl[8];
+  __device__ __forceinline__ void prepare(uint32_t raw, float s2, const DecodeTables &tb) {
+    sc = group_scale<FMT>(raw, s2, tb);
+    if constexpr (FMT != FMT_MXFP4) nf4_planes(sc, pl);
+  }
+  __device__ __forceinline__ u32x4 operator()(uint32_t w) const {
+    if constexpr (FMT == FMT_MXFP4) return mxfp4_word_to_bf16(w, sc);
+    else return nf4_decode_planes(w, pl);
+  }
+};
 // Raw scale fetch of one group: NF4 fp32 absmax, NF4_DQ 8-bit code (+ its second-level
 // scale, through buffer rs2), MXFP4 E8M0 byte.  `dead` = OOB turns the loads into zero reads.
 template <int FMT>
@@ -393,7 +388,8 @@ template <int FMT>
 struct LQuantNK {
   u32x4 codes;
   uint32_t sraw;
-  float s2, sc;
+  float s2;
+  GroupDecoder<FMT> dec;
   uint32_t cvoff, svoff;  // byte offsets at k0 = 0
   int64_t blk0;
   __device__ __forceinline__ void init(const QStack &q, int e, const RowMap &map, int Nrows) {
@@ -416,12 +412,10 @@ struct LQuantNK {
                                                                                        : (uint32_t)(k0 / 32);
     fetch_scale<FMT>(rs, rs2, svoff, soff, blk0 + k0 / 64, dead, sraw, s2);
   }
-  __device__ __forceinline__ void prepare(const DecodeTables &tb) { sc = group_scale<FMT>(sraw, s2, tb); }
-  __device__ __forceinline__ void lookup(int part, const DecodeTables &tb, float (&v)[8]) const {
-    decode_lookup<FMT>(codes[part], tb, v);
-  }
-  __device__ __forceinline__ void finish(LTile &t, int part, const float (&v)[8]) const {
-    st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + part * 8], decode_finish<FMT>(codes[part], sc, v));
+  __device__ __forceinline__ void prepare(const DecodeTables &tb) { dec.prepare(sraw, s2, tb); }
+  // decode code word `part` (8 k) and write it into the tile
+  __device__ __forceinline__ void store(LTile &t, int part) const {
+    st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + part * 8], dec(codes[part]));
   }
 };
 
@@ -435,7 +429,8 @@ template <int FMT>
 struct LQuantKN {
   u32x4 w;
   uint32_t sraw;
-  float s2, sc;
+  float s2;
+  GroupDecoder<FMT> dec;
   uint32_t cvoff, svoff, crow, srow;  // offsets at k0 = 0 of this thread's stored row; per-row steps
   int64_t blk0, blkrow;
   __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout) {
@@ -459,13 +454,10 @@ struct LQuantKN {
     w = bload128(rc, cvoff, ((uint32_t)k0 * crow) | dead);
     fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)k0 * srow, blk0 + (int64_t)k0 * blkrow, dead, sraw, s2);
   }
-  __device__ __forceinline__ void prepare(const DecodeTables &tb) { sc = group_scale<FMT>(sraw, s2, tb); }
-  __device__ __forceinline__ void lookup(int part, const DecodeTables &tb, float (&v)[8]) const {
-    decode_lookup<FMT>(w[part], tb, v);
-  }
-  __device__ __forceinline__ void finish(LTileKN &t, int part, const float (&v)[8]) const {
+  __device__ __forceinline__ void prepare(const DecodeTables &tb) { dec.prepare(sraw, s2, tb); }
+  __device__ __forceinline__ void store(LTileKN &t, int part) const {
     const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
-    st_lds16(&t.v[kb][knswz(nb * 32 + part * 8)], decode_finish<FMT>(w[part], sc, v));
+    st_lds16(&t.v[kb][knswz(nb * 32 + part * 8)], dec(w[part]));
   }
 };
 

@@ -156,9 +156,9 @@ __global__ __launch_bounds__(NTHREADS) void dense_gemm_kernel(GroupedArgs g) {
 
 // Large-tile grouped GEMM (256 x 256 per workgroup, 8 waves, double-buffered LDS).
 // Software pipeline over K slabs of 64: while the MFMAs consume slab s from LDS buffer
-// s&1, the registers of slab s+1 (loaded one slab earlier) are decoded and written into
-// the other buffer piece by piece between the MFMA k-steps, and the global loads of slab
-// s+2 are in flight.  One barrier per slab.
+// s&1, the registers of slab s+1 (loaded two slabs earlier) are decoded and written into
+// the other buffer piece by piece between the MFMA k-steps, and the global loads of slabs
+// s+2 and s+3 are in flight.  One barrier per slab.
 // Direct-to-LDS loads count in vmcnt and are not covered by the barrier: every wave
 // waits for its own before the workgroup barrier that publishes them.  vmcnt(n) waits
 // until at most n vector-memory loads of this wave are outstanding (loads retire in
@@ -173,7 +173,7 @@ __device__ __forceinline__ void wait_lds_dma() { wait_vmcnt<0>(); }
 // Workgroup barrier after this wave's LDS stores (lgkmcnt(0)) and all but its last N
 // vector-memory loads (vmcnt(N): the direct-to-LDS A loads, issued first) completed.
 // A fenced __syncthreads() would drain every outstanding load, including the B loads
-// prefetched two slabs ahead; the empty asm statements keep the compiler from moving
+// prefetched ahead; the empty asm statements keep the compiler from moving
 // memory accesses across the barrier.
 template <int N>
 __device__ __forceinline__ void slab_barrier() {
@@ -204,7 +204,7 @@ struct LargePipe {
   const GroupedArgs &g;
   __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
   LDirectA la;
-  BLoader lb[2];
+  BLoader lb[3];  // B register ring: slab t lives in lb[t % 3]
   LMma mma;
 
   // Members are set here, never zero-filled as an aggregate: a memset over the buffer
@@ -236,25 +236,25 @@ struct LargePipe {
   __device__ __forceinline__ void issue_a(ATile &t, int slab, int nmain) {
     la.issue(ra, t, (uint32_t)(slab * BK * 2) | dead(slab, nmain));
   }
-  // Slab s computes from buffers P while slab s+1 is completed into buffers P^1: its A
-  // rows by direct loads issued now, its B from registers P^1 decoded between the
-  // k-steps; the B loads of slab s+2 go into registers P.  Every body runs its MFMAs, so
-  // the accumulators follow one path; a slab past the end has zero A and B.
-  template <int P>
+  // Slab s (LDS buffers P = s % 2) computes while slab s+1 is completed into buffers P^1:
+  // its A rows by direct loads issued now, its B decoded from registers lb[(s+1) % 3]
+  // between the k-steps.  The B loads of slab s+3 go into lb[s % 3], so B codes arrive two
+  // slabs before they are decoded.  Every body runs its MFMAs, so the accumulators follow
+  // one path; a slab past the end has zero A and B.
+  template <int P, int Q>
   __device__ __forceinline__ void body(int s, int nmain) {
+    constexpr int QD = (Q + 1) % 3;
     // The scheduler keeps the issue order: the A rows first, then the B loads, whose
     // count is the vmcnt the closing barrier leaves outstanding.
     issue_a(atile<P ^ 1>(), s + 1, nmain);
     __builtin_amdgcn_sched_barrier(0);
-    fetch_b(P, s + 2, nmain);
+    fetch_b(Q, s + 3, nmain);
     __builtin_amdgcn_sched_barrier(0);
-    lb[P ^ 1].prepare(tb);
+    lb[QD].prepare(tb);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       mma.template kstep<KN>(atile<P>(), btile<P>(), ks);
-      float v[8];
-      lb[P ^ 1].lookup(ks, tb, v);
-      lb[P ^ 1].finish(btile<P ^ 1>(), ks, v);
+      lb[QD].store(btile<P ^ 1>(), ks);
     }
     slab_barrier<b_fetch_loads<KN, FMT>()>();  // the A rows of slab s+1 have landed
   }
@@ -262,18 +262,26 @@ struct LargePipe {
     issue_a(A0, 0, nmain);
     fetch_b(0, 0, nmain);
     fetch_b(1, 1, nmain);
+    fetch_b(2, 2, nmain);
     lb[0].prepare(tb);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      float v[8];
-      lb[0].lookup(p, tb, v);
-      lb[0].finish(btile<0>(), p, v);
-    }
+    for (int p = 0; p < 4; ++p) lb[0].store(btile<0>(), p);
     wait_lds_dma();
     __syncthreads();
-    for (int s = 0; s < nmain; s += 2) {
-      body<0>(s, nmain);
-      body<1>(s + 1, nmain);
+    // six bodies cycle both the LDS buffer parity and the register stage
+    for (int s = 0;; s += 6) {
+      body<0, 0>(s, nmain);
+      if (s + 1 >= nmain) break;
+      body<1, 1>(s + 1, nmain);
+      if (s + 2 >= nmain) break;
+      body<0, 2>(s + 2, nmain);
+      if (s + 3 >= nmain) break;
+      body<1, 0>(s + 3, nmain);
+      if (s + 4 >= nmain) break;
+      body<0, 1>(s + 4, nmain);
+      if (s + 5 >= nmain) break;
+      body<1, 2>(s + 5, nmain);
+      if (s + 6 >= nmain) break;
     }
   }
 };
@@ -302,6 +310,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
   if constexpr (BKIND == B_QKN) pipe.lb[0].init(g.q, e, n0, g.N);
   else pipe.lb[0].init(g.q, e, map, Nrows);
   pipe.lb[1] = pipe.lb[0];
+  pipe.lb[2] = pipe.lb[0];
   pipe.run(g.K / BK);
   LMma &mma = pipe.mma;
 
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
           if (row < tm.rows) {
             const int64_t p = tm.row0 + row;
             const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
-            const float act = gt / (1.0f + expf(-gt));
+            const float act = gt * sigmoid_fast(gt);
             Hout[p * g.ldc + col] = f2bf(act * up);
             if (g.Gout) {
               g.Gout[p * g.ldg + col] = f2bf(gt);
@@ -344,7 +353,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
           }
         }
     }
-  } else {
+  } else if constexpr (EPI == EPI_F32) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + LMma::col_of(j);
@@ -354,18 +363,40 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = LMma::row_of(i, v);
-          if (row >= tm.rows) continue;
-          const int64_t p = tm.row0 + row;
-          const float val = mma.acc[i][j][v];
-          if constexpr (EPI == EPI_F32) {
-            ((float *)g.C)[p * g.ldc + n] = g.alpha * val;
-          } else {  // EPI_SWIGLU_BWD: val = dh
-            const float gt = bf2f(g.Gin[p * g.ldg + n]), up = bf2f(g.Gin[p * g.ldg + g.I + n]);
-            const float sg = 1.0f / (1.0f + expf(-gt));
-            g.Gout[p * g.ldg + n] = f2bf(val * up * sg * (1.0f + gt * (1.0f - sg)));
-            g.Gout[p * g.ldg + g.I + n] = f2bf(val * gt * sg);
-          }
+          if (row < tm.rows) ((float *)g.C)[(tm.row0 + row) * g.ldc + n] = g.alpha * mma.acc[i][j][v];
         }
+    }
+  } else {  // EPI_SWIGLU_BWD: acc = dh; dG from the saved pre-activation G
+    // G and dG are separate buffers.  The 32 G values of a 16-row group are loaded
+    // unconditionally (rows past the tile read the tile's first row) before any of them is
+    // used, so their latencies overlap instead of adding up.
+    const uint16_t *__restrict__ gin = g.Gin;
+    uint16_t *__restrict__ gout = g.Gout;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + LMma::col_of(j);
+      const bool nok = n < g.N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t gv[16], uv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = LMma::row_of(i, v);
+          const int64_t off = nok && row < tm.rows ? (tm.row0 + row) * g.ldg + n : tm.row0 * g.ldg;
+          gv[v] = gin[off];
+          uv[v] = gin[off + g.I];
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = LMma::row_of(i, v);
+          if (!nok || row >= tm.rows) continue;
+          const int64_t off = (tm.row0 + row) * g.ldg + n;
+          const float dh = mma.acc[i][j][v], gt = bf2f((uint16_t)gv[v]), up = bf2f((uint16_t)uv[v]);
+          const float sg = sigmoid_fast(gt);
+          gout[off] = f2bf(dh * up * sg * (1.0f + gt * (1.0f - sg)));
+          gout[off + g.I] = f2bf(dh * gt * sg);
+        }
+      }
     }
   }
 }

@@ -307,7 +307,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
         if (n < 16 && i < g.I && t < tm.rows) {
           const int64_t p = tm.row0 + t;
           const float gt = mine, up = other;
-          const float act = gt / (1.0f + expf(-gt));
+          const float act = gt * sigmoid_fast(gt);
           ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(act * up);
           if (g.Gout) {
             g.Gout[p * g.ldg + i] = f2bf(gt);
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         if (n < 16 && i < g.I && t >= t0 && t < t0 + xrows) {
           const int64_t p = tm.row0 + t;
           const float gt = mine, up = other;
-          const float act = gt / (1.0f + expf(-gt));
+          const float act = gt * sigmoid_fast(gt);
           ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(act * up);
           if (g.Gout) {
             g.Gout[p * g.ldg + i] = f2bf(gt);
