@@ -1,6 +1,7 @@
 // C ABI of libe4b: argument validation, workspace layout, the three layer calls
 // (forward, input gradient, LoRA weight gradients) as stream-ordered kernel
 // sequences, and the verification / observability exports.
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -59,7 +60,7 @@ bool last_launch_ok() { return hipGetLastError() == hipSuccess; }
 
 // ------------------------------------------------------------------ workspace layout
 struct Layout {
-  size_t cnt, off, perm, inv, z1, z2, G, h, O, dO, u2, dG, u1, dXp, A1T, B1T, A2T, B2T, total;
+  size_t cnt, off, perm, inv, z1, z2, G, h, O, dO, u2, dG, u1, dXp, A1T, B1T, A2T, B2T, part, total;
 };
 static constexpr size_t NONE = ~(size_t)0;
 
@@ -96,6 +97,26 @@ static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
   } else {
     L.dO = L.u2 = L.dG = L.u1 = L.dXp = L.A1T = L.B1T = L.A2T = L.B2T = NONE;
   }
+  // fp32 partial sums of the split skinny GEMMs (LoRA-A projections, LoRA weight gradients),
+  // sized for the largest of them
+  size_t part = 0;
+  auto lora = [&](int r, int K) {
+    const int sp = r ? lora_a_splits((int)M, (int)E, r, K) : 1;
+    if (sp > 1) part = std::max(part, (size_t)sp * M * r * 4);
+  };
+  auto wgrad = [&](int Na, int Nb) {
+    const int sp = Na && Nb ? wgrad_splits((int)M, (int)E, Na, Nb) : 1;
+    if (sp > 1) part = std::max(part, (size_t)sp * E * Na * Nb * 4);
+  };
+  lora(r1, (int)H);
+  lora(r2, (int)I);
+  if (train) {
+    lora(r2, (int)H);
+    lora(r1, (int)(2 * I));
+    if (r1) { wgrad((int)(2 * I), r1); wgrad(r1, (int)H); }
+    if (r2) { wgrad((int)H, r2); wgrad(r2, (int)I); }
+  }
+  L.part = part ? take(part) : NONE;
   L.total = o;
   return L;
 }
@@ -225,6 +246,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
   uint16_t *z1 = at<uint16_t>(ws, L.z1), *z2 = at<uint16_t>(ws, L.z2), *h = at<uint16_t>(ws, L.h);
   float *O = at<float>(ws, L.O);
   uint16_t *G = L.G == NONE ? nullptr : at<uint16_t>(ws, L.G);
+  float *part = L.part == NONE ? nullptr : at<float>(ws, L.part);
 
   E4B_LAUNCH(launch_route(ids, M, E, cnt, off, perm, inv, s));
   if (M == 0) return E4B_OK;
@@ -239,6 +261,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.A = x; a.lda = H; a.a_gather = perm; a.a_gdiv = d.topk;
     a.Bd = l_gu->A; a.b_estride = (int64_t)r1 * H; a.ldb = H;
     a.C = z1; a.ldc = r1; a.alpha = l_gu->scaling;
+    a.part = part; a.nsplit = lora_a_splits(M, E, a.N, a.K);
     E4B_LAUNCH(lora_a(a));
   }
   {  // h = silu(G_gate) * G_up, G = W1 x + B1 z1
@@ -259,6 +282,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.A = h; a.lda = I; a.a_gdiv = 1;
     a.Bd = l_dn->A; a.b_estride = (int64_t)r2 * I; a.ldb = I;
     a.C = z2; a.ldc = r2; a.alpha = l_dn->scaling;
+    a.part = part; a.nsplit = lora_a_splits(M, E, a.N, a.K);
     E4B_LAUNCH(lora_a(a));
   }
   int nsplit = 1;
@@ -301,6 +325,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
   uint16_t *G = at<uint16_t>(ws, L.G), *dO = at<uint16_t>(ws, L.dO), *dG = at<uint16_t>(ws, L.dG);
   uint16_t *u1 = at<uint16_t>(ws, L.u1), *u2 = at<uint16_t>(ws, L.u2);
   float *O = at<float>(ws, L.O), *dXp = at<float>(ws, L.dXp);
+  float *part = L.part == NONE ? nullptr : at<float>(ws, L.part);
   uint16_t *A1T = at<uint16_t>(ws, L.A1T), *B1T = at<uint16_t>(ws, L.B1T);
   uint16_t *A2T = at<uint16_t>(ws, L.A2T), *B2T = at<uint16_t>(ws, L.B2T);
 
@@ -313,6 +338,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     a.A = dO; a.lda = H; a.a_gdiv = 1;
     a.Bd = B2T; a.b_estride = (int64_t)r2 * H; a.ldb = H;
     a.C = u2; a.ldc = r2; a.alpha = l_dn->scaling;
+    a.part = part; a.nsplit = lora_a_splits(M, E, a.N, a.K);
     E4B_LAUNCH(launch_lora_a(a, s));
   }
   {  // dH = dO W2 + u2 A2 -> SwiGLU backward -> dG
@@ -334,6 +360,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     a.A = dG; a.lda = 2 * I; a.a_gdiv = 1;
     a.Bd = B1T; a.b_estride = (int64_t)r1 * 2 * I; a.ldb = 2 * I;
     a.C = u1; a.ldc = r1; a.alpha = l_gu->scaling;
+    a.part = part; a.nsplit = lora_a_splits(M, E, a.N, a.K);
     E4B_LAUNCH(launch_lora_a(a, s));
   }
   {  // dXp = dG W1 + u1 A1
@@ -367,18 +394,26 @@ e4b_status e4b_lora_wgrad(const e4b_moe_desc *desc, const e4b_lora *l_gu, const 
   hipStream_t s = (hipStream_t)stream;
   const int E = d.E, H = d.H, I = d.I;
   int32_t *off = at<int32_t>(ws, L.off), *perm = at<int32_t>(ws, L.perm);
+  float *part = L.part == NONE ? nullptr : at<float>(ws, L.part);
+  const int M = d.T * d.topk;
+  auto split = [&](WgradArgs &w) {
+    w.part = part;
+    w.nsplit = wgrad_splits(M, E, w.Na, w.Nb);
+  };
   if (r1) {
     WgradArgs a{};  // dB1[e] = dG_e^T z1_e
     a.off = off; a.E = E;
     a.P = at<uint16_t>(ws, L.dG); a.ldp = 2 * I; a.Na = 2 * I; a.p_gdiv = 1;
     a.Q = at<uint16_t>(ws, L.z1); a.ldq = r1; a.Nb = r1; a.q_gdiv = 1;
     a.C = dB_gu;
+    split(a);
     E4B_LAUNCH(launch_wgrad(a, s));
     WgradArgs b{};  // dA1[e] = u1_e^T X_e
     b.off = off; b.E = E;
     b.P = at<uint16_t>(ws, L.u1); b.ldp = r1; b.Na = r1; b.p_gdiv = 1;
     b.Q = x; b.ldq = H; b.Nb = H; b.q_gather = perm; b.q_gdiv = d.topk;
     b.C = dA_gu;
+    split(b);
     E4B_LAUNCH(launch_wgrad(b, s));
   }
   if (r2) {
@@ -387,12 +422,14 @@ e4b_status e4b_lora_wgrad(const e4b_moe_desc *desc, const e4b_lora *l_gu, const 
     a.P = at<uint16_t>(ws, L.dO); a.ldp = H; a.Na = H; a.p_gdiv = 1;
     a.Q = at<uint16_t>(ws, L.z2); a.ldq = r2; a.Nb = r2; a.q_gdiv = 1;
     a.C = dB_dn;
+    split(a);
     E4B_LAUNCH(launch_wgrad(a, s));
     WgradArgs b{};  // dA2[e] = u2_e^T h_e
     b.off = off; b.E = E;
     b.P = at<uint16_t>(ws, L.u2); b.ldp = r2; b.Na = r2; b.p_gdiv = 1;
     b.Q = at<uint16_t>(ws, L.h); b.ldq = I; b.Nb = I; b.q_gdiv = 1;
     b.C = dA_dn;
+    split(b);
     E4B_LAUNCH(launch_wgrad(b, s));
   }
   return E4B_OK;

@@ -147,7 +147,8 @@ struct DenseNKLoader {
 // ---------------------------------------------------------------- K-major loader
 // Tile rows a (BR of them) x 64 k where the source is row-major [k][a] (a
 // contiguous): source row of k is row0 + k (or gather[row0 + k] / gdiv).  Thread
-// -> 4 k rows x (BR/16) a columns, transposed into LDS.  Used by the segmented
+// -> 4 k rows x (BR/16) a columns, transposed into LDS.  Row lengths and column offsets
+// are multiples of 8 elements (LoRA ranks are), so each row piece is one vector load.  Used by the segmented
 // weight-gradient GEMMs whose reduction runs over routed rows.
 template <int BR>
 struct KMajorLoader {
@@ -165,9 +166,17 @@ struct KMajorLoader {
       const bool ok = kk < krows && a < Na;
       int64_t src = 0;
       if (ok) src = gather ? (int64_t)(gather[row0 + kk] / gdiv) : (int64_t)(row0 + kk);
-      const uint32_t *p = (const uint32_t *)(base + src * ld + a);
+      // one 16-byte (or 8-byte) load per source row: a and ld are multiples of 8 elements
+      const uint16_t *p = base + src * ld + a;
+      if constexpr (NW == 4) {
+        const u32x4 v = ok ? *(const u32x4 *)p : u32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int j = 0; j < NW; ++j) w[i][j] = ok ? p[j] : 0u;
+        for (int j = 0; j < 4; ++j) w[i][j] = v[j];
+      } else {
+        const u32x2 v = ok ? *(const u32x2 *)p : u32x2{0, 0};
+#pragma unroll
+        for (int j = 0; j < NW; ++j) w[i][j] = v[j];
+      }
     }
   }
   __device__ __forceinline__ void store(LdsTile<BR> &t) {

@@ -6,6 +6,7 @@
 
 #include "gemm.hpp"
 #include "kernels.hpp"
+#include <algorithm>
 
 namespace e4b {
 
@@ -133,25 +134,71 @@ __global__ __launch_bounds__(NTHREADS) void dense_gemm_kernel(GroupedArgs g) {
   RowLoader<BMt> la;
   DenseNKLoader<BN> ld;
   const uint16_t *Bd_e = g.Bd + (int64_t)e * g.b_estride;
-  const int nsl = g.K / BK;
+  // this split's slabs
+  const int nall = g.K / BK, chunk = (nall + g.nsplit - 1) / g.nsplit;
+  const int s0 = min(nall, (int)blockIdx.z * chunk), s1 = min(nall, s0 + chunk);
   auto fetch = [&](int s) {
     la.fetch(g.A, g.lda, tm.rows, tm.row0, g.a_gather, g.a_gdiv, s * BK, g.K);
     ld.fetch(Bd_e, g.ldb, map, g.N, s * BK, g.K);
   };
-  if (nsl > 0) fetch(0);
-  for (int s = 0; s < nsl; ++s) {
+  if (s0 < s1) fetch(s0);
+  for (int s = s0; s < s1; ++s) {
     __syncthreads();
     la.store(As);
     ld.store(Bs);
     __syncthreads();
-    if (s + 1 < nsl) fetch(s + 1);
+    if (s + 1 < s1) fetch(s + 1);
     mma.step(As, Bs, 4);
   }
-  mma.for_each([&](int row, int col, float v) {
-    const int n = n0 + col;
-    if (row >= tm.rows || n >= g.N) return;
-    ((uint16_t *)g.C)[(int64_t)(tm.row0 + row) * g.ldc + n] = f2bf(g.alpha * v);
-  });
+  if (g.nsplit > 1) {
+    float *P = g.part + (int64_t)blockIdx.z * g.M * g.N;
+    mma.for_each([&](int row, int col, float v) {
+      const int n = n0 + col;
+      if (row < tm.rows && n < g.N) P[(int64_t)(tm.row0 + row) * g.N + n] = v;
+    });
+  } else {
+    mma.for_each([&](int row, int col, float v) {
+      const int n = n0 + col;
+      if (row < tm.rows && n < g.N) ((uint16_t *)g.C)[(int64_t)(tm.row0 + row) * g.ldc + n] = f2bf(g.alpha * v);
+    });
+  }
+}
+
+// out[row][col] = alpha * sum over s of part[s * stride + row * cols + col], added in split
+// order; fp32 or bf16 output with leading dimension ldo.
+__global__ void reduce_splits_kernel(const float *__restrict__ part, int nsplit, int64_t stride, int64_t count,
+                                     int cols, int64_t ldo, float alpha, int out_bf16, void *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  float acc = part[i];
+  for (int s2 = 1; s2 < nsplit; ++s2) acc += part[s2 * stride + i];
+  const int64_t o = (i / cols) * ldo + i % cols;
+  if (out_bf16) ((uint16_t *)out)[o] = f2bf(alpha * acc);
+  else ((float *)out)[o] = alpha * acc;
+}
+
+static bool launch_reduce_splits(const float *part, int nsplit, int64_t stride, int64_t count, int cols,
+                                 int64_t ldo, float alpha, bool out_bf16, void *out, hipStream_t s) {
+  if (count == 0) return true;
+  reduce_splits_kernel<<<(unsigned)((count + 255) / 256), 256, 0, s>>>(part, nsplit, stride, count, cols, ldo,
+                                                                        alpha, out_bf16 ? 1 : 0, out);
+  return last_launch_ok();
+}
+
+// Aim for about four workgroups per compute unit; each split keeps at least 4 slabs.
+static constexpr int SPLIT_TARGET_WGS = 1024, SPLIT_MAX = 8;
+static int splits_for(int64_t wgs, int64_t slabs) {
+  int sp = (int)std::min<int64_t>(SPLIT_MAX, std::max<int64_t>(1, (SPLIT_TARGET_WGS + wgs - 1) / std::max<int64_t>(1, wgs)));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(sp, slabs / 4));
+}
+int lora_a_splits(int M, int E, int N, int K) {
+  if (M == 0) return 1;
+  return splits_for((int64_t)cdiv(N, 64) * (cdiv(M, 128) + E), K / BK);
+}
+int wgrad_splits(int M, int E, int Na, int Nb) {
+  if (M == 0 || E == 0) return 1;
+  const int64_t tiles = Nb <= 64 ? (int64_t)cdiv(Nb, 64) * cdiv(Na, 128) : (int64_t)cdiv(Nb, 128) * cdiv(Na, 64);
+  return splits_for(tiles * E, (int64_t)M / E / BK);
 }
 
 // Large-tile grouped GEMM (256 x 256 per workgroup, 8 waves, double-buffered LDS).
@@ -447,9 +494,16 @@ bool launch_gemm_gate_up_dgrad(const GroupedArgs &a, hipStream_t s) {
 bool launch_lora_a(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_LORA_A, s);
-  dim3 grid(cdiv(a.N, 64), m_slots(a, 128));
-  dense_gemm_kernel<64, 4, 1><<<grid, NTHREADS, 0, s>>>(a);
-  return last_launch_ok();
+  GroupedArgs b = a;
+  if (!b.part) b.nsplit = 1;
+  b.nsplit = std::max(1, b.nsplit);
+  dim3 grid(cdiv(b.N, 64), m_slots(b, 128), b.nsplit);
+  dense_gemm_kernel<64, 4, 1><<<grid, NTHREADS, 0, s>>>(b);
+  if (!last_launch_ok()) return false;
+  if (b.nsplit > 1)
+    return launch_reduce_splits(b.part, b.nsplit, (int64_t)b.M * b.N, (int64_t)b.M * b.N, b.N, b.ldc, b.alpha, true,
+                                b.C, s);
+  return true;
 }
 
 // =============================================================== LoRA weight gradients
@@ -458,30 +512,33 @@ template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
   __shared__ LdsTile<BM> As;
   __shared__ LdsTile<BN> Bs;
-  const int e = blockIdx.z;
+  const int e = blockIdx.z / g.nsplit, sp = blockIdx.z % g.nsplit;
   const int a0 = blockIdx.y * BM, b0 = blockIdx.x * BN;
   const int row0 = g.off[e], krows = g.off[e + 1] - g.off[e];
   Mma<BM, BN, WM, WN> mma;
   mma.zero();
   KMajorLoader<BM> la;
   KMajorLoader<BN> lb;
-  const int nsl = (krows + BK - 1) / BK;
-  if (nsl > 0) {
-    la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, 0);
-    lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, 0);
+  // this split's slabs of the expert's rows
+  const int nall = (krows + BK - 1) / BK, chunk = (nall + g.nsplit - 1) / g.nsplit;
+  const int s0 = min(nall, sp * chunk), s1 = min(nall, s0 + chunk);
+  if (s0 < s1) {
+    la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, s0 * BK);
+    lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, s0 * BK);
   }
-  for (int s = 0; s < nsl; ++s) {
+  for (int s = s0; s < s1; ++s) {
     __syncthreads();
     la.store(As);
     lb.store(Bs);
     __syncthreads();
-    if (s + 1 < nsl) {
+    if (s + 1 < s1) {
       la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, (s + 1) * BK);
       lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, (s + 1) * BK);
     }
     mma.step(As, Bs, 4);
   }
-  float *C = g.C + (int64_t)e * g.Na * g.Nb;
+  // every split writes its (possibly zero) partial sums
+  float *C = g.nsplit > 1 ? g.part + ((int64_t)sp * g.E + e) * g.Na * g.Nb : g.C + (int64_t)e * g.Na * g.Nb;
   mma.for_each([&](int row, int col, float v) {
     const int a = a0 + row, b = b0 + col;
     if (a < g.Na && b < g.Nb) C[(int64_t)a * g.Nb + b] = v;
@@ -491,14 +548,22 @@ __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
 bool launch_wgrad(const WgradArgs &a, hipStream_t s) {
   if (a.E == 0) return true;
   LaunchScope ls(FAM_WGRAD, s);
-  if (a.Nb <= 64) {  // tall-skinny: rows = weight rows, cols = rank
-    dim3 grid(cdiv(a.Nb, 64), cdiv(a.Na, 128), a.E);
-    wgrad_kernel<128, 64, 4, 1><<<grid, NTHREADS, 0, s>>>(a);
+  WgradArgs b = a;
+  if (!b.part) b.nsplit = 1;
+  b.nsplit = std::max(1, b.nsplit);
+  if (b.Nb <= 64) {  // tall-skinny: rows = weight rows, cols = rank
+    dim3 grid(cdiv(b.Nb, 64), cdiv(b.Na, 128), b.E * b.nsplit);
+    wgrad_kernel<128, 64, 4, 1><<<grid, NTHREADS, 0, s>>>(b);
   } else {  // short-wide: rows = rank, cols = weight columns
-    dim3 grid(cdiv(a.Nb, 128), cdiv(a.Na, 64), a.E);
-    wgrad_kernel<64, 128, 1, 4><<<grid, NTHREADS, 0, s>>>(a);
+    dim3 grid(cdiv(b.Nb, 128), cdiv(b.Na, 64), b.E * b.nsplit);
+    wgrad_kernel<64, 128, 1, 4><<<grid, NTHREADS, 0, s>>>(b);
   }
-  return last_launch_ok();
+  if (!last_launch_ok()) return false;
+  if (b.nsplit > 1) {
+    const int64_t n = (int64_t)b.E * b.Na * b.Nb;
+    return launch_reduce_splits(b.part, b.nsplit, n, n, b.Nb, b.Nb, 1.0f, false, b.C, s);
+  }
+  return true;
 }
 
 // =============================================================== combine and friends

@@ -69,6 +69,10 @@ struct GroupedArgs {
   const uint16_t *Gin;  // SwiGLU bwd: saved pre-activation
   int64_t ldg;
   int I;
+  // small-N dense GEMM only: with nsplit > 1 the reduction is split nsplit ways and the
+  // fp32 partial sums [nsplit][M][N] go to `part`, then are added in split order
+  float *part;
+  int nsplit;
 };
 
 enum BKind : int { B_QNK = 0, B_QKN = 1, B_DENSE = 2 };
@@ -102,8 +106,15 @@ struct WgradArgs {
   const int32_t *q_gather;
   int q_gdiv;
   float *C;  // [E][Na][Nb]
+  // with nsplit > 1 each expert's rows are split nsplit ways; the fp32 partial sums
+  // [nsplit][E][Na][Nb] go to `part` and are added in split order
+  float *part;
+  int nsplit;
 };
 bool launch_wgrad(const WgradArgs &a, hipStream_t s);
+// Reduction splits that give the skinny GEMMs enough workgroups to fill the device.
+int lora_a_splits(int M, int E, int N, int K);
+int wgrad_splits(int M, int E, int Na, int Nb);
 
 // y[t] = bf16(sum_j w[t,j] * O[inv[t,j]]); O holds `nsplit` partial sums, split_stride
 // floats apart, that are added in split order first.
