@@ -69,9 +69,19 @@ struct SmallX {
   uint16_t v[2][SM_BMT][SM_XSTRIDE];
 };
 
+// Byte o / the dword at byte offset o (a multiple of 4) of a 16-byte window.  Byte permutes
+// with per-lane selectors pick within each half and a select picks the half, so the window
+// stays in registers: a chain of selects over the four words is recognised as a
+// variable-index vector extract, which puts the window in a private array (scratch).
 __device__ __forceinline__ uint32_t byte_at(const u32x4 &r, uint32_t o) {
-  const uint32_t w = o < 4 ? r[0] : o < 8 ? r[1] : o < 12 ? r[2] : r[3];
-  return (w >> (8 * (o & 3))) & 0xffu;
+  const uint32_t sel = 0x0C0C0C00u | (o & 7u);
+  const uint32_t lo = __builtin_amdgcn_perm(r[1], r[0], sel), hi = __builtin_amdgcn_perm(r[3], r[2], sel);
+  return (o & 8u) ? hi : lo;
+}
+__device__ __forceinline__ uint32_t dword_at(const u32x4 &r, uint32_t o) {
+  const uint32_t sel = (o & 4u) ? 0x07060504u : 0x03020100u;
+  const uint32_t lo = __builtin_amdgcn_perm(r[1], r[0], sel), hi = __builtin_amdgcn_perm(r[3], r[2], sel);
+  return (o & 8u) ? hi : lo;
 }
 
 // Raw scales of one chunk (4 blocks) of one weight row, read as one 16-byte window that
@@ -209,9 +219,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   // scale of block b of the chunk in `slot` for strip s
   auto scale_of = [&](int slot, int s, int b, int c) -> float {
     if constexpr (FMT == FMT_NF4) {
-      const uint32_t o = cs[slot][s].sh + 4 * b;  // a multiple of 4
-      const u32x4 &r = cs[slot][s].raw;
-      return __uint_as_float(o < 4 ? r[0] : o < 8 ? r[1] : o < 12 ? r[2] : r[3]);
+      return __uint_as_float(dword_at(cs[slot][s].raw, cs[slot][s].sh + 4 * b));  // a multiple of 4
     } else if constexpr (FMT == FMT_NF4_DQ) {
       const uint32_t code = byte_at(cs[slot][s].raw, cs[slot][s].sh + b);
       const bool second = ((blk0[s] + c * SM_CB + b) >> 8) != ((blk0[s] + c * SM_CB) >> 8);
@@ -264,6 +272,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
                                                             0, 0, 0);
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[s][v] += sc * blk[v];
+            // keeps the scaling of this block's partial sum here: sunk to the end of the
+            // step, the partial sums of all its blocks stay live and spill, and the spill
+            // reloads (vector-memory loads) then wait for every weight load in flight
+            asm volatile("" : "+v"(acc[s]));
           } else {
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4)
@@ -441,8 +453,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     // scale of block j (slot d) from the quad window `q`, block b = j % 4 of it
     auto scale_in = [&](const ChunkScale &q, int b, int j) -> float {
       if constexpr (FMT == FMT_NF4) {
-        const uint32_t o = q.sh + 4 * b;
-        return __uint_as_float(o < 4 ? q.raw[0] : o < 8 ? q.raw[1] : o < 12 ? q.raw[2] : q.raw[3]);
+        return __uint_as_float(dword_at(q.raw, q.sh + 4 * b));
       } else if constexpr (FMT == FMT_NF4_DQ) {
         const uint32_t code = byte_at(q.raw, q.sh + b);
         const bool second = ((blk0 + j) >> 8) != ((blk0 + j - b) >> 8);
@@ -583,7 +594,7 @@ static void launch_small_fmt(const GroupedArgs &a, int spw, int strips_per_exper
     small_direct_kernel<FMT, EPI><<<grid, SM_THREADS, lds + xlds, s>>>(a, kbs, split_stride);
   } else {
     const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, SM_BMT), splits);
-    small_gemm_kernel<FMT, 1, EPI, 2><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride);
+    small_gemm_kernel<FMT, 1, EPI, 3><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride);
   }
 }
 
