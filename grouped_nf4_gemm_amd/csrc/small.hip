@@ -35,12 +35,13 @@ struct SmallTables {
   uint32_t cp[256][64];
 };
 
-// thread t builds entry t % 256 and writes its 64 copies (16 bytes at a time)
+// 16-byte piece i of the table (entry i / 16, copies 4 (i % 16) .. +3): consecutive lanes
+// write consecutive pieces, so the stores are free of bank conflicts.
 __device__ __forceinline__ void init_small_tables(SmallTables &t) {
-  for (int b = threadIdx.x; b < 256; b += blockDim.x) {
+  for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x) {
+    const uint32_t b = (uint32_t)i >> 4;
     const uint32_t v = pack_bf16x2(nf4_value(b >> 4), nf4_value(b & 15));
-#pragma unroll
-    for (int c = 0; c < 64; c += 4) *(u32x4 *)&t.cp[b][c] = u32x4{v, v, v, v};
+    *(u32x4 *)&t.cp[b][4 * (i & 15)] = u32x4{v, v, v, v};
   }
 }
 
@@ -173,22 +174,22 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
 
   u32x4 cw[R][SPW][SM_CB];
   ChunkScale cs[R][SPW];
-  u32x4 xr[2];
+  u32x4 xr[R][2];  // activation pieces ride the same ring as the weights
   f32x16 acc[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[s][v] = 0.0f;
 
-  auto load_x = [&](int c) {
+  auto load_x = [&](int slot, int c) {
     const uint32_t dead = c < nchunks ? 0u : OOB;
-    xr[0] = bload128(ra, xoff, ((uint32_t)c * SM_CB * 128) | dead);
-    xr[1] = bload128(ra, xoff, ((uint32_t)c * SM_CB * 128 + 16) | dead);
+    xr[slot][0] = bload128(ra, xoff, ((uint32_t)c * SM_CB * 128) | dead);
+    xr[slot][1] = bload128(ra, xoff, ((uint32_t)c * SM_CB * 128 + 16) | dead);
   };
-  auto store_x = [&](int c) {
+  auto store_x = [&](int slot, int c) {
     uint16_t *dst = &xs.v[c & 1][xrow][16 * xpiece];
-    *(u32x4 *)dst = xr[0];
-    *(u32x4 *)(dst + 8) = xr[1];
+    *(u32x4 *)dst = xr[slot][0];
+    *(u32x4 *)(dst + 8) = xr[slot][1];
   };
   auto load_w = [&](int slot, int c) {
 #pragma unroll
@@ -229,27 +230,26 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     }
   };
 
-  // prologue: activations of chunk 0 (waited for at once, so issued first), then the
-  // weights of chunks 0 .. DC-1 in slot order
-  __builtin_amdgcn_sched_barrier(0);
-  load_x(0);
+  // prologue: the activations and weights of chunks 0 .. DC-1 in slot order (activations
+  // first in each group: they are waited for one step before the weights)
 #pragma unroll
   for (int d = 0; d < DC; ++d) {
     __builtin_amdgcn_sched_barrier(0);
+    load_x(d, d);
     load_w(d, d);
   }
   __builtin_amdgcn_sched_barrier(0);
-  store_x(0);
+  store_x(0, 0);
   lds_barrier();
 
   for (int cb = 0; cb < nchunks; cb += R) {
 #pragma unroll
     for (int d = 0; d < R; ++d) {
       const int c = cb + d;  // chunk c sits in slot d; its activations in xs.v[c & 1]
-      // loads: activations of chunk c+1 first (needed at the end of this step), then
-      // the weights of chunk c+DC into the slot the previous step freed
+      // loads of chunk c+DC (activations, then weights) into the slot the previous step
+      // freed; the activations of chunk c+1, loaded DC-1 steps ago, are staged at the end
       __builtin_amdgcn_sched_barrier(0);
-      load_x(c + 1);
+      load_x((d + DC) % R, c + DC);
       load_w((d + DC) % R, c + DC);
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t *xb = &xs.v[c & 1][n][32 * hh];
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
           }
         }
       }
-      store_x(c + 1);
+      store_x((d + 1) % R, c + 1);
       lds_barrier();
     }
   }
