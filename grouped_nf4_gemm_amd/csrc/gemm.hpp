@@ -277,17 +277,20 @@ __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t vo
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
 
-// A tile written by direct-to-LDS buffer loads: 256 rows of 64 bf16 (128 bytes, no
-// padding) whose eight 16-byte chunks are XOR-swizzled by (row & 7), which keeps both
-// the DMA writes (lane t -> bytes 16t of a 1 KB block) and the MFMA fragment reads free
-// of bank conflicts.
+// Operand tiles of 64-wide slabs: rows of 64 bf16 (128 bytes, no padding) whose eight
+// 16-byte chunks sit at chunk ^ ((row >> 1) & 7).  LDS serves 16 lanes of a 16-byte access
+// per pass, over 64 banks: the 16 rows one fragment read touches then hit 16 distinct
+// groups of 4 banks (row parity picks the bank half, the swizzle the group), and the DMA
+// writes (lane t -> bytes 16t of a 1 KB block) stay conflict-free as well.
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 struct ATile {
   uint16_t v[L_BM * BK];
 };
-__device__ __forceinline__ int aswz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
-struct LTile {  // [256 n][64 (+8) k] bf16, k contiguous
-  uint16_t v[L_BN][LDS_STRIDE];
+__device__ __forceinline__ int aswz(int row, int chunk) { return row * BK + (swz_chunk(row, chunk) << 3); }
+struct LTile {  // [256 n][64 k] bf16, k contiguous, chunks swizzled as the A tile
+  uint16_t v[L_BN][BK];
 };
+__device__ __forceinline__ int bswz(int row, int chunk) { return swz_chunk(row, chunk) << 3; }
 // [64 k][256 (+16) n] bf16, n contiguous, whose 16-byte chunks c (8 columns) sit at
 // c ^ ((c >> 3) & 3) within the row.  With the row stride of 32 mod 128 bytes this keeps
 // both access patterns free of bank conflicts: the decode stores (8 lanes write chunks
@@ -300,11 +303,15 @@ __device__ __forceinline__ int knswz(int col) {
   const int c = col >> 3;
   return ((c ^ ((c >> 3) & 3)) << 3) | (col & 7);
 }
-static_assert(sizeof(LTileKN) <= sizeof(LTile), "B tile layouts share one buffer");
+// one LDS buffer holds either B tile layout
+union BBuf {
+  LTile nk;
+  LTileKN kn;
+};
 
 // A: 256 rows x 64 k of a row-major bf16 matrix (optionally gathered rows) loaded
 // straight into LDS.  Wave w, instruction i fills the 1 KB block of rows 8*(4w+i) ..
-// +7: lane l reads row 8*(4w+i) + l/8, logical chunk (l%8) ^ (l/8).
+// +7: lane l reads row 8*(4w+i) + l/8, the logical chunk that lands at physical chunk l%8.
 struct LDirectA {
   uint32_t voff[4];
   __device__ __forceinline__ void init(int rows, int64_t row0, const int32_t *__restrict__ gather,
@@ -313,7 +320,7 @@ struct LDirectA {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (w * 4 + i) * 8 + (l >> 3);
-      const int lc = (l & 7) ^ (l >> 3);
+      const int lc = swz_chunk(r, l & 7);  // the swizzle is its own inverse
       if (r < rows) {
         const int64_t s = gather ? (int64_t)(gather[row0 + r] / gdiv) : row0 + r;
         voff[i] = (uint32_t)((s * ld + lc * 8) * 2);
@@ -342,7 +349,7 @@ struct LRegA {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = (w * 4 + i) * 8 + (l >> 3);
-      const int kk = k0 + ((l & 7) ^ (l >> 3)) * 8;
+      const int kk = k0 + swz_chunk(r, l & 7) * 8;
       buf[i] = (r < rows && kk < kbound) ? *(const u32x4 *)(base + (row0 + r) * ld + kk) : u32x4{0, 0, 0, 0};
     }
   }
@@ -424,7 +431,8 @@ struct LQuantNK {
   __device__ __forceinline__ void prepare(const DecodeTables &tb) { dec.prepare(sraw, s2, tb); }
   // decode code word `part` (8 k) and write it into the tile
   __device__ __forceinline__ void store(LTile &t, int part) const {
-    st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + part * 8], dec(codes[part]));
+    const int row = threadIdx.x & 255;
+    st_lds16(&t.v[row][bswz(row, (threadIdx.x >> 8) * 4 + part)], dec(codes[part]));
   }
 };
 
@@ -491,7 +499,10 @@ struct LDenseNK {
   }
   __device__ __forceinline__ void store(LTile &t) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) st_lds16(&t.v[threadIdx.x & 255][(threadIdx.x >> 8) * 32 + 8 * v], buf[v]);
+    for (int v = 0; v < 4; ++v) {
+      const int row = threadIdx.x & 255;
+      st_lds16(&t.v[row][bswz(row, (threadIdx.x >> 8) * 4 + v)], buf[v]);
+    }
   }
 };
 
@@ -514,7 +525,8 @@ struct LMma {
   // B fragments from an [n][k] tile (ds_read_b128).
   __device__ __forceinline__ static bf16x8 bfrag_nk(const LTile &B, int j, int ks) {
     const int lane = threadIdx.x & 63;
-    return *(const bf16x8 *)&B.v[wn() * 64 + j * 32 + (lane & 31)][ks * 16 + (lane >> 5) * 8];
+    const int row = wn() * 64 + j * 32 + (lane & 31);
+    return *(const bf16x8 *)&B.v[row][bswz(row, ks * 2 + (lane >> 5))];
   }
   // B fragments from a [k][n] tile with the transposing LDS read: within each 16-lane
   // group, lane i receives element i%4 of the 8-byte pieces addressed by lanes 4j + i/4,

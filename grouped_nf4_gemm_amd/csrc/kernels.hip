@@ -247,7 +247,7 @@ struct LargePipe {
   using BTile = typename std::conditional<KN, LTileKN, LTile>::type;
   DecodeTables &tb;
   ATile &A0, &A1;
-  LTile &B0, &B1;
+  BBuf &B0, &B1;
   const GroupedArgs &g;
   __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
   LDirectA la;
@@ -256,7 +256,7 @@ struct LargePipe {
 
   // Members are set here, never zero-filled as an aggregate: a memset over the buffer
   // resources would keep them in memory and make every buffer load a per-lane loop.
-  __device__ __forceinline__ LargePipe(DecodeTables &tb_, ATile &a0, ATile &a1, LTile &b0, LTile &b1,
+  __device__ __forceinline__ LargePipe(DecodeTables &tb_, ATile &a0, ATile &a1, BBuf &b0, BBuf &b1,
                                        const GroupedArgs &g_)
       : tb(tb_), A0(a0), A1(a1), B0(b0), B1(b1), g(g_),
         ra(make_rsrc(g_.A, g_.a_bytes)),
@@ -271,8 +271,9 @@ struct LargePipe {
   }
   template <int P>
   __device__ __forceinline__ BTile &btile() {
-    if constexpr (P == 0) return *reinterpret_cast<BTile *>(&B0);
-    else return *reinterpret_cast<BTile *>(&B1);
+    BBuf &b = P == 0 ? B0 : B1;
+    if constexpr (KN) return b.kn;
+    else return b.nk;
   }
   // Loads of a slab past the end read zero (scalar offset pushed out of range), so every
   // load is issued unconditionally and the loop body is straight-line code.
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
   // 16-bit immediate of the LDS reads)
   __shared__ DecodeTables tb;
   __shared__ ATile A0, A1;
-  __shared__ LTile B0, B1;
+  __shared__ BBuf B0, B1;
   __shared__ int tile_sh[4];
   init_decode_tables(tb);
   TileM tm;
@@ -369,9 +370,9 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
       lx.load(g.xa, g.ldxa, tm.rows, tm.row0, k0, g.r);
       lbd.fetch(k0, g.r);
       lx.store(A0);
-      lbd.store(B0);
+      lbd.store(B0.nk);
       __syncthreads();
-      mma.step<false>(A0, B0, min(4, (g.r - k0 + 15) / 16));
+      mma.step<false>(A0, B0.nk, min(4, (g.r - k0 + 15) / 16));
       __syncthreads();
     }
   }
