@@ -158,7 +158,7 @@ struct KMajorLoader {
   __device__ __forceinline__ void fetch(const uint16_t *__restrict__ base, int64_t ld, int a0,
                                         int Na, int row0, int krows, const int32_t *__restrict__ gather,
                                         int gdiv, int k0) {
-    const int kb = threadIdx.x >> 4, ab = threadIdx.x & 15;
+    const int kb = threadIdx.x & 15, ab = threadIdx.x >> 4;
     const int a = a0 + ab * AW;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -179,8 +179,10 @@ struct KMajorLoader {
       }
     }
   }
+  // lanes 16j .. 16j+15 share a column group and cover the 64 k of a tile row: each
+  // 16-lane LDS pass writes 128 contiguous bytes of one row (no bank conflicts)
   __device__ __forceinline__ void store(LdsTile<BR> &t) {
-    const int kb = threadIdx.x >> 4, ab = threadIdx.x & 15;
+    const int kb = threadIdx.x & 15, ab = threadIdx.x >> 4;
 #pragma unroll
     for (int c = 0; c < AW; ++c) {
       const int sh = (c & 1) * 16, wi = c >> 1;
