@@ -58,6 +58,23 @@ __device__ __forceinline__ bf16x8 nf4_codes_bf16(uint32_t w, uint32_t l4, const 
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Static LDS of the two kernels: the code table (NF4 formats only) comes first, at LDS
+// address 0, so that a table address formed by a byte permute needs no base added.
+template <bool TABLE, class Rest>
+struct WithTable {
+  SmallTables tb;
+  Rest rest;
+};
+template <class Rest>
+struct WithTable<false, Rest> {
+  Rest rest;
+};
+template <bool TABLE, class Rest>
+__device__ __forceinline__ SmallTables &table_of(WithTable<TABLE, Rest> &s) {
+  if constexpr (TABLE) return s.tb;
+  else return *reinterpret_cast<SmallTables *>(&s);  // not read: the formats without a table
+}
+
 constexpr int SM_WAVES = 8, SM_THREADS = 64 * SM_WAVES;
 constexpr int SM_BMT = 32;                  // tokens per workgroup slot
 constexpr int SM_CB = 4;                    // 64-wide blocks per chunk
@@ -112,11 +129,14 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
                                                                  int64_t split_stride) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
   constexpr int R = DC + 1;  // chunk slots of the register ring
-  // the code table lives in dynamic LDS, sized at launch (NF4 formats only)
-  extern __shared__ __attribute__((aligned(16))) uint32_t small_lds[];
-  SmallTables &tb = *reinterpret_cast<SmallTables *>(small_lds);
-  __shared__ SmallX xs;
-  __shared__ int tile_sh[4];
+  struct Rest {
+    SmallX xs;
+    int tile_sh[4];
+  };
+  __shared__ __attribute__((aligned(16))) WithTable<NF4ISH, Rest> sm;
+  SmallTables &tb = table_of(sm);
+  SmallX &xs = sm.rest.xs;
+  int *tile_sh = sm.rest.tile_sh;
   if constexpr (NF4ISH) init_small_tables(tb);
   TileM tm;
   if (!find_tile(g.off, g.E, SM_BMT, blockIdx.y, tm, tile_sh)) return;  // (synchronises)
@@ -354,13 +374,18 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
                                                                    int64_t split_stride) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
   constexpr int D = 7, R = 8;
-  // dynamic LDS: the code table (NF4 formats), then the staged activation rows
-  // [rows][blocks of the split][64]
+  // static LDS: the code table (NF4 formats), a zero line and the tile scan; dynamic
+  // LDS: the staged activation rows [rows][blocks of the split][64]
+  struct Rest {
+    uint16_t xzero[64];
+    int tile_sh[4];
+  };
+  __shared__ __attribute__((aligned(16))) WithTable<NF4ISH, Rest> sm;
   extern __shared__ __attribute__((aligned(16))) uint32_t small_lds[];
-  SmallTables &tb = *reinterpret_cast<SmallTables *>(small_lds);
-  uint16_t *xs = (uint16_t *)(small_lds + (NF4ISH ? sizeof(SmallTables) / 4 : 0));
-  __shared__ __attribute__((aligned(16))) uint16_t xzero[64];
-  __shared__ int tile_sh[4];
+  SmallTables &tb = table_of(sm);
+  uint16_t *xs = (uint16_t *)small_lds;
+  uint16_t *xzero = sm.rest.xzero;
+  int *tile_sh = sm.rest.tile_sh;
   if (threadIdx.x < 8) *(u32x4 *)&xzero[threadIdx.x * 8] = u32x4{0, 0, 0, 0};
   TileM tm;
   if (!find_tile(g.off, g.E, XMAX, blockIdx.y, tm, tile_sh)) return;  // (synchronises)
@@ -420,9 +445,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     }
     const int tok = n;
     const bool xlane = tok >= t0 && tok < t0 + xrows;
-    // fragment source of this lane: its token row, or the zero line (stride 0)
+    // fragment source of this lane: its token row, or the zero line (block stride 0):
+    // every lane reads, branch-free, and the zero-line reads are one broadcast address
     const uint16_t *xsrc = xlane ? xs + (tok - t0) * xrow_len + 32 * hh : xzero;
-    const int xstep = xlane ? 1 : 0;
+    const int xjstride = xlane ? 64 : 0;
 
     u32x4 cw[R];
     ChunkScale sq[R / 4], cur;
@@ -468,14 +494,9 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       float sc;
     };
     auto prepare = [&](int d, int j, Ops &o) {
+      const uint16_t *xb = xsrc + xjstride * j;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-      // only the lanes of real tokens read activations (the others hold zeros), so the
-      // LDS traffic of the fragments scales with the tokens, not with the 32 MFMA rows
-      if (xlane) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xsrc + 64 * j + 8 * s4);
-      }
+      for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xb + 8 * s4);
       // the quad of block j: in the slot's own window if j starts it, else in `cur`
       const float sc = d % 4 == 0 ? scale_in(sq[d / 4], 0, j) : scale_in(cur, d % 4, j);
       // a block past the range has zero codes (nf4 code 0 = -1): zero its scale
@@ -585,16 +606,15 @@ static bool use_direct(const GroupedArgs &a, int kbs) {
 template <int FMT, int EPI>
 static void launch_small_fmt(const GroupedArgs &a, int spw, int strips_per_expert, int slots, int splits,
                              int kbs, int64_t split_stride, hipStream_t s) {
-  const size_t lds = FMT == FMT_MXFP4 ? 0 : sizeof(SmallTables);
   (void)spw;
   (void)slots;
   if (use_direct(a, kbs)) {
     const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, XMAX), splits);
     const size_t xlds = (size_t)direct_rows(a) * kbs * 64 * 2;
-    small_direct_kernel<FMT, EPI><<<grid, SM_THREADS, lds + xlds, s>>>(a, kbs, split_stride);
+    small_direct_kernel<FMT, EPI><<<grid, SM_THREADS, xlds, s>>>(a, kbs, split_stride);
   } else {
     const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, SM_BMT), splits);
-    small_gemm_kernel<FMT, 1, EPI, 3><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride);
+    small_gemm_kernel<FMT, 1, EPI, 3><<<grid, SM_THREADS, 0, s>>>(a, kbs, split_stride);
   }
 }
 
