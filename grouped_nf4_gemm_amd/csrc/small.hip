@@ -367,6 +367,8 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
 // operands of block j+1 (activation fragments, table reads, scale) are read while the
 // MFMAs of block j run.  Eight waves per workgroup, one strip each.
 constexpr int XMAX = 8;
+// (the block scaling touches accumulator values v < 4 only: C rows 8(v/4) + 4h + v%4 < 8)
+static_assert(XMAX == 8, "token rows of a direct slot");
 constexpr int XPT = 8;  // staged 16-byte activation pieces per thread: rows x blocks <= 512
 
 template <int FMT, int EPI>
@@ -494,7 +496,9 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       float sc;
     };
     auto prepare = [&](int d, int j, Ops &o) {
-      const uint16_t *xb = xsrc + xjstride * j;
+      // blocks past the range (the ring runs up to R - 1 blocks beyond it) read the zero
+      // line: the staged rows end at the range, and LDS past them is not initialised
+      const uint16_t *xb = j < nblk ? xsrc + xjstride * j : xzero;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xb + 8 * s4);
       // the quad of block j: in the slot's own window if j starts it, else in `cur`
@@ -512,8 +516,9 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         f32x16 blk = {};
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) blk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[s4], o.b[s4], blk, 0, 0, 0);
+        // only C rows 8(v/4) + 4h + v%4 < XMAX hold tokens of the slot: v < 4
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] += o.sc * blk[v];
+        for (int v = 0; v < 4; ++v) acc[v] += o.sc * blk[v];
       } else {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[s4], o.b[s4], acc, 0, 0, 0);

@@ -136,3 +136,25 @@ def test_zero_tokens():
     assert out["y"].shape == (0, 64) and out["dx"].shape == (0, 64)
     for k in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
         assert torch.count_nonzero(out[k]) == 0
+
+
+def test_decode_shape_ignores_stale_lds():
+    """Few tokens per expert (the weight-streaming path): blocks past the K range must
+    not read LDS that this call did not write.  A call whose staged activations are all
+    +Inf runs first, then a call with one token per expert; its output must be finite
+    and equal, bit for bit, to the same call after a clean one."""
+    s = synth.custom(4, 192, 192, 4, 1, 8, 16.0, "nf4", name="decode-stale")
+    clean = synth.make_inputs(s, seed=41)
+    clean.ids[:, 0] = np.arange(4)
+    poison = synth.make_inputs(s, seed=41)
+    poison.ids[:, 0] = 0
+    poison.x[:] = np.uint16(0x7F80)  # +Inf in every activation
+    case_c = Case(clean, train=False)
+    case_p = Case(poison, train=False)
+    case_c.run(dgrad=False)
+    ref = case_c.run(dgrad=False)["y"].clone()
+    case_p.run(dgrad=False)
+    got = case_c.run(dgrad=False)["y"]
+    assert torch.isfinite(got.float()).all()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    _check_all(case_c, {"y": got})
