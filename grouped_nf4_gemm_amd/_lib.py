@@ -14,6 +14,8 @@ SO_PATH = os.path.join(_PKG, "libe4b.so")
 E4B_OK, E4B_ERR_INVALID_ARG, E4B_ERR_UNSUPPORTED, E4B_ERR_WORKSPACE, E4B_ERR_HIP = range(5)
 FMT = {"nf4": 0, "nf4_dq": 1, "mxfp4": 2}
 E4B_TRAIN = 1
+E4B_EXPAND = 2
+E4B_NO_EXPAND = 4
 
 EXPORTS = [
     "e4b_version", "e4b_status_str", "e4b_moe_workspace_size", "e4b_moe_fwd", "e4b_moe_dgrad",
@@ -48,7 +50,7 @@ class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "launches_total", "route", "lora_a", "gemm_gate_up", "gemm_down", "combine",
         "combine_bwd", "gemm_down_dgrad", "gemm_gate_up_dgrad", "unpermute", "wgrad", "quant",
-        "dequant", "fallbacks")]
+        "dequant", "expand", "fallbacks")]
 
 
 _lib = None

@@ -30,7 +30,7 @@ const char *family_name(int f) {
                                          "gemm_down",      "combine",      "combine_bwd",
                                          "gemm_down_dgrad", "gemm_gate_up_dgrad", "unpermute",
                                          "wgrad",          "quant",        "dequant",
-                                         "transpose"};
+                                         "transpose",      "expand"};
   return (f >= 0 && f < FAM_COUNT) ? names[f] : "?";
 }
 
@@ -60,9 +60,27 @@ bool last_launch_ok() { return hipGetLastError() == hipSuccess; }
 
 // ------------------------------------------------------------------ workspace layout
 struct Layout {
-  size_t cnt, off, perm, inv, z1, z2, G, h, O, dO, u2, dG, u1, dXp, A1T, B1T, A2T, B2T, part, total;
+  size_t cnt, off, perm, inv, z1, z2, G, h, O, dO, u2, dG, u1, dXp, A1T, B1T, A2T, B2T, part, W1x, W2x,
+      total;
 };
 static constexpr size_t NONE = ~(size_t)0;
+// Activations and stacks that the 4-bit GEMMs stream with buffer loads must each stay
+// below 2 GiB (32-bit per-lane byte offsets).
+static constexpr int64_t BUF_LIMIT = ((int64_t)1 << 31) - 1;
+
+// Large batches: with many row tiles per expert, the large-tile GEMMs would decode every
+// weight once per row tile.  Above EXPAND_MIN_ROWS routed rows per expert on average the
+// forward instead writes bf16 copies of both stacks into the workspace once (kept for the
+// dgrad of a training forward) and the GEMMs load those directly.  E4B_EXPAND and
+// E4B_NO_EXPAND override the choice; the decode-shaped path (few rows) never expands.
+static constexpr int64_t EXPAND_MIN_ROWS = 1024;
+static bool use_expand(const e4b_moe_desc &d) {
+  const int64_t M = (int64_t)d.T * d.topk;
+  if (M <= SMALL_M_MAX || (d.flags & E4B_NO_EXPAND)) return false;
+  if ((int64_t)2 * d.I * d.H * 2 > BUF_LIMIT) return false;  // one expert's copy: 32-bit offsets
+  if (d.flags & E4B_EXPAND) return true;
+  return M >= EXPAND_MIN_ROWS * d.E;
+}
 
 static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
   Layout L;
@@ -117,6 +135,12 @@ static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
     if (r2) { wgrad((int)H, r2); wgrad(r2, (int)I); }
   }
   L.part = part ? take(part) : NONE;
+  if (use_expand(d)) {
+    L.W1x = take(E * 2 * I * H * 2);
+    L.W2x = take(E * H * I * 2);
+  } else {
+    L.W1x = L.W2x = NONE;
+  }
   L.total = o;
   return L;
 }
@@ -127,9 +151,6 @@ static T *at(void *ws, size_t off) {
 }
 
 // ------------------------------------------------------------------ validation
-// Activations and stacks that the 4-bit GEMMs stream with buffer loads must each stay
-// below 2 GiB (32-bit per-lane byte offsets).
-static constexpr int64_t BUF_LIMIT = ((int64_t)1 << 31) - 1;
 
 static e4b_status check_desc(const e4b_moe_desc *d) {
   if (!d) return E4B_ERR_INVALID_ARG;
@@ -139,7 +160,8 @@ static e4b_status check_desc(const e4b_moe_desc *d) {
   const int64_t M = (int64_t)d->T * d->topk;
   if ((int64_t)d->T * d->H * 2 > BUF_LIMIT || M * d->H * 4 > BUF_LIMIT || M * 2 * d->I * 2 > BUF_LIMIT)
     return E4B_ERR_INVALID_ARG;
-  if (d->flags & ~E4B_TRAIN) return E4B_ERR_INVALID_ARG;
+  if (d->flags & ~(E4B_TRAIN | E4B_EXPAND | E4B_NO_EXPAND)) return E4B_ERR_INVALID_ARG;
+  if ((d->flags & E4B_EXPAND) && (d->flags & E4B_NO_EXPAND)) return E4B_ERR_INVALID_ARG;
   return E4B_OK;
 }
 
@@ -247,9 +269,15 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
   float *O = at<float>(ws, L.O);
   uint16_t *G = L.G == NONE ? nullptr : at<uint16_t>(ws, L.G);
   float *part = L.part == NONE ? nullptr : at<float>(ws, L.part);
+  uint16_t *W1x = L.W1x == NONE ? nullptr : at<uint16_t>(ws, L.W1x);
+  uint16_t *W2x = L.W2x == NONE ? nullptr : at<uint16_t>(ws, L.W2x);
 
   E4B_LAUNCH(launch_route(ids, M, E, cnt, off, perm, inv, s));
   if (M == 0) return E4B_OK;
+  if (W1x) {
+    E4B_LAUNCH(launch_expand(qstack(w_gu), E, W1x, s));
+    E4B_LAUNCH(launch_expand(qstack(w_dn), E, W2x, s));
+  }
   // few routed rows: weight-streaming kernels (small.hip); otherwise the large tiles
   const bool small = M <= SMALL_M_MAX;
   const bool train = d.flags & E4B_TRAIN;
@@ -270,6 +298,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.A = x; a.lda = H; a.a_gather = perm; a.a_gdiv = d.topk;
     a.a_bytes = (uint32_t)((int64_t)d.T * H * 2);
     a.q = qstack(w_gu);
+    a.Bx = W1x; a.bx_estride = (int64_t)2 * I * H; a.bx_bytes = (uint32_t)(a.bx_estride * 2);
     a.xa = z1; a.ldxa = r1; a.xb = r1 ? l_gu->B : nullptr; a.xb_estride = (int64_t)2 * I * r1;
     a.ldxb = r1; a.r = r1;
     a.C = h; a.ldc = I; a.alpha = 1.0f;
@@ -292,6 +321,7 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.A = h; a.lda = I; a.a_gdiv = 1;
     a.a_bytes = (uint32_t)((int64_t)M * I * 2);
     a.q = qstack(w_dn);
+    a.Bx = W2x; a.bx_estride = (int64_t)H * I; a.bx_bytes = (uint32_t)(a.bx_estride * 2);
     a.xa = z2; a.ldxa = r2; a.xb = r2 ? l_dn->B : nullptr; a.xb_estride = (int64_t)H * r2;
     a.ldxb = r2; a.r = r2;
     a.C = O; a.ldc = H; a.alpha = 1.0f; a.I = I;
@@ -328,6 +358,9 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
   float *part = L.part == NONE ? nullptr : at<float>(ws, L.part);
   uint16_t *A1T = at<uint16_t>(ws, L.A1T), *B1T = at<uint16_t>(ws, L.B1T);
   uint16_t *A2T = at<uint16_t>(ws, L.A2T), *B2T = at<uint16_t>(ws, L.B2T);
+  // bf16 copies of the stacks that the training forward wrote (expanded calls only)
+  const uint16_t *W1x = L.W1x == NONE ? nullptr : at<uint16_t>(ws, L.W1x);
+  const uint16_t *W2x = L.W2x == NONE ? nullptr : at<uint16_t>(ws, L.W2x);
 
   E4B_LAUNCH(launch_combine_bwd(dy, O, inv, topw, d.T, d.topk, H, dO, d_topw, s));
   if (r2) {
@@ -347,6 +380,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     a.A = dO; a.lda = H; a.a_gdiv = 1;
     a.a_bytes = (uint32_t)((int64_t)M * H * 2);
     a.q = qstack(w_dn);
+    a.Bx = W2x; a.bx_estride = (int64_t)H * I; a.bx_bytes = (uint32_t)(a.bx_estride * 2);
     a.xa = u2; a.ldxa = r2; a.xb = r2 ? A2T : nullptr; a.xb_estride = (int64_t)I * r2;
     a.ldxb = r2; a.r = r2;
     a.Gin = G; a.Gout = dG; a.ldg = 2 * I; a.I = I;
@@ -369,6 +403,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     a.A = dG; a.lda = 2 * I; a.a_gdiv = 1;
     a.a_bytes = (uint32_t)((int64_t)M * 2 * I * 2);
     a.q = qstack(w_gu);
+    a.Bx = W1x; a.bx_estride = (int64_t)2 * I * H; a.bx_bytes = (uint32_t)(a.bx_estride * 2);
     a.xa = u1; a.ldxa = r1; a.xb = r1 ? A1T : nullptr; a.xb_estride = (int64_t)H * r1;
     a.ldxb = r1; a.r = r1;
     a.C = dXp; a.ldc = H; a.alpha = 1.0f; a.I = I;
@@ -497,6 +532,7 @@ e4b_status e4b_get_stats(e4b_stats *out) {
   out->wgrad = g_count[FAM_WGRAD].load();
   out->quant = g_count[FAM_QUANT].load();
   out->dequant = g_count[FAM_DEQUANT].load();
+  out->expand = g_count[FAM_EXPAND].load();
   out->fallbacks = 0;
   return E4B_OK;
 }

@@ -54,10 +54,45 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ off, int E
     }
   }
   __syncthreads();
-  t.e = s_e;
-  t.row0 = s_row0;
-  t.rows = s_rows;
+  // the same for every lane: kept in scalar registers (buffer resources built from them
+  // must be wave-uniform)
+  t.e = __builtin_amdgcn_readfirstlane(s_e);
+  t.row0 = __builtin_amdgcn_readfirstlane(s_row0);
+  t.rows = __builtin_amdgcn_readfirstlane(s_rows);
   return t.e >= 0;
+}
+
+// The same lookup done by each wave on its own, with no LDS and no barrier; the result is
+// wave-uniform (scalar registers).
+__device__ __forceinline__ bool find_tile_wave(const int32_t *__restrict__ off, int E, int BMt, int slot, TileM &t) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int c = 0; c < E; c += 64) {
+    const int ee = c + lane;
+    const int cnt = ee < E ? off[ee + 1] - off[ee] : 0;
+    const int nt = (cnt + BMt - 1) / BMt;
+    int incl = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int excl = incl - nt;
+    const uint64_t hit = __ballot(nt > 0 && slot >= base + excl && slot < base + incl);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int e = __builtin_amdgcn_readfirstlane(__shfl(ee, src));
+      const int mt = slot - base - __builtin_amdgcn_readfirstlane(__shfl(excl, src));
+      const int n = __builtin_amdgcn_readfirstlane(__shfl(cnt, src));
+      t.e = e;
+      t.row0 = __builtin_amdgcn_readfirstlane(off[e]) + mt * BMt;
+      t.rows = min(BMt, n - mt * BMt);
+      return true;
+    }
+    base += __shfl(incl, 63);
+    if (base > slot) break;
+  }
+  return false;
 }
 
 // ---------------------------------------------------------------- LDS tiles
@@ -278,6 +313,21 @@ __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t v
 __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
+__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint16_t v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ void bstore32(__amdgpu_buffer_rsrc_t r, float v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, 0, 0);
+}
+// Buffer over rows row0 .. row0 + rows - 1 of a row-major matrix with ld elements of esize
+// bytes per row: per-lane offsets past the last row read zero / are not written.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *base, int64_t row0, int rows, int64_t ld,
+                                                            int esize) {
+  return make_rsrc((const char *)base + row0 * ld * esize, (uint32_t)(rows * ld * esize));
+}
 
 // Operand tiles of 64-wide slabs: rows of 64 bf16 (128 bytes, no padding) whose eight
 // 16-byte chunks sit at chunk ^ ((row >> 1) & 7).  LDS serves 16 lanes of a 16-byte access
@@ -305,10 +355,21 @@ __device__ __forceinline__ int knswz(int col) {
   const int c = col >> 3;
   return ((c ^ ((c >> 3) & 3)) << 3) | (col & 7);
 }
-// one LDS buffer holds either B tile layout
+// [64 k][256 n] bf16 without padding, for B tiles that direct-to-LDS loads fill from a
+// bf16 copy of a stack stored [K rows][N]: row k keeps its 16-byte chunk c at c ^ ((k & 3)
+// << 2).  A 32-lane pass of the transposing fragment read covers 4 rows x 4 chunks, which
+// the swizzle spreads over 16 distinct groups of 4 banks; the loads write whole 1 KB blocks.
+struct LTileKD {
+  uint16_t v[BK][L_BN];
+};
+__device__ __forceinline__ int kdswz(int k, int col) {
+  return (((col >> 3) ^ ((k & 3) << 2)) << 3) | (col & 7);
+}
+// one LDS buffer holds any of the B tile layouts
 union BBuf {
   LTile nk;
   LTileKN kn;
+  LTileKD kd;
 };
 
 // A: 256 rows x 64 k of a row-major bf16 matrix (optionally gathered rows) loaded
@@ -338,6 +399,54 @@ struct LDirectA {
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void *)&t.v[(w * 4 + i) * 8 * BK], 16, voff[i], soff, 0, 0);
+  }
+};
+
+// B rows of a bf16 copy of a stack stored [N, K] (K contiguous) straight into an [n][k] tile,
+// with the A tile's block mapping; tile row lr holds weight row map(lr).  Rows past Nrows
+// read as zero.
+struct LDirectBNK {
+  uint32_t voff[4];
+  __device__ __forceinline__ void init(const RowMap &map, int Nrows, int64_t K) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (w * 4 + i) * 8 + (l >> 3);
+      const int n = map(r);
+      voff[i] = n < Nrows ? (uint32_t)(((int64_t)n * K + swz_chunk(r, l & 7) * 8) * 2) : OOB;
+    }
+  }
+  // soff: byte offset of the slab's first column (OOB: the slab reads as zero)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, LTile &t, uint32_t soff) {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void *)&t.v[(w * 4 + i) * 8][0], 16, voff[i], soff, 0, 0);
+  }
+};
+// B of a bf16 copy of a stack stored [Krows, Ncols] reduced over its stored rows, into a
+// [64 k][256 n] tile (LTileKD): wave w, load i fills stored rows 2 (4w + i) and +1 of the
+// slab; lane l reads row 2 (4w + i) + l / 32, the chunk that lands at physical chunk l % 32.
+// Columns past Ncols read as zero.
+struct LDirectBKN {
+  uint32_t voff[4];
+  __device__ __forceinline__ void init(int n0, int Ncols) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = (w * 4 + i) * 2 + (l >> 5);
+      const int col = n0 + (((l & 31) ^ ((k & 3) << 2)) << 3);
+      voff[i] = col < Ncols ? (uint32_t)(((int64_t)k * Ncols + col) * 2) : OOB;
+    }
+  }
+  // soff: byte offset of the slab's first stored row (OOB: the slab reads as zero)
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, LTileKD &t, uint32_t soff) {
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void *)&t.v[(w * 4 + i) * 2][0], 16, voff[i], soff, 0, 0);
   }
 };
 
@@ -545,6 +654,21 @@ struct LMma {
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
   }
+  // B fragments from an unpadded [k][n] tile (LTileKD), transposing LDS read as above.
+  __device__ __forceinline__ static bf16x8 bfrag_kd(const LTileKD &B, int j, int ks) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 4, i = lane & 15;
+    const int row = ks * 16 + (G >> 1) * 8 + (i >> 2);
+    const int col = wn() * 64 + j * 32 + (G & 1) * 16 + (i & 3) * 4;
+    typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row][kdswz(row, col)]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row + 4][kdswz(row + 4, col)]));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+  }
+  __device__ __forceinline__ static bf16x8 bfrag(const LTile &B, int j, int ks) { return bfrag_nk(B, j, ks); }
+  __device__ __forceinline__ static bf16x8 bfrag(const LTileKN &B, int j, int ks) { return bfrag_kn(B, j, ks); }
+  __device__ __forceinline__ static bf16x8 bfrag(const LTileKD &B, int j, int ks) { return bfrag_kd(B, j, ks); }
   // The operand fragments of one k-step (16 k) for this wave.
   struct Frag {
     bf16x8 a[4], b[2];
@@ -554,10 +678,7 @@ struct LMma {
     const int lane = threadIdx.x & 63;
     const int r = lane & 31, kc = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if constexpr (KN) f.b[j] = bfrag_kn(B, j, ks);
-      else f.b[j] = bfrag_nk(B, j, ks);
-    }
+    for (int j = 0; j < 2; ++j) f.b[j] = bfrag(B, j, ks);
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.a[i] = *(const bf16x8 *)&A.v[aswz(wm() * 128 + i * 32 + r, kc)];
   }

@@ -334,6 +334,219 @@ struct LargePipe {
   }
 };
 
+// The same main loop over a bf16 copy of the stack (written by expand_kernel with the same
+// decode functions): A and B both go HBM -> LDS by direct loads, with no decode work, and
+// the MFMA sequence over identical LDS contents is that of LargePipe, so the two give
+// bit-identical accumulators.  The A rows land one slab ahead; the weight tiles, which
+// other workgroups on the same L2 rarely share, land two slabs ahead in a ring of three
+// LDS tiles.
+union XBuf {
+  LTile nk;
+  LTileKD kd;
+};
+template <bool KN>
+struct XPipe {
+  using BTile = typename std::conditional<KN, LTileKD, LTile>::type;
+  ATile &A0, &A1;
+  XBuf &B0, &B1, &B2;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  LDirectA la;
+  typename std::conditional<KN, LDirectBKN, LDirectBNK>::type lb;
+  uint32_t bstep;  // bytes of B per slab
+  LMma mma;
+  LMma::Frag f[2];
+  __device__ __forceinline__ XPipe(ATile &a0, ATile &a1, XBuf &b0, XBuf &b1, XBuf &b2, const GroupedArgs &g,
+                                   int e)
+      : A0(a0), A1(a1), B0(b0), B1(b1), B2(b2),
+        ra(make_rsrc(g.A, g.a_bytes)),
+        rb(make_rsrc(g.Bx + (int64_t)e * g.bx_estride, g.bx_bytes)),
+        bstep(KN ? (uint32_t)(BK * g.N * 2) : (uint32_t)(BK * 2)) {}
+  template <int P>
+  __device__ __forceinline__ ATile &atile() {
+    if constexpr (P == 0) return A0;
+    else return A1;
+  }
+  template <int Q>
+  __device__ __forceinline__ BTile &btile() {
+    XBuf &b = Q == 0 ? B0 : Q == 1 ? B1 : B2;
+    if constexpr (KN) return b.kd;
+    else return b.nk;
+  }
+  __device__ __forceinline__ static uint32_t dead(int slab, int nmain) { return slab < nmain ? 0u : OOB; }
+  template <int P>
+  __device__ __forceinline__ void issue_a(int slab, int nmain) {
+    la.issue(ra, atile<P>(), (uint32_t)(slab * BK * 2) | dead(slab, nmain));
+  }
+  template <int Q>
+  __device__ __forceinline__ void issue_b(int slab, int nmain) {
+    lb.issue(rb, btile<Q>(), (uint32_t)slab * bstep | dead(slab, nmain));
+  }
+  // Scheduling hint for one k-step: each MFMA followed by one fragment read of the next.
+  __device__ __forceinline__ static void interleave() {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+  }
+  // Slab s computes from A tile P = s % 2 and B tile Q = s % 3.  Fragments are read one
+  // k-step ahead (f[0] holds k-step 0 of slab s on entry).  The barrier sits between the
+  // reads of k-step 3 and its MFMAs: past it the A rows and weights of slab s+1 are in LDS
+  // and every wave has finished reading slab s, so k-step 0 of slab s+1 is read while the
+  // last MFMAs of slab s run.  The B loads of slab s+2 go into the tile slab s-1 used.
+  template <int P, int Q>
+  __device__ __forceinline__ void body(int s, int nmain) {
+    issue_a<P ^ 1>(s + 1, nmain);
+    issue_b<(Q + 2) % 3>(s + 2, nmain);
+    __builtin_amdgcn_sched_barrier(0);
+    LMma::load<KN>(atile<P>(), btile<Q>(), 1, f[1]);
+    mma.mma(f[0]);
+    interleave();
+    LMma::load<KN>(atile<P>(), btile<Q>(), 2, f[0]);
+    mma.mma(f[1]);
+    interleave();
+    LMma::load<KN>(atile<P>(), btile<Q>(), 3, f[1]);
+    mma.mma(f[0]);
+    interleave();
+    slab_barrier<4>();  // A rows and weights of slab s+1 have landed (those of s+2 may not)
+    LMma::load<KN>(atile<P ^ 1>(), btile<(Q + 1) % 3>(), 0, f[0]);
+    mma.mma(f[1]);
+    interleave();
+  }
+  __device__ __forceinline__ void run(int nmain) {
+    issue_a<0>(0, nmain);
+    issue_b<0>(0, nmain);
+    issue_b<1>(1, nmain);
+    wait_lds_dma();
+    __syncthreads();
+    LMma::load<KN>(A0, btile<0>(), 0, f[0]);
+    // six bodies cycle both tile rings
+    for (int s = 0;; s += 6) {
+      body<0, 0>(s, nmain);
+      if (s + 1 >= nmain) break;
+      body<1, 1>(s + 1, nmain);
+      if (s + 2 >= nmain) break;
+      body<0, 2>(s + 2, nmain);
+      if (s + 3 >= nmain) break;
+      body<1, 0>(s + 3, nmain);
+      if (s + 4 >= nmain) break;
+      body<0, 1>(s + 4, nmain);
+      if (s + 5 >= nmain) break;
+      body<1, 2>(s + 5, nmain);
+      if (s + 6 >= nmain) break;
+    }
+    // the last body's weight loads (past the end) must land before B0 is reused
+    wait_lds_dma();
+    __syncthreads();
+  }
+};
+
+// After the main loop: the LoRA K-extension into the same accumulator (through the A0 /
+// B0 tiles), then the epilogue.
+template <int EPI>
+__device__ __forceinline__ void large_finish(LMma &mma, const GroupedArgs &g, const TileM &tm, int e, int n0,
+                                             const RowMap &map, int Nrows, ATile &A0, LTile &B0) {
+  if (g.r > 0) {  // LoRA rank as a K-extension of the same accumulator
+    LRegA lx;
+    LDenseNK lbd;
+    lbd.init(g.xb + (int64_t)e * g.xb_estride, g.ldxb, map, Nrows);
+    for (int k0 = 0; k0 < g.r; k0 += BK) {
+      lx.load(g.xa, g.ldxa, tm.rows, tm.row0, k0, g.r);
+      lbd.fetch(k0, g.r);
+      lx.store(A0);
+      lbd.store(B0);
+      __syncthreads();
+      mma.step<false>(A0, B0, min(4, (g.r - k0 + 15) / 16));
+      __syncthreads();
+    }
+  }
+
+  // Outputs go through buffer resources over exactly this tile's rows, so the range check
+  // drops the stores of rows past the tile; a lane whose column is past the end gets an
+  // out-of-range offset.  Each lane's offset is fixed; the (i, v) step of the accumulator
+  // element adds a multiple of the row pitch that is the same for all lanes.
+  const int lane = threadIdx.x & 63;
+  const int rl = LMma::wm() * 128 + (lane >> 5) * 4;  // the lane's first tile row
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    // tile rows interleave 32 gate and 32 up weight rows: the wave's pair (0, 1) holds gate
+    // and up of h columns n0 + wn*32 + lane%32
+    const int col = n0 + LMma::wn() * 32 + (lane & 31);
+    const __amdgpu_buffer_rsrc_t rh = rows_rsrc(g.C, tm.row0, tm.rows, g.ldc, 2);
+    const uint32_t hoff = col < g.I ? (uint32_t)((rl * g.ldc + col) * 2) : OOB;
+    const uint32_t hpitch = (uint32_t)(g.ldc * 2);
+    if (g.Gout) {
+      const __amdgpu_buffer_rsrc_t rg = rows_rsrc(g.Gout, tm.row0, tm.rows, g.ldg, 2);
+      const uint32_t goff = col < g.I ? (uint32_t)((rl * g.ldg + col) * 2) : OOB;
+      const uint32_t gpitch = (uint32_t)(g.ldg * 2), uoff = (uint32_t)(g.I * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+          const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
+          const float act = gt * sigmoid_fast(gt);
+          bstore16(rh, f2bf(act * up), hoff + dr * hpitch);
+          bstore16(rg, f2bf(gt), goff + dr * gpitch);
+          bstore16(rg, f2bf(up), goff + dr * gpitch + uoff);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+          const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
+          const float act = gt * sigmoid_fast(gt);
+          bstore16(rh, f2bf(act * up), hoff + dr * hpitch);
+        }
+    }
+  } else if constexpr (EPI == EPI_F32) {
+    const __amdgpu_buffer_rsrc_t rc = rows_rsrc(g.C, tm.row0, tm.rows, g.ldc, 4);
+    const uint32_t pitch = (uint32_t)(g.ldc * 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + LMma::col_of(j);
+      const uint32_t off = n < g.N ? (uint32_t)((rl * g.ldc + n) * 4) : OOB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+          bstore32(rc, g.alpha * mma.acc[i][j][v], off + dr * pitch);
+        }
+    }
+  } else {  // EPI_SWIGLU_BWD: acc = dh; dG from the saved pre-activation G
+    // G and dG are separate buffers.  The 32 G values of a 16-row group are loaded before
+    // any of them is used, so their latencies overlap; rows past the tile read zero.
+    const __amdgpu_buffer_rsrc_t ri = rows_rsrc(g.Gin, tm.row0, tm.rows, g.ldg, 2);
+    const __amdgpu_buffer_rsrc_t ro = rows_rsrc(g.Gout, tm.row0, tm.rows, g.ldg, 2);
+    const uint32_t pitch = (uint32_t)(g.ldg * 2), uoff = (uint32_t)(g.I * 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + LMma::col_of(j);
+      const uint32_t off = n < g.N ? (uint32_t)((rl * g.ldg + n) * 2) : OOB;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t gv[16], uv[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t o = off + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * pitch;
+          gv[v] = bload16(ri, o);
+          uv[v] = bload16(ri, o + uoff);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t o = off + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * pitch;
+          const float dh = mma.acc[i][j][v], gt = bf2f((uint16_t)gv[v]), up = bf2f((uint16_t)uv[v]);
+          const float sg = sigmoid_fast(gt);
+          bstore16(ro, f2bf(dh * up * sg * (1.0f + gt * (1.0f - sg))), o);
+          bstore16(ro, f2bf(dh * gt * sg), o + uoff);
+        }
+      }
+    }
+  }
+}
+
 template <int BKIND, int EPI, bool SWIGLU, int FMT>
 __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
   // separate LDS objects, so the compiler can tell the A tiles that direct loads fill
@@ -360,97 +573,37 @@ __global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
   pipe.lb[1] = pipe.lb[0];
   pipe.lb[2] = pipe.lb[0];
   pipe.run(g.K / BK);
-  LMma &mma = pipe.mma;
+  large_finish<EPI>(pipe.mma, g, tm, e, n0, map, Nrows, A0, B0.nk);
+}
 
-  if (g.r > 0) {  // LoRA rank as a K-extension of the same accumulator
-    LRegA lx;
-    LDenseNK lbd;
-    lbd.init(g.xb + (int64_t)e * g.xb_estride, g.ldxb, map, Nrows);
-    for (int k0 = 0; k0 < g.r; k0 += BK) {
-      lx.load(g.xa, g.ldxa, tm.rows, tm.row0, k0, g.r);
-      lbd.fetch(k0, g.r);
-      lx.store(A0);
-      lbd.store(B0.nk);
-      __syncthreads();
-      mma.step<false>(A0, B0.nk, min(4, (g.r - k0 + 15) / 16));
-      __syncthreads();
-    }
-  }
+// The large tile over a bf16 copy of the stack (XPipe).  Its LDS is the two A tiles and
+// the three B tiles (160 KB): the tile lookup runs in every wave instead of through LDS.
+template <bool KN, int EPI, bool SWIGLU>
+__global__ __launch_bounds__(L_THREADS) void gemm_x_kernel(GroupedArgs g) {
+  __shared__ ATile A0, A1;
+  __shared__ XBuf B0, B1, B2;
+  TileM tm;
+  if (!find_tile_wave(g.off, g.E, L_BM, blockIdx.y, tm)) return;
+  const int e = tm.e;
+  const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
+  const RowMap map{n0, g.I, SWIGLU};
+  const int Nrows = SWIGLU ? 2 * g.I : g.N;
 
-  const int lane = threadIdx.x & 63;
-  if constexpr (EPI == EPI_SWIGLU_FWD) {
-    // tile rows interleave 32 gate and 32 up weight rows: the wave's pair (0, 1) holds gate
-    // and up of h columns n0 + wn*32 + lane%32
-    uint16_t *Hout = (uint16_t *)g.C;
-    const int col = n0 + LMma::wn() * 32 + (lane & 31);
-    if (col < g.I) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = LMma::row_of(i, v);
-          if (row < tm.rows) {
-            const int64_t p = tm.row0 + row;
-            const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
-            const float act = gt * sigmoid_fast(gt);
-            Hout[p * g.ldc + col] = f2bf(act * up);
-            if (g.Gout) {
-              g.Gout[p * g.ldg + col] = f2bf(gt);
-              g.Gout[p * g.ldg + g.I + col] = f2bf(up);
-            }
-          }
-        }
-    }
-  } else if constexpr (EPI == EPI_F32) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + LMma::col_of(j);
-      if (n >= g.N) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = LMma::row_of(i, v);
-          if (row < tm.rows) ((float *)g.C)[(tm.row0 + row) * g.ldc + n] = g.alpha * mma.acc[i][j][v];
-        }
-    }
-  } else {  // EPI_SWIGLU_BWD: acc = dh; dG from the saved pre-activation G
-    // G and dG are separate buffers.  The 32 G values of a 16-row group are loaded
-    // unconditionally (rows past the tile read the tile's first row) before any of them is
-    // used, so their latencies overlap instead of adding up.
-    const uint16_t *__restrict__ gin = g.Gin;
-    uint16_t *__restrict__ gout = g.Gout;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + LMma::col_of(j);
-      const bool nok = n < g.N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t gv[16], uv[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = LMma::row_of(i, v);
-          const int64_t off = nok && row < tm.rows ? (tm.row0 + row) * g.ldg + n : tm.row0 * g.ldg;
-          gv[v] = gin[off];
-          uv[v] = gin[off + g.I];
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = LMma::row_of(i, v);
-          if (!nok || row >= tm.rows) continue;
-          const int64_t off = (tm.row0 + row) * g.ldg + n;
-          const float dh = mma.acc[i][j][v], gt = bf2f((uint16_t)gv[v]), up = bf2f((uint16_t)uv[v]);
-          const float sg = sigmoid_fast(gt);
-          gout[off] = f2bf(dh * up * sg * (1.0f + gt * (1.0f - sg)));
-          gout[off + g.I] = f2bf(dh * gt * sg);
-        }
-      }
-    }
-  }
+  XPipe<KN> pipe(A0, A1, B0, B1, B2, g, e);
+  pipe.mma.zero();
+  pipe.la.init(tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
+  if constexpr (KN) pipe.lb.init(n0, g.N);
+  else pipe.lb.init(map, Nrows, g.K);
+  pipe.run(g.K / BK);
+  large_finish<EPI>(pipe.mma, g, tm, e, n0, map, Nrows, A0, B0.nk);
 }
 
 template <int BKIND, int EPI, bool SWIGLU>
 static void launch_large(const GroupedArgs &a, dim3 grid, hipStream_t s) {
+  if (a.Bx) {  // bf16 copy of the stack: no decode in the GEMM
+    gemm_x_kernel<BKIND == B_QKN, EPI, SWIGLU><<<grid, L_THREADS, 0, s>>>(a);
+    return;
+  }
   switch (a.q.fmt) {
     case FMT_NF4: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_NF4><<<grid, L_THREADS, 0, s>>>(a); break;
     case FMT_NF4_DQ: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_NF4_DQ><<<grid, L_THREADS, 0, s>>>(a); break;
@@ -853,6 +1006,50 @@ __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *_
     *(f32x4 *)(f32 + i * 8 + 4) = b;
   }
   if (b16) *(u32x4 *)(b16 + i * 8) = bits;
+}
+
+// bf16 copy of a stack in its stored layout.  Thread -> 32 consecutive elements of one row
+// (one 16-byte code load: half an NF4 block, one MXFP4 block), decoded with the large tiles'
+// GroupDecoder and written as four 16-byte stores.
+template <int FMT>
+__global__ __launch_bounds__(256) void expand_kernel(QStack q, int64_t nchunks, uint16_t *__restrict__ out) {
+  __shared__ DecodeTables tb;
+  if constexpr (FMT == FMT_NF4_DQ) {
+    init_decode_tables(tb);
+    __syncthreads();
+  }
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= nchunks) return;
+  const int64_t el = i * 32;
+  const u32x4 codes = *(const u32x4 *)(q.codes + el / 2);
+  uint32_t raw;
+  float s2 = 1.0f;
+  if constexpr (FMT == FMT_NF4) {
+    raw = ((const uint32_t *)q.scale)[el >> 6];
+  } else if constexpr (FMT == FMT_NF4_DQ) {
+    raw = ((const uint8_t *)q.scale)[el >> 6];
+    s2 = q.scale2[el >> 14];
+  } else {
+    raw = ((const uint8_t *)q.scale)[el >> 5];
+  }
+  GroupDecoder<FMT> dec;
+  dec.prepare(raw, s2, tb);
+  u32x4 *o = (u32x4 *)(out + el);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) o[p] = dec(codes[p]);
+}
+
+bool launch_expand(const QStack &q, int E, uint16_t *out, hipStream_t s) {
+  const int64_t nchunks = (int64_t)E * q.N * q.K / 32;
+  if (nchunks == 0) return true;
+  LaunchScope ls(FAM_EXPAND, s);
+  const unsigned grid = (unsigned)((nchunks + 255) / 256);
+  switch (q.fmt) {
+    case FMT_NF4: expand_kernel<FMT_NF4><<<grid, 256, 0, s>>>(q, nchunks, out); break;
+    case FMT_NF4_DQ: expand_kernel<FMT_NF4_DQ><<<grid, 256, 0, s>>>(q, nchunks, out); break;
+    default: expand_kernel<FMT_MXFP4><<<grid, 256, 0, s>>>(q, nchunks, out); break;
+  }
+  return last_launch_ok();
 }
 
 bool launch_dequant(const QStack &q, int64_t elem0, int64_t n, float *out_f32, uint16_t *out_bf16,

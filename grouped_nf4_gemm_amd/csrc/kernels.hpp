@@ -24,6 +24,7 @@ enum Family : int {
   FAM_QUANT,
   FAM_DEQUANT,
   FAM_TRANSPOSE,
+  FAM_EXPAND,
   FAM_COUNT
 };
 const char *family_name(int f);
@@ -53,6 +54,11 @@ struct GroupedArgs {
   uint32_t a_bytes;  // extent of A (large-tile buffer loads)
   // B operand
   QStack q;            // 4-bit stack (NK: [N, K] rows; KN: stored [K, N])
+  // bf16 copy of q in its stored layout (nullable): the large tiles then load it directly
+  // instead of decoding; bx_estride elements and bx_bytes bytes per expert
+  const uint16_t *Bx;
+  int64_t bx_estride;
+  uint32_t bx_bytes;
   const uint16_t *Bd;  // dense bf16 [E][N][ldb]
   int64_t b_estride, ldb;
   // LoRA K-extension: xa [M][ldxa] sorted rows, xb [E][N][ldxb]; r = 0 disables
@@ -138,5 +144,8 @@ bool launch_quantize(int fmt, int64_t n, const float *w, uint8_t *codes, void *s
                      hipStream_t s);
 bool launch_dequant(const QStack &q, int64_t elem0, int64_t n, float *out_f32, uint16_t *out_bf16,
                     hipStream_t s);
+// bf16 copy of a whole stack [E][N][K] in its stored layout, decoded exactly as the GEMM
+// tiles decode it.
+bool launch_expand(const QStack &q, int E, uint16_t *out, hipStream_t s);
 
 }  // namespace e4b

@@ -12,7 +12,7 @@ import dataclasses
 import torch
 
 from . import _lib
-from ._lib import FMT, E4B_TRAIN, check
+from ._lib import FMT, E4B_EXPAND, E4B_NO_EXPAND, E4B_TRAIN, check
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -119,14 +119,17 @@ def route(ids: torch.Tensor, E: int):
 
 class MoELayer:
     """One routed-expert layer: frozen stacks w_gu [E, 2I, H], w_dn [E, H, I] plus
-    optional adapters on each.  Owns its workspace (caller-side allocation)."""
+    optional adapters on each.  Owns its workspace (caller-side allocation).
+    expand: None lets the library choose between decoding the stacks inside the GEMM
+    tiles and streaming bf16 copies of them (large batches); True / False force it."""
 
     def __init__(self, w_gu: QStack, w_dn: QStack, l_gu: LoRA | None, l_dn: LoRA | None,
-                 T: int, topk: int, train: bool = True):
+                 T: int, topk: int, train: bool = True, expand: bool | None = None):
         self.w_gu, self.w_dn, self.l_gu, self.l_dn = w_gu, w_dn, l_gu, l_dn
         self.E, self.H, self.I = w_gu.E, w_gu.K, w_dn.K
         self.T, self.topk = T, topk
-        self.flags = E4B_TRAIN if train else 0
+        self.flags = (E4B_TRAIN if train else 0) | (
+            0 if expand is None else E4B_EXPAND if expand else E4B_NO_EXPAND)
         self.desc = _lib.Desc(self.E, self.H, self.I, T, topk, self.flags)
         n = ctypes.c_size_t()
         check(_lib.lib().e4b_moe_workspace_size(ctypes.byref(self.desc), _lora_c(l_gu), _lora_c(l_dn),

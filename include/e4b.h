@@ -79,6 +79,14 @@ typedef struct {
 } e4b_lora;
 
 #define E4B_TRAIN 1u /* forward keeps what dgrad and wgrad read, in the workspace */
+/* The 4-bit GEMMs of a call with more than 256 routed rows either decode the stacks
+ * inside the GEMM tiles, once per 256-row tile, or -- by default when there are at
+ * least 1024 routed rows per expert on average -- first write bf16 copies of both
+ * stacks into the workspace (decoded by the same rules; 2 bytes per weight, kept from a
+ * training forward for its dgrad) and stream those.  Results are bit-identical either
+ * way.  These flags force the choice (not both; ignored at 256 rows or fewer). */
+#define E4B_EXPAND 2u
+#define E4B_NO_EXPAND 4u
 
 typedef struct {
   int32_t E, H, I, T, topk;
@@ -149,6 +157,7 @@ typedef struct {
   int64_t launches_total;
   int64_t route, lora_a, gemm_gate_up, gemm_down, combine;
   int64_t combine_bwd, gemm_down_dgrad, gemm_gate_up_dgrad, unpermute, wgrad, quant, dequant;
+  int64_t expand;    /* bf16 copies of stacks written by large-batch calls */
   int64_t fallbacks; /* always 0: there is no slower path to fall back to */
 } e4b_stats;
 e4b_status e4b_get_stats(e4b_stats *out);

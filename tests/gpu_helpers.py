@@ -49,7 +49,7 @@ def assert_close(gpu, ref, name: str):
 class Case:
     """One layer call: host inputs, oracle-quantised stacks, and device copies."""
 
-    def __init__(self, inp: synth.LayerInputs, lora: bool = True, train: bool = True):
+    def __init__(self, inp: synth.LayerInputs, lora: bool = True, train: bool = True, expand=None):
         s = inp.shape
         self.inp, self.s = inp, s
         self.q1 = oracle.quantize(s.fmt, inp.W1)
@@ -64,7 +64,8 @@ class Case:
         self.dy = b16(inp.dy)
         self.ids = torch.from_numpy(inp.ids).to(dev)
         self.topw = torch.from_numpy(inp.topw).to(dev)
-        self.layer = MoELayer(self.w_gu, self.w_dn, self.l_gu, self.l_dn, s.T, s.k, train=train)
+        self.layer = MoELayer(self.w_gu, self.w_dn, self.l_gu, self.l_dn, s.T, s.k, train=train,
+                              expand=expand)
         self.lora = lora
 
     def oracle_layer(self):

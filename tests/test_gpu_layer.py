@@ -158,3 +158,33 @@ def test_decode_shape_ignores_stale_lds():
     assert torch.isfinite(got.float()).all()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
     _check_all(case_c, {"y": got})
+
+
+EXPAND_SHAPES = [
+    # name, E, H, I, T, k, r, alpha, fmt  (more than 256 routed rows: the large tiles)
+    ("x-ragged", 5, 192, 320, 150, 3, 16, 32.0, "nf4"),
+    ("x-dq", 4, 320, 192, 150, 2, 8, 16.0, "nf4_dq"),
+    ("x-mxfp4", 6, 192, 192, 100, 4, 8, 16.0, "mxfp4"),
+    ("x-multi-tile", 3, 256, 448, 300, 2, 64, 128.0, "nf4"),
+]
+
+
+@pytest.mark.parametrize("shape", EXPAND_SHAPES, ids=[s[0] for s in EXPAND_SHAPES])
+def test_expanded_stacks_bitwise(shape):
+    """Large-batch calls that stream bf16 copies of the stacks give every output and
+    gradient bit for bit equal to the same calls decoding inside the GEMM tiles, and
+    both match the oracle."""
+    name, E, H, I, T, k, r, alpha, fmt = shape
+    print(f"expanded stacks {shape}", flush=True)
+    inp = synth.make_inputs(synth.custom(E, H, I, T, k, r, alpha, fmt, name=name), seed=200 + E + T)
+    reset_stats()
+    a = Case(inp, expand=True).run()
+    assert get_stats()["expand"] == 2
+    reset_stats()
+    b = Case(inp, expand=False).run()
+    assert get_stats()["expand"] == 0
+    for key in a:
+        va = a[key].view(torch.int32) if a[key].dtype == torch.float32 else a[key].view(torch.int16)
+        vb = b[key].view(torch.int32) if b[key].dtype == torch.float32 else b[key].view(torch.int16)
+        assert torch.equal(va, vb), key
+    _check_all(Case(inp, expand=True), a)
