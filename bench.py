@@ -173,12 +173,13 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str, command: str) -
     print("\n".join(lines))
 
 
-# kernel family (as the library's event timing names it) -> kernel symbol fragment
+# kernel family (as the library's event timing names it) -> kernel symbol fragments: the
+# kernel over bf16 copies of the stacks (large batches) and the one that decodes in the tile
 FAMILY_SYMBOL = {
-    "gemm_gate_up": "gemm_large_kernel<0, 2,",
-    "gemm_down": "gemm_large_kernel<0, 0,",
-    "gemm_down_dgrad": "gemm_large_kernel<1, 3,",
-    "gemm_gate_up_dgrad": "gemm_large_kernel<1, 0,",
+    "gemm_gate_up": ("gemm_x_kernel<false, 2,", "gemm_large_kernel<0, 2,"),
+    "gemm_down": ("gemm_x_kernel<false, 0,", "gemm_large_kernel<0, 0,"),
+    "gemm_down_dgrad": ("gemm_x_kernel<true, 3,", "gemm_large_kernel<1, 3,"),
+    "gemm_gate_up_dgrad": ("gemm_x_kernel<true, 0,", "gemm_large_kernel<1, 0,"),
 }
 
 
@@ -193,13 +194,14 @@ def read_traffic(family: str, workload: str):
     sha = next((l.split(":", 1)[1].strip() for l in lines if l.startswith("csrc_sha:")), None)
     if sha != csrc_sha():
         return None
-    for line in lines:
-        parts = line.split()
-        if sym in line and len(parts) >= 4:
-            try:
-                return (float(parts[-2]) + float(parts[-1])) * 1e6
-            except ValueError:
-                continue
+    for frag in sym:
+        for line in lines:
+            parts = line.split()
+            if frag in line and len(parts) >= 4:
+                try:
+                    return (float(parts[-2]) + float(parts[-1])) * 1e6
+                except ValueError:
+                    continue
     return None
 
 

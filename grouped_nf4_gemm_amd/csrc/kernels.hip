@@ -1008,46 +1008,57 @@ __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *_
   if (b16) *(u32x4 *)(b16 + i * 8) = bits;
 }
 
-// bf16 copy of a stack in its stored layout.  Thread -> 32 consecutive elements of one row
-// (one 16-byte code load: half an NF4 block, one MXFP4 block), decoded with the large tiles'
-// GroupDecoder and written as four 16-byte stores.
+// bf16 copy of a stack in its stored layout, decoded with the large tiles' GroupDecoder.
+// A workgroup covers 1024 consecutive 8-code words; load and store p of thread t handle
+// word 256 p + t, so consecutive lanes read consecutive 4-byte code words and write
+// consecutive 16-byte pieces.
 template <int FMT>
-__global__ __launch_bounds__(256) void expand_kernel(QStack q, int64_t nchunks, uint16_t *__restrict__ out) {
+__global__ __launch_bounds__(256) void expand_kernel(QStack q, int64_t nwords, uint16_t *__restrict__ out) {
   __shared__ DecodeTables tb;
   if constexpr (FMT == FMT_NF4_DQ) {
     init_decode_tables(tb);
     __syncthreads();
   }
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nchunks) return;
-  const int64_t el = i * 32;
-  const u32x4 codes = *(const u32x4 *)(q.codes + el / 2);
-  uint32_t raw;
-  float s2 = 1.0f;
-  if constexpr (FMT == FMT_NF4) {
-    raw = ((const uint32_t *)q.scale)[el >> 6];
-  } else if constexpr (FMT == FMT_NF4_DQ) {
-    raw = ((const uint8_t *)q.scale)[el >> 6];
-    s2 = q.scale2[el >> 14];
-  } else {
-    raw = ((const uint8_t *)q.scale)[el >> 5];
-  }
-  GroupDecoder<FMT> dec;
-  dec.prepare(raw, s2, tb);
-  u32x4 *o = (u32x4 *)(out + el);
+  const int64_t w0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  uint32_t code[4], raw[4];
+  float s2[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) o[p] = dec(codes[p]);
+  for (int p = 0; p < 4; ++p) {
+    const int64_t w = w0 + 256 * p;
+    code[p] = 0;
+    raw[p] = 0;
+    s2[p] = 1.0f;
+    if (w < nwords) {
+      code[p] = ((const uint32_t *)q.codes)[w];
+      if constexpr (FMT == FMT_NF4) {
+        raw[p] = ((const uint32_t *)q.scale)[w >> 3];
+      } else if constexpr (FMT == FMT_NF4_DQ) {
+        raw[p] = ((const uint8_t *)q.scale)[w >> 3];
+        s2[p] = q.scale2[w >> 11];
+      } else {
+        raw[p] = ((const uint8_t *)q.scale)[w >> 2];
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t w = w0 + 256 * p;
+    if (w >= nwords) continue;
+    GroupDecoder<FMT> dec;
+    dec.prepare(raw[p], s2[p], tb);
+    *(u32x4 *)(out + w * 8) = dec(code[p]);
+  }
 }
 
 bool launch_expand(const QStack &q, int E, uint16_t *out, hipStream_t s) {
-  const int64_t nchunks = (int64_t)E * q.N * q.K / 32;
-  if (nchunks == 0) return true;
+  const int64_t nwords = (int64_t)E * q.N * q.K / 8;
+  if (nwords == 0) return true;
   LaunchScope ls(FAM_EXPAND, s);
-  const unsigned grid = (unsigned)((nchunks + 255) / 256);
+  const unsigned grid = (unsigned)((nwords + 1023) / 1024);
   switch (q.fmt) {
-    case FMT_NF4: expand_kernel<FMT_NF4><<<grid, 256, 0, s>>>(q, nchunks, out); break;
-    case FMT_NF4_DQ: expand_kernel<FMT_NF4_DQ><<<grid, 256, 0, s>>>(q, nchunks, out); break;
-    default: expand_kernel<FMT_MXFP4><<<grid, 256, 0, s>>>(q, nchunks, out); break;
+    case FMT_NF4: expand_kernel<FMT_NF4><<<grid, 256, 0, s>>>(q, nwords, out); break;
+    case FMT_NF4_DQ: expand_kernel<FMT_NF4_DQ><<<grid, 256, 0, s>>>(q, nwords, out); break;
+    default: expand_kernel<FMT_MXFP4><<<grid, 256, 0, s>>>(q, nwords, out); break;
   }
   return last_launch_ok();
 }

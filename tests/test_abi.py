@@ -62,6 +62,26 @@ def test_workspace_size_valid(L):
     assert st3 == 0
 
 
+def test_expanded_stacks_workspace(L):
+    """Large calls (more than 256 routed rows) reserve the bf16 copies of both stacks:
+    E*2I*H + E*H*I bf16 values, by default from 1024 routed rows per expert on average or
+    when forced; calls of at most 256 rows never do."""
+    E, H, I = 4, 128, 256
+    copies = 2 * (E * 2 * I * H + E * H * I)
+    TRAIN, EXPAND, NO_EXPAND = 1, 2, 4
+    _, big_default = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN))      # 1024 rows/expert
+    _, big_off = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN | NO_EXPAND))
+    assert big_default - big_off >= copies
+    _, mid_default = _ws(L, _desc(L, E=E, H=H, I=I, T=1024, k=2, flags=TRAIN))      # 512 rows/expert
+    _, mid_forced = _ws(L, _desc(L, E=E, H=H, I=I, T=1024, k=2, flags=TRAIN | EXPAND))
+    assert mid_forced - mid_default >= copies
+    _, small_default = _ws(L, _desc(L, E=E, H=H, I=I, T=128, k=2, flags=TRAIN))     # 256 rows
+    _, small_forced = _ws(L, _desc(L, E=E, H=H, I=I, T=128, k=2, flags=TRAIN | EXPAND))
+    assert small_forced == small_default
+    st, _ = _ws(L, _desc(L, flags=TRAIN | EXPAND | NO_EXPAND))
+    assert st == L.E4B_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("kw", [dict(H=100), dict(I=96), dict(E=0), dict(k=9), dict(k=0),
                                 dict(T=-1), dict(E=2000, k=1), dict(flags=8)])
 def test_bad_desc_rejected(L, kw):
