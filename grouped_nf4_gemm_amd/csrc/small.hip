@@ -371,13 +371,26 @@ constexpr int XMAX = 8;
 static_assert(XMAX == 8, "token rows of a direct slot");
 constexpr int XPT = 8;  // staged 16-byte activation pieces per thread: rows x blocks <= 512
 
-template <int FMT, int EPI>
+// The codes of a strip are read CH blocks at a time with each lane loading 16 bytes of one
+// row (2 CH lanes per row, so a load covers whole 32 CH-byte row segments), staged in a
+// per-wave LDS buffer, and read back in the MFMA lane layout: loads in which the 64 lanes
+// touch 32 different rows keep the vector memory unit stalled on its cache.
+template <int CH>
+__device__ __forceinline__ int stage_swz(int rho, int p) {
+  if constexpr (CH == 4) return p ^ ((rho >> 1) & 7);  // 8 pieces per row
+  else return p ^ ((rho >> 2) & 3);                      // 4 pieces per row
+}
+constexpr int stage_bytes(int ch) { return SM_WAVES * 32 * ch * 32; }
+
+template <int FMT, int EPI, int CH>
 __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g, int kb_per_split,
                                                                    int64_t split_stride) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
   constexpr int D = 7, R = 8;
+  static_assert(CH == 2 || CH == 4, "staged chunk");
+  constexpr int LPR = 2 * CH, RPI = 64 / LPR, NI = 32 / RPI, CS = R / CH;  // lanes/row, rows/load, loads, slots
   // static LDS: the code table (NF4 formats), a zero line and the tile scan; dynamic
-  // LDS: the staged activation rows [rows][blocks of the split][64]
+  // LDS: the staged activation rows [rows][blocks of the split][64], then the code stages
   struct Rest {
     uint16_t xzero[64];
     int tile_sh[4];
@@ -425,6 +438,24 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
                                           : (uint32_t)(el >> 5) + 2u * kb0 + hh;
   const uint32_t ssh = sb & 3u, sbase = ok ? (sb & ~3u) : OOB;
   if (!ok) row = -1;
+  // staged code loads: load i of a chunk reads strip row RPI i + lane / LPR, piece lane % LPR
+  uint32_t voffc[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int rho = RPI * i + lane / LPR;
+    const int st = blockIdx.x * SM_WAVES + w;
+    int r;
+    bool rok;
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      const int ii = st * 16 + (rho & 15);
+      rok = ii < g.I;
+      r = rho < 16 ? ii : g.I + ii;
+    } else {
+      r = st * 32 + rho;
+      rok = r < N;
+    }
+    voffc[i] = rok ? (uint32_t)((((int64_t)e * N + r) * K) / 2) + (uint32_t)kb0 * 32 + 16u * (lane % LPR) : OOB;
+  }
 
   {
     const int t0 = 0, xrows = tm.rows;
@@ -451,8 +482,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     // every lane reads, branch-free, and the zero-line reads are one broadcast address
     const uint16_t *xsrc = xlane ? xs + (tok - t0) * xrow_len + 32 * hh : xzero;
     const int xjstride = xlane ? 64 : 0;
+    // this wave's code stage: [32 strip rows][2 CH pieces of 16 bytes], pieces swizzled
+    char *stage = (char *)small_lds + ((xrows * xrow_len * 2 + 15) & ~15) + w * (32 * CH * 32);
 
-    u32x4 cw[R];
+    u32x4 craw[CS][NI];
     ChunkScale sq[R / 4], cur;
     f32x16 acc;
 #pragma unroll
@@ -460,7 +493,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
 
     auto load_blk = [&](int slot, int j) {
       const uint32_t dead = j < nblk ? 0u : OOB;
-      cw[slot] = bload128(rc, cbase, ((uint32_t)j * 32) | dead);
+      if (slot % CH == 0) {  // the codes of blocks j .. j+CH-1, 32 rows
+#pragma unroll
+        for (int i = 0; i < NI; ++i) craw[slot / CH][i] = bload128(rc, voffc[i], ((uint32_t)j * 32) | dead);
+      }
       if (slot % 4 == 0) {  // the scales of blocks j .. j+3
         const uint32_t step = FMT == FMT_NF4 ? 16u : FMT == FMT_NF4_DQ ? 4u : 8u;
         ChunkScale &q = sq[slot / 4];
@@ -490,6 +526,18 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         return e8m0_to_f32(byte_at(q.raw, q.sh + 2 * b));
       }
     };
+    // chunk slot cs -> this wave's stage (after the previous chunk's reads, in LDS order)
+    auto stage_write = [&](int cs) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int rho = RPI * i + lane / LPR;
+        *(u32x4 *)(stage + rho * (CH * 32) + stage_swz<CH>(rho, lane % LPR) * 16) = craw[cs][i];
+      }
+    };
+    // the codes of block b of the staged chunk in the MFMA layout: row n, piece 2 b + h
+    auto stage_read = [&](int b) -> u32x4 {
+      return *(const u32x4 *)(stage + n * (CH * 32) + stage_swz<CH>(n, 2 * b + hh) * 16);
+    };
     // operands of block j in slot d: activation fragments, B fragments, scale
     struct Ops {
       bf16x8 a[4], b[4];
@@ -505,10 +553,12 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       const float sc = d % 4 == 0 ? scale_in(sq[d / 4], 0, j) : scale_in(cur, d % 4, j);
       // a block past the range has zero codes (nf4 code 0 = -1): zero its scale
       o.sc = j < nblk ? sc : 0.0f;
+      const u32x4 cwb = stage_read(d % CH);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        if constexpr (NF4ISH) o.b[s4] = nf4_codes_bf16(cw[d][s4], l4, tb);
-        else o.b[s4] = __builtin_bit_cast(bf16x8, mxfp4_word_to_bf16(cw[d][s4], o.sc));
+        const uint32_t cw4 = cwb[s4];
+        if constexpr (NF4ISH) o.b[s4] = nf4_codes_bf16(cw4, l4, tb);
+        else o.b[s4] = __builtin_bit_cast(bf16x8, mxfp4_word_to_bf16(cw4, o.sc));
       }
     };
     auto compute = [&](const Ops &o) {
@@ -540,6 +590,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     lds_barrier();
 
     Ops ops[2];
+    stage_write(0);
     prepare(0, 0, ops[0]);
     for (int jb = 0; jb < nblk; jb += R) {
 #pragma unroll
@@ -549,6 +600,8 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         if (d % 4 == 0) cur = sq[d / 4];  // before the next step refills the slot holding it
         load_blk((d + D) % R, j + D);
         __builtin_amdgcn_sched_barrier(0);
+        // block j+1 starts a chunk: stage it (block j's reads were issued a step ago)
+        if ((d + 1) % CH == 0) stage_write(((d + 1) % R) / CH);
         prepare((d + 1) % R, j + 1, ops[(d + 1) & 1]);
         compute(ops[d & 1]);
       }
@@ -615,8 +668,13 @@ static void launch_small_fmt(const GroupedArgs &a, int spw, int strips_per_exper
   (void)slots;
   if (use_direct(a, kbs)) {
     const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, XMAX), splits);
-    const size_t xlds = (size_t)direct_rows(a) * kbs * 64 * 2;
-    small_direct_kernel<FMT, EPI><<<grid, SM_THREADS, xlds, s>>>(a, kbs, split_stride);
+    const size_t xlds = ((size_t)direct_rows(a) * kbs * 64 * 2 + 15) & ~(size_t)15;
+    // four-block stages when they fit beside the table and the staged activations
+    constexpr size_t STATIC_LDS = (FMT != FMT_MXFP4 ? sizeof(SmallTables) : 0) + 256;
+    if (STATIC_LDS + xlds + stage_bytes(4) <= 160 * 1024)
+      small_direct_kernel<FMT, EPI, 4><<<grid, SM_THREADS, xlds + stage_bytes(4), s>>>(a, kbs, split_stride);
+    else
+      small_direct_kernel<FMT, EPI, 2><<<grid, SM_THREADS, xlds + stage_bytes(2), s>>>(a, kbs, split_stride);
   } else {
     const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, SM_BMT), splits);
     small_gemm_kernel<FMT, 1, EPI, 3><<<grid, SM_THREADS, 0, s>>>(a, kbs, split_stride);
