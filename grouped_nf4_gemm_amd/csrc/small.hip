@@ -124,13 +124,26 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The codes of a strip are read CH blocks at a time with each lane loading 16 bytes of one
+// row (2 CH lanes per row, so a load covers whole 32 CH-byte row segments), staged in a
+// per-wave LDS buffer, and read back in the MFMA lane layout: loads in which the 64 lanes
+// touch 32 different rows keep the vector memory unit stalled on its cache.
+template <int CH>
+__device__ __forceinline__ int stage_swz(int rho, int p) {
+  if constexpr (CH == 4) return p ^ ((rho >> 1) & 7);  // 8 pieces per row
+  else return p ^ ((rho >> 2) & 3);                      // 4 pieces per row
+}
+constexpr int stage_bytes(int ch) { return SM_WAVES * 32 * ch * 32; }
+
 template <int FMT, int SPW, int EPI, int DC>
 __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, int kb_per_split,
                                                                  int64_t split_stride) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
   constexpr int R = DC + 1;  // chunk slots of the register ring
+  static_assert(SPW == 1 && SM_CB == 4, "one strip per wave, codes staged four blocks at a time");
   struct Rest {
     SmallX xs;
+    u32x4 stage[SM_WAVES][32 * 8];  // per wave: [32 strip rows][8 swizzled 16-byte pieces]
     int tile_sh[4];
   };
   __shared__ __attribute__((aligned(16))) WithTable<NF4ISH, Rest> sm;
@@ -157,7 +170,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
 
   // this lane's weight row in each strip; code and scale offsets at block kb0
   int row[SPW];
-  uint32_t cbase[SPW], sbase[SPW], ssh[SPW];
+  uint32_t sbase[SPW], ssh[SPW];
   int64_t blk0[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
@@ -173,7 +186,6 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     }
     const int64_t el = ((int64_t)e * N + row[s]) * K;
     blk0[s] = (el >> 6) + kb0;
-    cbase[s] = ok ? (uint32_t)(el / 2) + (uint32_t)kb0 * 32 + 16 * hh : OOB;
     // scale windows: NF4 byte 4*blk; NF4_DQ byte blk; MXFP4 byte (el >> 5) + 2 kb + h,
     // each read from the 4-byte aligned address at or below it
     const uint32_t sb = FMT == FMT_NF4 ? (uint32_t)(blk0[s] * 4)
@@ -183,6 +195,25 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     sbase[s] = ok ? (sb & ~3u) : OOB;
     if (!ok) row[s] = -1;
   }
+  // staged code loads (a chunk of 4 blocks): load i reads strip row 8 i + lane / 8, piece lane % 8
+  uint32_t voffc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rho = 8 * i + lane / 8;
+    const int st = blockIdx.x * SM_WAVES + w;
+    int r;
+    bool rok;
+    if constexpr (EPI == EPI_SWIGLU_FWD) {
+      const int ii = st * 16 + (rho & 15);
+      rok = ii < g.I;
+      r = rho < 16 ? ii : g.I + ii;
+    } else {
+      r = st * 32 + rho;
+      rok = r < N;
+    }
+    voffc[i] = rok ? (uint32_t)((((int64_t)e * N + r) * K) / 2) + (uint32_t)kb0 * 32 + 16u * (lane % 8) : OOB;
+  }
+  char *stage = (char *)&sm.rest.stage[w][0];
   // activation staging: thread -> token row t / 16, 16 elements at 16 * (t % 16) of a chunk
   const int xrow = threadIdx.x >> 4, xpiece = threadIdx.x & 15;
   uint32_t xoff = OOB;
@@ -214,11 +245,11 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   auto load_w = [&](int slot, int c) {
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
+      // the chunk's codes, 32 rows x 128 bytes (a chunk past the split reads zero; blocks of a
+      // chunk past kb1 read bytes that their zero scale cancels)
 #pragma unroll
-      for (int b = 0; b < SM_CB; ++b) {
-        const int kb = kb0 + c * SM_CB + b;
-        cw[slot][s][b] = bload128(rc, cbase[s], ((uint32_t)(c * SM_CB + b) * 32) | (kb < kb1 ? 0u : OOB));
-      }
+      for (int i = 0; i < 4; ++i)
+        cw[slot][s][i] = bload128(rc, voffc[i], ((uint32_t)(c * SM_CB) * 32) | (c < nchunks ? 0u : OOB));
       const uint32_t dead = c < nchunks ? 0u : OOB;
       const uint32_t step = FMT == FMT_NF4 ? SM_CB * 4 : FMT == FMT_NF4_DQ ? SM_CB : SM_CB * 2;
       uint32_t win = OOB, sh = 0;
@@ -273,8 +304,15 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
       load_w((d + DC) % R, c + DC);
       __builtin_amdgcn_sched_barrier(0);
       const uint16_t *xb = &xs.v[c & 1][n][32 * hh];
+      // this chunk's codes to the wave's stage (the previous chunk's reads came first)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rho = 8 * i + lane / 8;
+        *(u32x4 *)(stage + rho * 128 + stage_swz<4>(rho, lane % 8) * 16) = cw[d][0][i];
+      }
 #pragma unroll
       for (int b = 0; b < SM_CB; ++b) {
+        const u32x4 cwb = *(const u32x4 *)(stage + n * 128 + stage_swz<4>(n, 2 * b + hh) * 16);
         bf16x8 af[4];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) af[s4] = *(const bf16x8 *)(xb + 64 * b + 8 * s4);
@@ -287,9 +325,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
           if constexpr (NF4ISH) {
             f32x16 blk = {};
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-              blk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s4], nf4_codes_bf16(cw[d][s][b][s4], l4, tb), blk,
-                                                            0, 0, 0);
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const uint32_t cw4 = cwb[s4];
+              blk = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s4], nf4_codes_bf16(cw4, l4, tb), blk, 0, 0, 0);
+            }
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[s][v] += sc * blk[v];
             // keeps the scaling of this block's partial sum here: sunk to the end of the
@@ -298,9 +337,11 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
             asm volatile("" : "+v"(acc[s]));
           } else {
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
+            for (int s4 = 0; s4 < 4; ++s4) {
+              const uint32_t cw4 = cwb[s4];
               acc[s] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  af[s4], __builtin_bit_cast(bf16x8, mxfp4_word_to_bf16(cw[d][s][b][s4], sc)), acc[s], 0, 0, 0);
+                  af[s4], __builtin_bit_cast(bf16x8, mxfp4_word_to_bf16(cw4, sc)), acc[s], 0, 0, 0);
+            }
           }
         }
       }
@@ -370,17 +411,6 @@ constexpr int XMAX = 8;
 // (the block scaling touches accumulator values v < 4 only: C rows 8(v/4) + 4h + v%4 < 8)
 static_assert(XMAX == 8, "token rows of a direct slot");
 constexpr int XPT = 8;  // staged 16-byte activation pieces per thread: rows x blocks <= 512
-
-// The codes of a strip are read CH blocks at a time with each lane loading 16 bytes of one
-// row (2 CH lanes per row, so a load covers whole 32 CH-byte row segments), staged in a
-// per-wave LDS buffer, and read back in the MFMA lane layout: loads in which the 64 lanes
-// touch 32 different rows keep the vector memory unit stalled on its cache.
-template <int CH>
-__device__ __forceinline__ int stage_swz(int rho, int p) {
-  if constexpr (CH == 4) return p ^ ((rho >> 1) & 7);  // 8 pieces per row
-  else return p ^ ((rho >> 2) & 3);                      // 4 pieces per row
-}
-constexpr int stage_bytes(int ch) { return SM_WAVES * 32 * ch * 32; }
 
 template <int FMT, int EPI, int CH>
 __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g, int kb_per_split,
