@@ -516,7 +516,11 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     char *stage = (char *)small_lds + ((xrows * xrow_len * 2 + 15) & ~15) + w * (32 * CH * 32);
 
     u32x4 craw[CS][NI];
-    ChunkScale sq[R / 4], cur;
+    // scale windows, and the four block scales of the window in use, taken out of it as
+    // it comes into use: the windows are then never copied (a copy of a window whose load
+    // is in flight waits for every load issued before it)
+    ChunkScale sq[R / 4];
+    float scur[4];
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -579,8 +583,11 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       const uint16_t *xb = j < nblk ? xsrc + xjstride * j : xzero;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xb + 8 * s4);
-      // the quad of block j: in the slot's own window if j starts it, else in `cur`
-      const float sc = d % 4 == 0 ? scale_in(sq[d / 4], 0, j) : scale_in(cur, d % 4, j);
+      if (d % 4 == 0) {  // block j starts a window: take out its four scales
+#pragma unroll
+        for (int b = 0; b < 4; ++b) scur[b] = scale_in(sq[d / 4], b, j + b);
+      }
+      const float sc = scur[d % 4];
       // a block past the range has zero codes (nf4 code 0 = -1): zero its scale
       o.sc = j < nblk ? sc : 0.0f;
       const u32x4 cwb = stage_read(d % CH);
@@ -627,7 +634,6 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       for (int d = 0; d < R; ++d) {
         const int j = jb + d;  // block j sits in slot d; its operands are in ops[d & 1]
         __builtin_amdgcn_sched_barrier(0);
-        if (d % 4 == 0) cur = sq[d / 4];  // before the next step refills the slot holding it
         load_blk((d + D) % R, j + D);
         __builtin_amdgcn_sched_barrier(0);
         // block j+1 starts a chunk: stage it (block j's reads were issued a step ago)
