@@ -27,6 +27,8 @@
 
 namespace e4b {
 
+constexpr int SM_WAVES = 8, SM_THREADS = 64 * SM_WAVES;
+
 // 64 copies of the bf16 code-pair table, copy c for lane c: entry b of copy c at byte
 // offset b * 256 + c * 4, so one byte permute forms the address and no two lanes of a
 // wave share a bank.  Entry b holds bf16(nf4[b >> 4]) in its low half (element 2j, the
@@ -35,14 +37,16 @@ struct SmallTables {
   uint32_t cp[256][64];
 };
 
-// 16-byte piece i of the table (entry i / 16, copies 4 (i % 16) .. +3): consecutive lanes
-// write consecutive pieces, so the stores are free of bank conflicts.
+// Thread t of the 512 computes entry t / 2 once and writes 8 of its 16 pieces (16 bytes
+// each, copies 4p .. 4p+3).  In the k-th store lane t writes piece (k + t / 2 + 8 (t & 1))
+// mod 16: the 16 lanes of one store pass write 16 different pieces, so their banks differ.
 __device__ __forceinline__ void init_small_tables(SmallTables &t) {
-  for (int i = threadIdx.x; i < 256 * 16; i += blockDim.x) {
-    const uint32_t b = (uint32_t)i >> 4;
-    const uint32_t v = pack_bf16x2(nf4_value(b >> 4), nf4_value(b & 15));
-    *(u32x4 *)&t.cp[b][4 * (i & 15)] = u32x4{v, v, v, v};
-  }
+  static_assert(SM_THREADS == 512, "two threads per table entry");
+  const uint32_t b = threadIdx.x >> 1;
+  const uint32_t v = pack_bf16x2(nf4_value(b >> 4), nf4_value(b & 15));
+  const uint32_t p0 = b + 8 * (threadIdx.x & 1);
+#pragma unroll
+  for (uint32_t k = 0; k < 8; ++k) *(u32x4 *)&t.cp[b][4 * ((p0 + k) & 15)] = u32x4{v, v, v, v};
 }
 
 // bf16 code values of the four code bytes of word w for this lane (l4 = lane * 4).
@@ -75,7 +79,6 @@ __device__ __forceinline__ SmallTables &table_of(WithTable<TABLE, Rest> &s) {
   else return *reinterpret_cast<SmallTables *>(&s);  // not read: the formats without a table
 }
 
-constexpr int SM_WAVES = 8, SM_THREADS = 64 * SM_WAVES;
 constexpr int SM_BMT = 32;                  // tokens per workgroup slot
 constexpr int SM_CB = 4;                    // 64-wide blocks per chunk
 constexpr int SM_XSTRIDE = SM_CB * 64 + 8;  // staged activation row: 256 bf16 + 16 bytes
@@ -512,6 +515,15 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     // every lane reads, branch-free, and the zero-line reads are one broadcast address
     const uint16_t *xsrc = xlane ? xs + (tok - t0) * xrow_len + 32 * hh : xzero;
     const int xjstride = xlane ? 64 : 0;
+    // the LoRA operands of the first 16 adapter columns, loaded now so that their latency
+    // is not paid after the loop
+    const bool lora = g.r > 0 && blockIdx.z == 0;
+    u32x4 za0 = {0, 0, 0, 0}, zb0 = {0, 0, 0, 0};
+    if (lora) {
+      const int kc = 8 * hh;
+      if (xlane && kc < g.r) za0 = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
+      if (row >= 0 && kc < g.r) zb0 = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + kc);
+    }
     // this wave's code stage: [32 strip rows][2 CH pieces of 16 bytes], pieces swizzled
     char *stage = (char *)small_lds + ((xrows * xrow_len * 2 + 15) & ~15) + w * (32 * CH * 32);
 
@@ -577,7 +589,8 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       bf16x8 a[4], b[4];
       float sc;
     };
-    auto prepare = [&](int d, int j, Ops &o) {
+    // cwb: the block's codes, read from the stage a step earlier than the rest
+    auto prepare = [&](int d, int j, Ops &o, const u32x4 &cwb) {
       // blocks past the range (the ring runs up to R - 1 blocks beyond it) read the zero
       // line: the staged rows end at the range, and LDS past them is not initialised
       const uint16_t *xb = j < nblk ? xsrc + xjstride * j : xzero;
@@ -590,7 +603,6 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       const float sc = scur[d % 4];
       // a block past the range has zero codes (nf4 code 0 = -1): zero its scale
       o.sc = j < nblk ? sc : 0.0f;
-      const u32x4 cwb = stage_read(d % CH);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const uint32_t cw4 = cwb[s4];
@@ -628,7 +640,8 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
 
     Ops ops[2];
     stage_write(0);
-    prepare(0, 0, ops[0]);
+    prepare(0, 0, ops[0], stage_read(0));
+    u32x4 ccur = stage_read(1);  // block 1 (chunk 0 holds at least two blocks)
     for (int jb = 0; jb < nblk; jb += R) {
 #pragma unroll
       for (int d = 0; d < R; ++d) {
@@ -636,19 +649,25 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         __builtin_amdgcn_sched_barrier(0);
         load_blk((d + D) % R, j + D);
         __builtin_amdgcn_sched_barrier(0);
-        // block j+1 starts a chunk: stage it (block j's reads were issued a step ago)
-        if ((d + 1) % CH == 0) stage_write(((d + 1) % R) / CH);
-        prepare((d + 1) % R, j + 1, ops[(d + 1) & 1]);
+        // block j+2 starts a chunk: stage it (block j+1's codes were read a step ago), then
+        // read block j+2's codes, a step before their table reads
+        if ((d + 2) % CH == 0) stage_write(((d + 2) % R) / CH);
+        const u32x4 cn = stage_read((d + 2) % CH);
+        prepare((d + 1) % R, j + 1, ops[(d + 1) & 1], ccur);
         compute(ops[d & 1]);
+        ccur = cn;
       }
     }
 
-    if (g.r > 0 && blockIdx.z == 0) {
+    if (lora) {
       for (int kk = 0; kk < g.r; kk += 16) {
         const int kc = kk + 8 * hh;
-        u32x4 za = {0, 0, 0, 0}, zb = {0, 0, 0, 0};
-        if (xlane && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
-        if (row >= 0 && kc < g.r) zb = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + kc);
+        u32x4 za = za0, zb = zb0;
+        if (kk > 0) {
+          za = zb = u32x4{0, 0, 0, 0};
+          if (xlane && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
+          if (row >= 0 && kc < g.r) zb = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + kc);
+        }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, za), __builtin_bit_cast(bf16x8, zb),
                                                       acc, 0, 0, 0);
       }
