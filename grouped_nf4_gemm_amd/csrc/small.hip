@@ -415,9 +415,9 @@ constexpr int XMAX = 8;
 static_assert(XMAX == 8, "token rows of a direct slot");
 constexpr int XPT = 8;  // staged 16-byte activation pieces per thread: rows x blocks <= 512
 
-template <int FMT, int EPI, int CH>
+template <int FMT, int EPI, int CH, bool SEQ>
 __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g, int kb_per_split,
-                                                                   int64_t split_stride) {
+                                                                   int64_t split_stride, int nseq) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
   constexpr int D = 7, R = 8;
   static_assert(CH == 2 || CH == 4, "staged chunk");
@@ -450,10 +450,18 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
   const __amdgpu_buffer_rsrc_t rs2 = make_rsrc(g.q.scale2, g.q.scale2_bytes);
   const uint32_t slast = g.q.scale_bytes >= 16 ? (g.q.scale_bytes - 16) & ~3u : 0u;
 
-  int row;
-  bool ok;
-  {
-    const int st = blockIdx.x * SM_WAVES + w;
+  // Each wave computes a sequence of nseq strips of 32 weight rows, strip k being
+  // (blockIdx.x nseq + k) SM_WAVES + w: the table, the staged activations and the start-up
+  // latency are paid once per workgroup.  Strip state: the output row of this lane, the
+  // scale windows and the staged code load offsets.
+  int row = -1;
+  int64_t blk0 = 0;
+  uint32_t ssh = 0, sbase = OOB;
+  uint32_t voffc[NI];
+  auto strip_of = [&](int k) { return (blockIdx.x * nseq + k) * SM_WAVES + w; };
+  auto strip_valid = [&](int st) { return EPI == EPI_SWIGLU_FWD ? st * 16 < g.I : st * 32 < N; };
+  auto setup_strip = [&](int st) {
+    bool ok;
     if constexpr (EPI == EPI_SWIGLU_FWD) {
       const int i = st * 16 + (n & 15);
       ok = i < g.I;
@@ -462,33 +470,32 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       row = st * 32 + n;
       ok = row < N;
     }
-  }
-  const int64_t el = ((int64_t)e * N + row) * K;
-  const int64_t blk0 = (el >> 6) + kb0;
-  const uint32_t cbase = ok ? (uint32_t)(el / 2) + (uint32_t)kb0 * 32 + 16 * hh : OOB;
-  const uint32_t sb = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4)
-                      : FMT == FMT_NF4_DQ ? (uint32_t)blk0
-                                          : (uint32_t)(el >> 5) + 2u * kb0 + hh;
-  const uint32_t ssh = sb & 3u, sbase = ok ? (sb & ~3u) : OOB;
-  if (!ok) row = -1;
-  // staged code loads: load i of a chunk reads strip row RPI i + lane / LPR, piece lane % LPR
-  uint32_t voffc[NI];
+    const int64_t el = ((int64_t)e * N + row) * K;
+    blk0 = (el >> 6) + kb0;
+    const uint32_t sb = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4)
+                        : FMT == FMT_NF4_DQ ? (uint32_t)blk0
+                                            : (uint32_t)(el >> 5) + 2u * kb0 + hh;
+    ssh = sb & 3u;
+    sbase = ok ? (sb & ~3u) : OOB;
+    if (!ok) row = -1;
+    // staged code loads: load i of a chunk reads strip row RPI i + lane / LPR, piece lane % LPR
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int rho = RPI * i + lane / LPR;
-    const int st = blockIdx.x * SM_WAVES + w;
-    int r;
-    bool rok;
-    if constexpr (EPI == EPI_SWIGLU_FWD) {
-      const int ii = st * 16 + (rho & 15);
-      rok = ii < g.I;
-      r = rho < 16 ? ii : g.I + ii;
-    } else {
-      r = st * 32 + rho;
-      rok = r < N;
+    for (int i = 0; i < NI; ++i) {
+      const int rho = RPI * i + lane / LPR;
+      int r;
+      bool rok;
+      if constexpr (EPI == EPI_SWIGLU_FWD) {
+        const int ii = st * 16 + (rho & 15);
+        rok = ii < g.I;
+        r = rho < 16 ? ii : g.I + ii;
+      } else {
+        r = st * 32 + rho;
+        rok = r < N;
+      }
+      voffc[i] = rok ? (uint32_t)((((int64_t)e * N + r) * K) / 2) + (uint32_t)kb0 * 32 + 16u * (lane % LPR) : OOB;
     }
-    voffc[i] = rok ? (uint32_t)((((int64_t)e * N + r) * K) / 2) + (uint32_t)kb0 * 32 + 16u * (lane % LPR) : OOB;
-  }
+  };
+  setup_strip(strip_of(0));
 
   {
     const int t0 = 0, xrows = tm.rows;
@@ -519,11 +526,12 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     // is not paid after the loop
     const bool lora = g.r > 0 && blockIdx.z == 0;
     u32x4 za0 = {0, 0, 0, 0}, zb0 = {0, 0, 0, 0};
-    if (lora) {
-      const int kc = 8 * hh;
-      if (xlane && kc < g.r) za0 = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
-      if (row >= 0 && kc < g.r) zb0 = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + kc);
-    }
+    auto load_zb0 = [&]() {
+      zb0 = u32x4{0, 0, 0, 0};
+      if (lora && row >= 0 && 8 * hh < g.r) zb0 = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + 8 * hh);
+    };
+    if (lora && xlane && 8 * hh < g.r) za0 = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + 8 * hh);
+    load_zb0();
     // this wave's code stage: [32 strip rows][2 CH pieces of 16 bytes], pieces swizzled
     char *stage = (char *)small_lds + ((xrows * xrow_len * 2 + 15) & ~15) + w * (32 * CH * 32);
 
@@ -638,7 +646,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     }
     lds_barrier();
 
+    for (int k = 0;;) {
     Ops ops[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
     stage_write(0);
     prepare(0, 0, ops[0], stage_read(0));
     u32x4 ccur = stage_read(1);  // block 1 (chunk 0 holds at least two blocks)
@@ -659,14 +670,17 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       }
     }
 
+    const int row_done = row, st_done = strip_of(k);
+    const u32x4 zb_done = zb0;
+
     if (lora) {
       for (int kk = 0; kk < g.r; kk += 16) {
         const int kc = kk + 8 * hh;
-        u32x4 za = za0, zb = zb0;
+        u32x4 za = za0, zb = zb_done;
         if (kk > 0) {
           za = zb = u32x4{0, 0, 0, 0};
           if (xlane && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
-          if (row >= 0 && kc < g.r) zb = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + kc);
+          if (row_done >= 0 && kc < g.r) zb = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row_done * g.ldxb + kc);
         }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, za), __builtin_bit_cast(bf16x8, zb),
                                                       acc, 0, 0, 0);
@@ -674,7 +688,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     }
     // accumulator rows are the slot's tokens: write those of this pass
     if constexpr (EPI == EPI_SWIGLU_FWD) {
-      const int i = (blockIdx.x * SM_WAVES + w) * 16 + (n & 15);
+      const int i = st_done * 16 + (n & 15);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float mine = acc[v];
@@ -691,15 +705,40 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
           }
         }
       }
-    } else if (row >= 0) {
+    } else if (row_done >= 0) {
       float *out = (float *)g.C + blockIdx.z * split_stride;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (t >= t0 && t < t0 + xrows) out[(tm.row0 + t) * g.ldc + row] = acc[v];
+        if (t >= t0 && t < t0 + xrows) out[(tm.row0 + t) * g.ldc + row_done] = acc[v];
       }
     }
+    // the next strip: its first loads
+    ++k;
+    if (!SEQ || k >= nseq || !strip_valid(strip_of(k))) break;
+    setup_strip(strip_of(k));
+    load_zb0();
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_blk(d, d);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    }  // strips
   }
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 // Strips (32 weight rows) per wave.  One: a second strip would double the register ring
@@ -722,14 +761,24 @@ static void launch_small_fmt(const GroupedArgs &a, int spw, int strips_per_exper
   (void)spw;
   (void)slots;
   if (use_direct(a, kbs)) {
-    const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, XMAX), splits);
+    // strips per wave: the fewest with which the workgroups of the touched experts (at most
+    // min(E, M)) fit on the compute units at once
+    const int cus = device_cus();
+    int nseq = 1;
+    while (nseq < 16 && (int64_t)cdiv(strips_per_expert, SM_WAVES * nseq) * min(a.E, a.M) * splits > cus) ++nseq;
+    const dim3 grid(cdiv(strips_per_expert, SM_WAVES * nseq), small_slots(a.M, a.E, XMAX), splits);
     const size_t xlds = ((size_t)direct_rows(a) * kbs * 64 * 2 + 15) & ~(size_t)15;
     // four-block stages when they fit beside the table and the staged activations
     constexpr size_t STATIC_LDS = (FMT != FMT_MXFP4 ? sizeof(SmallTables) : 0) + 256;
-    if (STATIC_LDS + xlds + stage_bytes(4) <= 160 * 1024)
-      small_direct_kernel<FMT, EPI, 4><<<grid, SM_THREADS, xlds + stage_bytes(4), s>>>(a, kbs, split_stride);
-    else
-      small_direct_kernel<FMT, EPI, 2><<<grid, SM_THREADS, xlds + stage_bytes(2), s>>>(a, kbs, split_stride);
+    const bool four = STATIC_LDS + xlds + stage_bytes(4) <= 160 * 1024;
+    const size_t lds = xlds + stage_bytes(four ? 4 : 2);
+    if (nseq > 1) {
+      if (four) small_direct_kernel<FMT, EPI, 4, true><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, nseq);
+      else small_direct_kernel<FMT, EPI, 2, true><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, nseq);
+    } else {
+      if (four) small_direct_kernel<FMT, EPI, 4, false><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, 1);
+      else small_direct_kernel<FMT, EPI, 2, false><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, 1);
+    }
   } else {
     const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, SM_BMT), splits);
     small_gemm_kernel<FMT, 1, EPI, 3><<<grid, SM_THREADS, 0, s>>>(a, kbs, split_stride);
