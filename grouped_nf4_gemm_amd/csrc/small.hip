@@ -422,21 +422,15 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
   constexpr int D = 7, R = 8;
   static_assert(CH == 2 || CH == 4, "staged chunk");
   constexpr int LPR = 2 * CH, RPI = 64 / LPR, NI = 32 / RPI, CS = R / CH;  // lanes/row, rows/load, loads, slots
-  // static LDS: the code table (NF4 formats), a zero line and the tile scan; dynamic
-  // LDS: the staged activation rows [rows][blocks of the split][64], then the code stages
-  struct Rest {
-    uint16_t xzero[64];
-    int tile_sh[4];
-  };
-  __shared__ __attribute__((aligned(16))) WithTable<NF4ISH, Rest> sm;
+  // static LDS: only the code table (NF4 formats), at LDS address 0; dynamic LDS: the
+  // staged activation rows [rows][blocks of the split][64], then the code stages.  With 8
+  // staged rows of 4096 and four-block stages this is the whole 160 KB.
+  __shared__ __attribute__((aligned(16))) SmallTables direct_tb;
   extern __shared__ __attribute__((aligned(16))) uint32_t small_lds[];
-  SmallTables &tb = table_of(sm);
+  SmallTables &tb = direct_tb;  // read by the NF4 formats only
   uint16_t *xs = (uint16_t *)small_lds;
-  uint16_t *xzero = sm.rest.xzero;
-  int *tile_sh = sm.rest.tile_sh;
-  if (threadIdx.x < 8) *(u32x4 *)&xzero[threadIdx.x * 8] = u32x4{0, 0, 0, 0};
   TileM tm;
-  if (!find_tile(g.off, g.E, XMAX, blockIdx.y, tm, tile_sh)) return;  // (synchronises)
+  if (!find_tile_wave(g.off, g.E, XMAX, blockIdx.y, tm)) return;  // the same for every wave
   const int e = tm.e;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -518,10 +512,9 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     }
     const int tok = n;
     const bool xlane = tok >= t0 && tok < t0 + xrows;
-    // fragment source of this lane: its token row, or the zero line (block stride 0):
-    // every lane reads, branch-free, and the zero-line reads are one broadcast address
-    const uint16_t *xsrc = xlane ? xs + (tok - t0) * xrow_len + 32 * hh : xzero;
-    const int xjstride = xlane ? 64 : 0;
+    // fragment source of this lane: its token row; a lane without a token reads token 0's
+    // row (its accumulator row is never stored, and rows do not mix in the product)
+    const uint16_t *xsrc = xs + (xlane ? tok - t0 : 0) * xrow_len + 32 * hh;
     // the LoRA operands of the first 16 adapter columns, loaded now so that their latency
     // is not paid after the loop
     const bool lora = g.r > 0 && blockIdx.z == 0;
@@ -599,9 +592,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     };
     // cwb: the block's codes, read from the stage a step earlier than the rest
     auto prepare = [&](int d, int j, Ops &o, const u32x4 &cwb) {
-      // blocks past the range (the ring runs up to R - 1 blocks beyond it) read the zero
-      // line: the staged rows end at the range, and LDS past them is not initialised
-      const uint16_t *xb = j < nblk ? xsrc + xjstride * j : xzero;
+      // blocks past the range (the ring runs up to R - 1 blocks beyond it) read the last
+      // staged block (LDS past the staged rows is not initialised and could hold NaN,
+      // which their zero scale would not cancel)
+      const uint16_t *xb = xsrc + 64 * max(0, min(j, nblk - 1));
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xb + 8 * s4);
       if (d % 4 == 0) {  // block j starts a window: take out its four scales
@@ -769,7 +763,7 @@ static void launch_small_fmt(const GroupedArgs &a, int spw, int strips_per_exper
     const dim3 grid(cdiv(strips_per_expert, SM_WAVES * nseq), small_slots(a.M, a.E, XMAX), splits);
     const size_t xlds = ((size_t)direct_rows(a) * kbs * 64 * 2 + 15) & ~(size_t)15;
     // four-block stages when they fit beside the table and the staged activations
-    constexpr size_t STATIC_LDS = (FMT != FMT_MXFP4 ? sizeof(SmallTables) : 0) + 256;
+    constexpr size_t STATIC_LDS = FMT != FMT_MXFP4 ? sizeof(SmallTables) : 0;
     const bool four = STATIC_LDS + xlds + stage_bytes(4) <= 160 * 1024;
     const size_t lds = xlds + stage_bytes(four ? 4 : 2);
     if (nseq > 1) {

@@ -138,6 +138,23 @@ def test_zero_tokens():
         assert torch.count_nonzero(out[k]) == 0
 
 
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+def test_decode_strip_sequence(fmt):
+    """Few tokens spread over many experts with wide gate_up stacks: one workgroup per
+    eight strips of every touched expert would not fit on the device at once (16 experts x
+    17 workgroups), so each wave of the weight-streaming kernel runs a sequence of strips."""
+    s = synth.custom(16, 128, 2112, 8, 2, 16, 32.0, fmt, name=f"decode-seq-{fmt}")
+    inp = synth.make_inputs(s, seed=57)
+    inp.ids[:, 0] = np.arange(8)
+    inp.ids[:, 1] = np.arange(8, 16)
+    case = Case(inp, train=False)
+    print(f"strip sequence {fmt}", flush=True)
+    reset_stats()
+    out = case.run(dgrad=False)
+    assert get_stats()["fallbacks"] == 0
+    _check_all(case, out)
+
+
 def test_decode_shape_ignores_stale_lds():
     """Few tokens per expert (the weight-streaming path): blocks past the K range must
     not read LDS that this call did not write.  A call whose staged activations are all
