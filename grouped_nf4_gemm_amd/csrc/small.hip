@@ -514,7 +514,14 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     const bool xlane = tok >= t0 && tok < t0 + xrows;
     // fragment source of this lane: its token row; a lane without a token reads token 0's
     // row (its accumulator row is never stored, and rows do not mix in the product)
-    const uint16_t *xsrc = xs + (xlane ? tok - t0 : 0) * xrow_len + 32 * hh;
+    // Staged rows are 128 n bytes apart, so all start in the same LDS bank: the 16-byte
+    // piece c of a block of row t sits at piece c ^ (t & 7), and the fragment reads of up
+    // to 8 token rows fall in different banks.
+    const int xrow = xlane ? tok - t0 : 0;
+    const uint16_t *xsrc = xs + xrow * xrow_len;
+    int xpc[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) xpc[s4] = ((4 * hh + s4) ^ (xrow & 7)) * 8;
     // the LoRA operands of the first 16 adapter columns, loaded now so that their latency
     // is not paid after the loop
     const bool lora = g.r > 0 && blockIdx.z == 0;
@@ -597,7 +604,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       // which their zero scale would not cancel)
       const uint16_t *xb = xsrc + 64 * max(0, min(j, nblk - 1));
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xb + 8 * s4);
+      for (int s4 = 0; s4 < 4; ++s4) o.a[s4] = *(const bf16x8 *)(xb + xpc[s4]);
       if (d % 4 == 0) {  // block j starts a window: take out its four scales
 #pragma unroll
         for (int b = 0; b < 4; ++b) scur[b] = scale_in(sq[d / 4], b, j + b);
@@ -636,7 +643,10 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int i = threadIdx.x + u * SM_THREADS;
-      if (i < npieces) *(u32x4 *)(xs + i * 8) = xp[u];  // piece i = row i / (8 nblk), same order
+      if (i < npieces) {  // piece i: row i / (8 nblk), block q / 8, piece q % 8 (swizzled)
+        const int xr = i / (nblk * 8), q = i - xr * (nblk * 8);
+        *(u32x4 *)(xs + xr * xrow_len + (q & ~7) * 8 + ((q & 7) ^ (xr & 7)) * 8) = xp[u];
+      }
     }
     lds_barrier();
 
