@@ -730,12 +730,28 @@ __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t 
   const int h = blockIdx.y * 1024 + threadIdx.x * 4;
   if (h >= H) return;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  // the rows and weights of up to 8 choices first, then per choice the loads of all its
+  // split partial sums at once (added in split order), so that the latencies overlap
+  constexpr int KP = 8;
+  int pj[KP];
+  float wj[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    pj[j] = j < k ? inv[(int64_t)t * k + j] : -1;
+    wj[j] = j < k ? topw[(int64_t)t * k + j] : 0.f;
+  }
   for (int j = 0; j < k; ++j) {
-    const int p = inv[(int64_t)t * k + j];
+    const int p = j < KP ? pj[j] : inv[(int64_t)t * k + j];
     if (p < 0) continue;
-    const float w = topw[(int64_t)t * k + j];
-    f32x4 o = *(const f32x4 *)(O + (int64_t)p * H + h);
-    for (int c = 1; c < nsplit; ++c) o += *(const f32x4 *)(O + c * split_stride + (int64_t)p * H + h);
+    const float w = j < KP ? wj[j] : topw[(int64_t)t * k + j];
+    f32x4 ov[COMBINE_MAX_SPLITS];
+#pragma unroll
+    for (int c = 0; c < COMBINE_MAX_SPLITS; ++c)
+      if (c < nsplit) ov[c] = *(const f32x4 *)(O + c * split_stride + (int64_t)p * H + h);
+    f32x4 o = ov[0];
+#pragma unroll
+    for (int c = 1; c < COMBINE_MAX_SPLITS; ++c)
+      if (c < nsplit) o += ov[c];
     a0 += w * o[0];
     a1 += w * o[1];
     a2 += w * o[2];
@@ -748,6 +764,7 @@ __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t 
 bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int32_t *inv, const float *topw,
                     int T, int k, int H, uint16_t *y, hipStream_t s) {
   if (T == 0) return true;
+  if (nsplit < 1 || nsplit > COMBINE_MAX_SPLITS) return false;
   LaunchScope ls(FAM_COMBINE, s);
   combine_kernel<<<dim3(T, cdiv(H, 1024)), 256, 0, s>>>(O, nsplit, split_stride, inv, topw, k, H, y);
   return last_launch_ok();

@@ -122,8 +122,8 @@ bool launch_wgrad(const WgradArgs &a, hipStream_t s);
 int lora_a_splits(int M, int E, int N, int K);
 int wgrad_splits(int M, int E, int Na, int Nb);
 
-// y[t] = bf16(sum_j w[t,j] * O[inv[t,j]]); O holds `nsplit` partial sums, split_stride
-// floats apart, that are added in split order first.
+// y[t] = bf16(sum_j w[t,j] * O[inv[t,j]]); O holds `nsplit` (at most COMBINE_MAX_SPLITS)
+// partial sums, split_stride floats apart, that are added in split order first.
 bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int32_t *inv, const float *topw,
                     int T, int k, int H, uint16_t *y, hipStream_t s);
 
@@ -131,6 +131,7 @@ bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int3
 // rows of a call are at most SMALL_M_MAX.
 constexpr int SMALL_M_MAX = 256;
 constexpr int SMALL_MAX_SPLITS = 8;
+constexpr int COMBINE_MAX_SPLITS = SMALL_MAX_SPLITS;
 bool launch_small_lora_a(const GroupedArgs &a, hipStream_t s);
 bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s);
 int small_down_splits(int M, int E, int N, int K);

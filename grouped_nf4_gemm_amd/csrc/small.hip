@@ -837,8 +837,10 @@ bool launch_small_down(const GroupedArgs &a, int splits, hipStream_t s) {
 __global__ __launch_bounds__(256) void small_lora_a_kernel(GroupedArgs g) {
   const int p = blockIdx.x, j0 = blockIdx.y * 4, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   __shared__ float red[4][4];
-  if (p >= g.off[g.E]) return;  // past the valid rows (uniform over the workgroup)
-  int e = 0;
+  // the row's source index is loaded alongside the expert lookup (the two are independent),
+  // so the operand loads wait for one round of memory latency, not two
+  const int32_t gsrc = g.a_gather ? g.a_gather[p] : 0;
+  int e = -1;
   for (int c = 0; c < g.E; c += 64) {
     const int ee = c + lane;
     const bool hit = ee < g.E && g.off[ee] <= p && p < g.off[ee + 1];
@@ -848,16 +850,18 @@ __global__ __launch_bounds__(256) void small_lora_a_kernel(GroupedArgs g) {
       break;
     }
   }
-  const int64_t src = g.a_gather ? (int64_t)(g.a_gather[p] / g.a_gdiv) : p;
+  if (e < 0) return;  // past the valid rows (uniform over the workgroup)
+  const int64_t src = g.a_gather ? (int64_t)(gsrc / g.a_gdiv) : p;
   const uint16_t *xr = g.A + src * g.lda;
   const uint16_t *br[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) br[jj] = g.Bd + e * g.b_estride + (int64_t)min(j0 + jj, g.N - 1) * g.ldb;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = tid * 8; k0 < g.K; k0 += 4 * 2048) {
-    u32x4 xv[4], bv[4][4];
+  // one round of loads covers K up to 16384 (the same k order per thread for any K)
+  for (int k0 = tid * 8; k0 < g.K; k0 += 8 * 2048) {
+    u32x4 xv[8], bv[8][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       const int k = k0 + u * 2048;
       const bool ok = k < g.K;
       xv[u] = ok ? *(const u32x4 *)(xr + k) : u32x4{0, 0, 0, 0};
@@ -865,7 +869,7 @@ __global__ __launch_bounds__(256) void small_lora_a_kernel(GroupedArgs g) {
       for (int jj = 0; jj < 4; ++jj) bv[u][jj] = ok ? *(const u32x4 *)(br[jj] + k) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
