@@ -322,6 +322,39 @@ __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint16_t v, u
 __device__ __forceinline__ void bstore32(__amdgpu_buffer_rsrc_t r, float v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, 0, 0);
 }
+// Two bf16 outputs per 4-byte store.  In the MFMA accumulator layout a lane holds one
+// column; lanes 2m and 2m+1 hold columns c and c+1 of the same rows.  x0 and x1 are this
+// lane's values of rows r and r+1: one lane swap (DPP quad_perm [1,0,3,2]) gives the even
+// lane row r at columns (c, c+1) and the odd lane row r+1 at columns (c-1, c).
+__device__ __forceinline__ uint32_t pair_bf16(float x0, float x1, bool odd) {
+  const float send = odd ? x0 : x1;
+  const float recv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, false));
+  return pack_bf16x2(odd ? recv : x0, odd ? x1 : recv);
+}
+__device__ __forceinline__ void bstore32u(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ uint32_t lane_swap1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+}
+// The same pairing for fp32 outputs: two columns per 8-byte store.
+__device__ __forceinline__ void bstore_pair_f32(__amdgpu_buffer_rsrc_t r, float x0, float x1, bool odd,
+                                                uint32_t voff) {
+  const float send = odd ? x0 : x1;
+  const float recv = __uint_as_float(lane_swap1(__float_as_uint(send)));
+  typedef int i32x2 __attribute__((ext_vector_type(2)));
+  const i32x2 d = {(int)__float_as_uint(odd ? recv : x0), (int)__float_as_uint(odd ? x1 : recv)};
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)voff, 0, 0);
+}
+// The inverse for loads: the even lane loaded row r and the odd lane row r+1, each as the
+// dword of columns (c, c+1) of its pair; returns this lane's column at rows r (lo) and r+1
+// (hi), as bf16 bits.
+__device__ __forceinline__ void unpair_bf16(uint32_t d, bool odd, uint32_t &r0, uint32_t &r1) {
+  const uint32_t recv = lane_swap1(odd ? (d & 0xffffu) : (d >> 16));
+  r0 = odd ? recv : (d & 0xffffu);
+  r1 = odd ? (d >> 16) : recv;
+}
+
 // Buffer over rows row0 .. row0 + rows - 1 of a row-major matrix with ld elements of esize
 // bytes per row: per-lane offsets past the last row read zero / are not written.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *base, int64_t row0, int rows, int64_t ld,

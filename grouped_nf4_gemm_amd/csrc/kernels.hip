@@ -469,78 +469,98 @@ __device__ __forceinline__ void large_finish(LMma &mma, const GroupedArgs &g, co
   const int rl = LMma::wm() * 128 + (lane >> 5) * 4;  // the lane's first tile row
   if constexpr (EPI == EPI_SWIGLU_FWD) {
     // tile rows interleave 32 gate and 32 up weight rows: the wave's pair (0, 1) holds gate
-    // and up of h columns n0 + wn*32 + lane%32
+    // and up of h columns n0 + wn*32 + lane%32.  Accumulator elements v and v+1 (v even) are
+    // rows r and r+1: lane pairs store two columns per 4-byte store (pair_bf16), the even
+    // lane row r and the odd lane row r+1.
     const int col = n0 + LMma::wn() * 32 + (lane & 31);
+    const bool odd = lane & 1;
+    const int pc = col & ~1, pr = rl + (odd ? 1 : 0);
     const __amdgpu_buffer_rsrc_t rh = rows_rsrc(g.C, tm.row0, tm.rows, g.ldc, 2);
-    const uint32_t hoff = col < g.I ? (uint32_t)((rl * g.ldc + col) * 2) : OOB;
+    const uint32_t hoff = col < g.I ? (uint32_t)((pr * g.ldc + pc) * 2) : OOB;
     const uint32_t hpitch = (uint32_t)(g.ldc * 2);
     if (g.Gout) {
       const __amdgpu_buffer_rsrc_t rg = rows_rsrc(g.Gout, tm.row0, tm.rows, g.ldg, 2);
-      const uint32_t goff = col < g.I ? (uint32_t)((rl * g.ldg + col) * 2) : OOB;
+      const uint32_t goff = col < g.I ? (uint32_t)((pr * g.ldg + pc) * 2) : OOB;
       const uint32_t gpitch = (uint32_t)(g.ldg * 2), uoff = (uint32_t)(g.I * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
-          const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
-          const float act = gt * sigmoid_fast(gt);
-          bstore16(rh, f2bf(act * up), hoff + dr * hpitch);
-          bstore16(rg, f2bf(gt), goff + dr * gpitch);
-          bstore16(rg, f2bf(up), goff + dr * gpitch + uoff);
+          const float gt0 = mma.acc[i][0][v], up0 = mma.acc[i][1][v];
+          const float gt1 = mma.acc[i][0][v + 1], up1 = mma.acc[i][1][v + 1];
+          const float h0 = gt0 * sigmoid_fast(gt0) * up0, h1 = gt1 * sigmoid_fast(gt1) * up1;
+          bstore32u(rh, pair_bf16(h0, h1, odd), hoff + dr * hpitch);
+          bstore32u(rg, pair_bf16(gt0, gt1, odd), goff + dr * gpitch);
+          bstore32u(rg, pair_bf16(up0, up1, odd), goff + dr * gpitch + uoff);
         }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
-          const float gt = mma.acc[i][0][v], up = mma.acc[i][1][v];
-          const float act = gt * sigmoid_fast(gt);
-          bstore16(rh, f2bf(act * up), hoff + dr * hpitch);
+          const float gt0 = mma.acc[i][0][v], up0 = mma.acc[i][1][v];
+          const float gt1 = mma.acc[i][0][v + 1], up1 = mma.acc[i][1][v + 1];
+          const float h0 = gt0 * sigmoid_fast(gt0) * up0, h1 = gt1 * sigmoid_fast(gt1) * up1;
+          bstore32u(rh, pair_bf16(h0, h1, odd), hoff + dr * hpitch);
         }
     }
   } else if constexpr (EPI == EPI_F32) {
+    // lane pairs store two columns per 8-byte store (bstore_pair_f32), as above
+    const bool odd = lane & 1;
     const __amdgpu_buffer_rsrc_t rc = rows_rsrc(g.C, tm.row0, tm.rows, g.ldc, 4);
     const uint32_t pitch = (uint32_t)(g.ldc * 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + LMma::col_of(j);
-      const uint32_t off = n < g.N ? (uint32_t)((rl * g.ldc + n) * 4) : OOB;
+      const uint32_t off = n < g.N ? (uint32_t)(((rl + (odd ? 1 : 0)) * g.ldc + (n & ~1)) * 4) : OOB;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
-          bstore32(rc, g.alpha * mma.acc[i][j][v], off + dr * pitch);
+          bstore_pair_f32(rc, g.alpha * mma.acc[i][j][v], g.alpha * mma.acc[i][j][v + 1], odd, off + dr * pitch);
         }
     }
   } else {  // EPI_SWIGLU_BWD: acc = dh; dG from the saved pre-activation G
-    // G and dG are separate buffers.  The 32 G values of a 16-row group are loaded before
-    // any of them is used, so their latencies overlap; rows past the tile read zero.
+    // G and dG are separate buffers.  The G values of a 16-row group are loaded before any
+    // of them is used, so their latencies overlap; rows past the tile read zero.  Loads
+    // and stores go two columns per dword through lane pairs (unpair_bf16, pair_bf16): the
+    // even lane handles rows r and the odd lane rows r+1 of accumulator pairs (v, v+1).
+    const bool odd = lane & 1;
     const __amdgpu_buffer_rsrc_t ri = rows_rsrc(g.Gin, tm.row0, tm.rows, g.ldg, 2);
     const __amdgpu_buffer_rsrc_t ro = rows_rsrc(g.Gout, tm.row0, tm.rows, g.ldg, 2);
     const uint32_t pitch = (uint32_t)(g.ldg * 2), uoff = (uint32_t)(g.I * 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + LMma::col_of(j);
-      const uint32_t off = n < g.N ? (uint32_t)((rl * g.ldg + n) * 2) : OOB;
+      const uint32_t off = n < g.N ? (uint32_t)(((rl + (odd ? 1 : 0)) * g.ldg + (n & ~1)) * 2) : OOB;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t gv[16], uv[16];
+        uint32_t gd[8], ud[8];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const uint32_t o = off + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * pitch;
-          gv[v] = bload16(ri, o);
-          uv[v] = bload16(ri, o + uoff);
+          gd[v / 2] = bload32(ri, o, 0);
+          ud[v / 2] = bload32(ri, o + uoff, 0);
         }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
+        for (int v = 0; v < 16; v += 2) {
           const uint32_t o = off + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * pitch;
-          const float dh = mma.acc[i][j][v], gt = bf2f((uint16_t)gv[v]), up = bf2f((uint16_t)uv[v]);
-          const float sg = sigmoid_fast(gt);
-          bstore16(ro, f2bf(dh * up * sg * (1.0f + gt * (1.0f - sg))), o);
-          bstore16(ro, f2bf(dh * gt * sg), o + uoff);
+          uint32_t g0, g1, u0, u1;
+          unpair_bf16(gd[v / 2], odd, g0, g1);
+          unpair_bf16(ud[v / 2], odd, u0, u1);
+          float dg[2], du[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const float dh = mma.acc[i][j][v + q], gt = bf2f((uint16_t)(q ? g1 : g0)), up = bf2f((uint16_t)(q ? u1 : u0));
+            const float sg = sigmoid_fast(gt);
+            dg[q] = dh * up * sg * (1.0f + gt * (1.0f - sg));
+            du[q] = dh * gt * sg;
+          }
+          bstore32u(ro, pair_bf16(dg[0], dg[1], odd), o);
+          bstore32u(ro, pair_bf16(du[0], du[1], odd), o + uoff);
         }
       }
     }
