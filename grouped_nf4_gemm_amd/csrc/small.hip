@@ -810,12 +810,18 @@ bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s) {
   return last_launch_ok();
 }
 
-// K splits of down: enough waves for the device, each split a whole number of chunks.
+// K splits of down: enough waves for the device, each split a whole number of chunks.  With
+// few tokens per expert, also enough splits for the staged activation rows of a split to
+// fit the direct variant.
 int small_down_splits(int M, int E, int N, int K) {
   const int64_t strips = (int64_t)cdiv(N, 32) * min(E, M);
   const int64_t waves = strips / pick_spw(strips);
   int splits = (int)((2048 + waves - 1) / waves);
   const int chunks = cdiv(K / 64, SM_CB);
+  if (M <= 2 * min(E, M)) {
+    const int max_kbs = (XPT * SM_THREADS) / (8 * min(XMAX, M));  // staged pieces per thread
+    splits = max(splits, cdiv(K / 64, max_kbs / SM_CB * SM_CB));
+  }
   splits = max(1, min(splits, min(SMALL_MAX_SPLITS, chunks / 4)));
   return splits;
 }
