@@ -81,14 +81,15 @@ __device__ __forceinline__ SmallTables &table_of(WithTable<TABLE, Rest> &s) {
 
 constexpr int SM_BMT = 32;                  // tokens per workgroup slot
 constexpr int SM_CB = 4;                    // 64-wide blocks per chunk
-constexpr int SM_XSTRIDE = SM_CB * 64 + 8;  // staged activation row: 256 bf16 + 16 bytes
 
-// Activations of one chunk for the slot's tokens, double-buffered: row t = token t of the
-// slot (zero past its rows).  The 16-byte row padding spreads the 32 fragment reads of a
-// k column over all banks.
+// Activations of one chunk for the slot's tokens in a ring of four buffers: row t = token t
+// of the slot (zero past its rows), 32 pieces of 16 bytes (4 blocks of 8).  Rows are 512
+// bytes apart, all starting in one bank: piece p of row t sits at p ^ (t & 15), so the
+// fragment reads of 16 rows (one 16-lane pass) fall in 16 different groups of 4 banks.
 struct SmallX {
-  uint16_t v[2][SM_BMT][SM_XSTRIDE];
+  uint16_t v[4][SM_BMT][SM_CB * 64];
 };
+__device__ __forceinline__ int xpiece_swz(int t, int p) { return p ^ (t & 15); }
 
 // Byte o / the dword at byte offset o (a multiple of 4) of a 16-byte window.  Byte permutes
 // with per-lane selectors pick within each half and a select picks the half, so the window
@@ -144,18 +145,18 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
   constexpr int R = DC + 1;  // chunk slots of the register ring
   static_assert(SPW == 1 && SM_CB == 4, "one strip per wave, codes staged four blocks at a time");
+  // LDS: the table (64 KB), the activation ring (64 KB) and the code stages (32 KB), the
+  // whole 160 KB: the tile lookup runs in each wave
   struct Rest {
     SmallX xs;
     u32x4 stage[SM_WAVES][32 * 8];  // per wave: [32 strip rows][8 swizzled 16-byte pieces]
-    int tile_sh[4];
   };
   __shared__ __attribute__((aligned(16))) WithTable<NF4ISH, Rest> sm;
   SmallTables &tb = table_of(sm);
   SmallX &xs = sm.rest.xs;
-  int *tile_sh = sm.rest.tile_sh;
   if constexpr (NF4ISH) init_small_tables(tb);
   TileM tm;
-  if (!find_tile(g.off, g.E, SM_BMT, blockIdx.y, tm, tile_sh)) return;  // (synchronises)
+  if (!find_tile_wave(g.off, g.E, SM_BMT, blockIdx.y, tm)) return;  // the same for every wave
   const int e = tm.e;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -241,9 +242,9 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     xr[slot][1] = bload128(ra, xoff, ((uint32_t)c * SM_CB * 128 + 16) | dead);
   };
   auto store_x = [&](int slot, int c) {
-    uint16_t *dst = &xs.v[c & 1][xrow][16 * xpiece];
-    *(u32x4 *)dst = xr[slot][0];
-    *(u32x4 *)(dst + 8) = xr[slot][1];
+    uint16_t *row = &xs.v[c & 3][xrow][0];
+    *(u32x4 *)(row + 8 * xpiece_swz(xrow, 2 * xpiece)) = xr[slot][0];
+    *(u32x4 *)(row + 8 * xpiece_swz(xrow, 2 * xpiece + 1)) = xr[slot][1];
   };
   auto load_w = [&](int slot, int c) {
 #pragma unroll
@@ -294,19 +295,21 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   }
   __builtin_amdgcn_sched_barrier(0);
   store_x(0, 0);
+  store_x(1, 1);
   lds_barrier();
 
+  static_assert(R % 2 == 0, "a barrier after every odd chunk");
   for (int cb = 0; cb < nchunks; cb += R) {
 #pragma unroll
     for (int d = 0; d < R; ++d) {
-      const int c = cb + d;  // chunk c sits in slot d; its activations in xs.v[c & 1]
+      const int c = cb + d;  // chunk c sits in slot d; its activations in xs.v[c & 3]
       // loads of chunk c+DC (activations, then weights) into the slot the previous step
-      // freed; the activations of chunk c+1, loaded DC-1 steps ago, are staged at the end
+      // freed; the activations of chunk c+2, loaded a step ago, are staged at the end
       __builtin_amdgcn_sched_barrier(0);
       load_x((d + DC) % R, c + DC);
       load_w((d + DC) % R, c + DC);
       __builtin_amdgcn_sched_barrier(0);
-      const uint16_t *xb = &xs.v[c & 1][n][32 * hh];
+      const uint16_t *xb = &xs.v[c & 3][n][0];
       // this chunk's codes to the wave's stage (the previous chunk's reads came first)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
         const u32x4 cwb = *(const u32x4 *)(stage + n * 128 + stage_swz<4>(n, 2 * b + hh) * 16);
         bf16x8 af[4];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) af[s4] = *(const bf16x8 *)(xb + 64 * b + 8 * s4);
+        for (int s4 = 0; s4 < 4; ++s4) af[s4] = *(const bf16x8 *)(xb + 8 * xpiece_swz(n, 8 * b + 4 * hh + s4));
         // a block past kb1 reads zero codes, which are nf4 code 0 (-1), against staged
         // activations that are not zero: its scale is set to zero instead
         const bool live = kb0 + c * SM_CB + b < kb1;
@@ -348,8 +351,11 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
           }
         }
       }
-      store_x((d + 1) % R, c + 1);
-      lds_barrier();
+      // The activations of chunk c+2 (loaded a step ago) go to buffer (c+2) & 3, last read
+      // at chunk c-2; a barrier after every odd chunk separates each buffer's writes from
+      // its earlier reads and from its later reads.
+      store_x((d + 2) % R, c + 2);
+      if (d & 1) lds_barrier();
     }
   }
 
