@@ -149,6 +149,27 @@ def route(ids: np.ndarray, E: int):
     return cnt, off, perm, inv
 
 
+def router_topk(logits: np.ndarray, k: int):
+    """Top-k ids (larger logit first, ties to the lower id) and the softmax over them."""
+    logits = np.ascontiguousarray(logits, np.float32)
+    T, E = logits.shape
+    ids = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float32)
+    lib().orc_router_topk(T, E, k, _p(logits), _p(ids), _p(w))
+    return ids, w
+
+
+def router_bwd(w: np.ndarray, dw: np.ndarray, ids: np.ndarray, E: int) -> np.ndarray:
+    """d logits [T, E] from d w [T, k] through the softmax over the chosen experts."""
+    w = np.ascontiguousarray(w, np.float32)
+    dw = np.ascontiguousarray(dw, np.float32)
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, k = w.shape
+    out = np.zeros((T, E), np.float32)
+    lib().orc_router_bwd(T, E, k, _p(w), _p(dw), _p(ids), _p(out))
+    return out
+
+
 class Layer:
     """Arguments of one layer call, kept alive for the C side."""
 

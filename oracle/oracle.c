@@ -237,6 +237,45 @@ typedef struct {
   const uint16_t *A1, *B1, *A2, *B2;
 } expert_view;
 
+/* Router (the frozen router of the method page, "Which project solves it": top-k expert
+ * ids and their weights are inputs to the layer; this is that step on its own).  For token
+ * t: the k largest logits, larger first, equal logits in ascending expert id; then the
+ * softmax over the k chosen, max-subtracted, in double precision, stored as float. */
+void orc_router_topk(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *ids, float *w) {
+  for (int32_t t = 0; t < T; ++t) {
+    const float *l = logits + (int64_t)t * E;
+    int32_t *id = ids + (int64_t)t * k;
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        int taken = 0;
+        for (int32_t q = 0; q < j; ++q) taken |= id[q] == e;
+        if (taken) continue;
+        if (best < 0 || l[e] > l[best]) best = e;
+      }
+      id[j] = best;
+    }
+    const double m = (double)l[id[0]];
+    double den = 0.0;
+    for (int32_t j = 0; j < k; ++j) den += exp((double)l[id[j]] - m);
+    for (int32_t j = 0; j < k; ++j) w[(int64_t)t * k + j] = (float)(exp((double)l[id[j]] - m) / den);
+  }
+}
+
+/* Gradient of the router weights with respect to the logits, the chosen experts held fixed:
+ * d_logit[ids[j]] = w_j (dw_j - sum_i w_i dw_i) (softmax Jacobian), zero for the others. */
+void orc_router_bwd(int32_t T, int32_t E, int32_t k, const float *w, const float *dw, const int32_t *ids,
+                    float *dlogits) {
+  for (int32_t t = 0; t < T; ++t) {
+    const float *wt = w + (int64_t)t * k, *gt = dw + (int64_t)t * k;
+    float *d = dlogits + (int64_t)t * E;
+    for (int32_t e = 0; e < E; ++e) d[e] = 0.0f;
+    double dot = 0.0;
+    for (int32_t j = 0; j < k; ++j) dot += (double)wt[j] * (double)gt[j];
+    for (int32_t j = 0; j < k; ++j) d[ids[(int64_t)t * k + j]] = (float)((double)wt[j] * ((double)gt[j] - dot));
+  }
+}
+
 static double silu(double g) { return g / (1.0 + exp(-g)); }
 static double sigm(double g) { return 1.0 / (1.0 + exp(-g)); }
 

@@ -65,6 +65,11 @@ void orc_dequant(int32_t fmt, int64_t n, const uint8_t *codes, const void *scale
 
 void orc_route(int32_t T, int32_t k, int32_t E, const int32_t *ids,
                int32_t *cnt, int32_t *off, int32_t *perm, int32_t *inv);
+/* Router: top-k ids (larger logit first, ties to the lower id) and the softmax over them;
+   its gradient with respect to the logits, the chosen ids held fixed. */
+void orc_router_topk(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *ids, float *w);
+void orc_router_bwd(int32_t T, int32_t E, int32_t k, const float *w, const float *dw, const int32_t *ids,
+                    float *dlogits);
 
 /* Forward.  tok_mask[T] (NULL = all tokens) selects the tokens whose rows are
  * computed.  y: fp64 [T, H] (unselected tokens get 0).  O (nullable): fp64

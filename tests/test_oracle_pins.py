@@ -442,3 +442,70 @@ def test_backward_mask_equals_zeroed_dy(orc):
     for k in ["dA1", "dB1", "dA2", "dB2"]:
         assert np.allclose(a[k], b[k], rtol=1e-12, atol=1e-300)
     assert np.array_equal(a["dx"][toks], b["dx"][toks])
+
+
+# ---------------------------------------------------------------- router (top-k + softmax)
+
+def _router_logits(T, E, seed, levels=None):
+    rng = np.random.default_rng(seed)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    if levels:  # few distinct values: many ties
+        l = np.round(l * levels) / levels
+    return l.astype(np.float32)
+
+
+@pytest.mark.parametrize("levels", [None, 2])
+def test_router_ids_are_a_stable_descending_sort(orc, levels):
+    """The chosen ids equal numpy's stable sort of the negated logits (ties: lower id first)."""
+    for E, k in [(13, 1), (13, 4), (13, 13), (64, 8)]:
+        l = _router_logits(40, E, 3 + E + k, levels)
+        ids, _ = orc.router_topk(l, k)
+        ref = np.argsort(-l, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref), (E, k)
+
+
+def test_router_weights_closed_form(orc):
+    """Weights are exp(l - max) / sum over the chosen logits (float64 closed form)."""
+    l = _router_logits(50, 32, 11)
+    ids, w = orc.router_topk(l, 6)
+    sel = np.take_along_axis(l.astype(np.float64), ids.astype(np.int64), axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    ref = ex / ex.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(w - ref)) < 1e-7
+    assert np.max(np.abs(w.sum(axis=1) - 1.0)) < 1e-6
+    assert np.all(np.diff(w, axis=1) <= 0)  # larger logit first
+
+
+def test_router_k1_weight_is_one_and_matches_argmax(orc):
+    l = _router_logits(30, 9, 5)
+    ids, w = orc.router_topk(l, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(l, axis=1))
+    assert np.all(w == 1.0)
+
+
+def test_router_bwd_finite_differences(orc):
+    """d logits from d w equals central finite differences (float64) of <dw, w(logits)> with
+    the chosen ids held fixed; ids outside the top-k get zero."""
+    T, E, k = 6, 10, 3
+    l = _router_logits(T, E, 21).astype(np.float64)
+    ids, w = orc.router_topk(l.astype(np.float32), k)
+    dw = np.random.default_rng(4).standard_normal((T, k)).astype(np.float32)
+    got = orc.router_bwd(w, dw, ids, E)
+
+    def f(lt):
+        sel = np.take_along_axis(lt, ids.astype(np.int64), axis=1)
+        ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+        return np.sum(dw * ex / ex.sum(axis=1, keepdims=True))
+
+    eps = 1e-6
+    num = np.zeros_like(l)
+    for t in range(T):
+        for e in range(E):
+            lp, lm = l.copy(), l.copy()
+            lp[t, e] += eps
+            lm[t, e] -= eps
+            num[t, e] = (f(lp) - f(lm)) / (2 * eps)
+    assert np.max(np.abs(got - num)) < 1e-5
+    mask = np.ones((T, E), bool)
+    np.put_along_axis(mask, ids.astype(np.int64), False, axis=1)
+    assert np.all(got[mask] == 0)
