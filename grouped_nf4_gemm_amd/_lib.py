@@ -21,6 +21,7 @@ EXPORTS = [
     "e4b_version", "e4b_status_str", "e4b_moe_workspace_size", "e4b_moe_fwd", "e4b_moe_dgrad",
     "e4b_lora_wgrad", "e4b_moe_route", "e4b_dequant", "e4b_quantize", "e4b_moe_check",
     "e4b_get_stats", "e4b_reset_stats", "e4b_timing_enable", "e4b_timing_read",
+    "e4b_router_topk", "e4b_router_bwd",
 ]
 
 
@@ -79,6 +80,10 @@ def lib() -> ctypes.CDLL:
         L.e4b_lora_wgrad.argtypes = [P(Desc), P(Lora), P(Lora), vp, vp, sz, vp, vp, vp, vp, vp]
         L.e4b_moe_route.restype = i32
         L.e4b_moe_route.argtypes = [P(Desc), vp, vp, vp, vp, vp, vp]
+        L.e4b_router_topk.restype = i32
+        L.e4b_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+        L.e4b_router_bwd.restype = i32
+        L.e4b_router_bwd.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         L.e4b_dequant.restype = i32
         L.e4b_dequant.argtypes = [P(QWeight), i32, vp, vp, vp]
         L.e4b_quantize.restype = i32

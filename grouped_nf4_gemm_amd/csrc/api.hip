@@ -479,6 +479,26 @@ e4b_status e4b_moe_route(const e4b_moe_desc *desc, const int32_t *ids, int32_t *
   return E4B_OK;
 }
 
+e4b_status e4b_router_topk(const float *logits, int32_t T, int32_t E, int32_t topk, int32_t *ids, float *topw,
+                           void *stream) {
+  if (T < 0 || E < 1 || E > E4B_ROUTER_MAX_E || topk < 1 || topk > E || topk > E4B_ROUTER_MAX_K)
+    return E4B_ERR_INVALID_ARG;
+  if (T == 0) return E4B_OK;
+  if (!logits || !ids || !topw) return E4B_ERR_INVALID_ARG;
+  E4B_LAUNCH(launch_router_topk(logits, T, E, topk, ids, topw, (hipStream_t)stream));
+  return E4B_OK;
+}
+
+e4b_status e4b_router_bwd(const float *topw, const float *d_topw, const int32_t *ids, int32_t T, int32_t E,
+                          int32_t topk, float *d_logits, void *stream) {
+  if (T < 0 || E < 1 || E > E4B_ROUTER_MAX_E || topk < 1 || topk > E || topk > E4B_ROUTER_MAX_K)
+    return E4B_ERR_INVALID_ARG;
+  if (T == 0) return E4B_OK;
+  if (!topw || !d_topw || !ids || !d_logits) return E4B_ERR_INVALID_ARG;
+  E4B_LAUNCH(launch_router_bwd(topw, d_topw, ids, T, E, topk, d_logits, (hipStream_t)stream));
+  return E4B_OK;
+}
+
 e4b_status e4b_dequant(const e4b_qweight *w, int32_t expert, float *out_f32, uint16_t *out_bf16,
                        void *stream) {
   if (!w || w->E < 1 || w->N < 1 || w->K < 64 || w->K % 64) return E4B_ERR_INVALID_ARG;

@@ -781,6 +781,101 @@ __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t 
   *(u32x2 *)(y + (int64_t)t * H + h) = out;
 }
 
+// ================================================================ router
+// One wave per token.  Lane l holds logits l, l + 64, ... (at most 16 each).  Each of the k
+// rounds takes the wave's largest remaining logit, equal logits in ascending expert id (a
+// local pass, then a butterfly over the lanes), and lane j keeps round j.  The softmax over
+// the chosen logits is fp32 and max-subtracted; its sum adds the lanes in a fixed tree.
+__device__ __forceinline__ float wave_sum_fixed(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_down(v, d);
+  return __shfl(v, 0);  // lane 0's sum, the same tree for every call
+}
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                          int32_t *__restrict__ ids, float *__restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float *l = logits + (int64_t)t * E;
+  float v[16];
+  uint32_t taken = 0;  // bit q: logit lane + 64 q is chosen or past E
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = lane + 64 * q;
+    v[q] = e < E ? l[e] : 0.0f;
+    if (e >= E) taken |= 1u << q;
+  }
+  float myv = 0.0f, m = 0.0f;
+  int myid = -1;
+  for (int j = 0; j < k; ++j) {
+    float bv = 0.0f;
+    int bi = -1;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = lane + 64 * q;
+      if (!((taken >> q) & 1u) && (bi < 0 || v[q] > bv)) bv = v[q], bi = e;  // ascending e: ties keep the lower
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const float ov = __shfl_xor(bv, d);
+      const int oi = __shfl_xor(bi, d);
+      if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) bv = ov, bi = oi;
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == j) myv = bv, myid = bi;
+    if (j == 0) m = bv;
+  }
+  const float ex = lane < k ? expf(myv - m) : 0.0f;
+  const float den = wave_sum_fixed(ex);
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = myid;
+    w[(int64_t)t * k + lane] = ex / den;
+  }
+}
+
+bool launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t s) {
+  if (T == 0) return true;
+  router_topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(logits, T, E, k, ids, w);
+  return hipGetLastError() == hipSuccess;
+}
+
+// d_logit[ids[t, j]] = w_j (dw_j - sum_i w_i dw_i), zero elsewhere: one wave per token.
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict__ w, const float *__restrict__ dw,
+                                                         const int32_t *__restrict__ ids, int T, int E, int k,
+                                                         float *__restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float wj = lane < k ? w[(int64_t)t * k + lane] : 0.0f;
+  const float gj = lane < k ? dw[(int64_t)t * k + lane] : 0.0f;
+  const int idj = lane < k ? ids[(int64_t)t * k + lane] : -1;
+  const float dot = wave_sum_fixed(wj * gj);
+  const float dj = wj * (gj - dot);
+  float out[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) out[q] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int id = __shfl(idj, j);
+    const float d = __shfl(dj, j);
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      if (id == lane + 64 * q) out[q] = d;
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E) dl[(int64_t)t * E + e] = out[q];
+  }
+}
+
+bool launch_router_bwd(const float *w, const float *dw, const int32_t *ids, int T, int E, int k, float *dl,
+                       hipStream_t s) {
+  if (T == 0) return true;
+  router_bwd_kernel<<<cdiv(T, 4), 256, 0, s>>>(w, dw, ids, T, E, k, dl);
+  return hipGetLastError() == hipSuccess;
+}
+
 bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int32_t *inv, const float *topw,
                     int T, int k, int H, uint16_t *y, hipStream_t s) {
   if (T == 0) return true;

@@ -136,6 +136,11 @@ bool launch_small_lora_a(const GroupedArgs &a, hipStream_t s);
 bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s);
 int small_down_splits(int M, int E, int N, int K);
 bool launch_small_down(const GroupedArgs &a, int splits, hipStream_t s);
+// Router: top-k ids (larger logit first, ties to the lower id) and the fp32 softmax over
+// them, E <= 1024, k <= 64; its gradient to the logits with the ids held fixed.
+bool launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t s);
+bool launch_router_bwd(const float *w, const float *dw, const int32_t *ids, int T, int E, int k, float *dl,
+                       hipStream_t s);
 bool launch_combine_bwd(const uint16_t *dy, const float *O, const int32_t *inv, const float *topw,
                         int T, int k, int H, uint16_t *dO, float *d_topw, hipStream_t s);
 bool launch_unpermute(const float *dXp, const int32_t *inv, int T, int k, int H, uint16_t *dx,

@@ -117,6 +117,26 @@ def route(ids: torch.Tensor, E: int):
     return cnt, off, perm[:M], inv[:M]
 
 
+def router_topk(logits: torch.Tensor, k: int):
+    """Top-k expert ids [T, k] (larger logit first, ties to the lower id) and the softmax
+    weights over them [T, k], from fp32 logits [T, E]."""
+    logits = logits.contiguous()
+    T, E = logits.shape
+    ids = torch.empty(max(T, 1), k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(max(T, 1), k, dtype=torch.float32, device=logits.device)
+    check(_lib.lib().e4b_router_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream()), "e4b_router_topk")
+    return ids[:T], w[:T]
+
+
+def router_bwd(topw: torch.Tensor, d_topw: torch.Tensor, ids: torch.Tensor, E: int) -> torch.Tensor:
+    """d logits [T, E] from d topw [T, k], the chosen ids held fixed."""
+    T, k = topw.shape
+    out = torch.empty(max(T, 1), E, dtype=torch.float32, device=topw.device)
+    check(_lib.lib().e4b_router_bwd(_ptr(topw.contiguous()), _ptr(d_topw.contiguous()), _ptr(ids.contiguous()), T, E,
+                                    k, _ptr(out), _stream()), "e4b_router_bwd")
+    return out[:T]
+
+
 class MoELayer:
     """One routed-expert layer: frozen stacks w_gu [E, 2I, H], w_dn [E, H, I] plus
     optional adapters on each.  Owns its workspace (caller-side allocation).

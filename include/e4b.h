@@ -137,6 +137,26 @@ e4b_status e4b_lora_wgrad(const e4b_moe_desc *desc, const e4b_lora *l_gu, const 
 e4b_status e4b_moe_route(const e4b_moe_desc *desc, const int32_t *ids, int32_t *cnt,
                          int32_t *off, int32_t *perm, int32_t *inv, void *stream);
 
+/* Router (method page, "Which project solves it": the router is frozen and outside the
+ * layer, whose inputs are the top-k ids and weights; this is that step on the device).
+ *  logits fp32 [T, E] row-major (device); ids int32 [T, topk] and topw fp32 [T, topk]
+ *  (device, written): per token the topk largest logits, larger first, equal logits in
+ *  ascending expert id, and the softmax over them (fp32, max-subtracted).  Logits must be
+ *  finite.  E <= E4B_ROUTER_MAX_E, 1 <= topk <= min(E, E4B_ROUTER_MAX_K); otherwise
+ *  E4B_ERR_INVALID_ARG before any launch.  T = 0 launches nothing. */
+#define E4B_ROUTER_MAX_E 1024
+#define E4B_ROUTER_MAX_K 64
+e4b_status e4b_router_topk(const float *logits, int32_t T, int32_t E, int32_t topk, int32_t *ids, float *topw,
+                           void *stream);
+
+/* Gradient of the router weights with respect to the logits, the chosen ids held fixed:
+ * d_logits[t, ids[t, j]] = topw[t, j] (d_topw[t, j] - sum_i topw[t, i] d_topw[t, i]),
+ * zero for the other experts.  topw, d_topw fp32 [T, topk], ids int32 [T, topk] (as
+ * e4b_router_topk wrote them), d_logits fp32 [T, E] (written in full).  Limits and errors
+ * as for e4b_router_topk. */
+e4b_status e4b_router_bwd(const float *topw, const float *d_topw, const int32_t *ids, int32_t T, int32_t E,
+                          int32_t topk, float *d_logits, void *stream);
+
 /* Decode expert `expert` of a stack (or the whole stack if expert < 0) to fp32
  * and/or bf16 [N, K] row-major (either output nullable). */
 e4b_status e4b_dequant(const e4b_qweight *w, int32_t expert, float *out_f32,

@@ -152,6 +152,21 @@ def test_quantize_and_dequant_rejections(L):
     assert L.get_stats()["launches_total"] == 0
 
 
+def test_router_rejections(L):
+    """Router entry points check their sizes before any launch; T = 0 launches nothing."""
+    lib = L.lib()
+    bad = L.E4B_ERR_INVALID_ARG
+    assert lib.e4b_router_topk(0x1, 4, 8, 9, 0x2, 0x3, None) == bad      # topk > E
+    assert lib.e4b_router_topk(0x1, 4, 1025, 2, 0x2, 0x3, None) == bad   # E above the limit
+    assert lib.e4b_router_topk(0x1, 4, 128, 65, 0x2, 0x3, None) == bad   # topk above the limit
+    assert lib.e4b_router_topk(0x1, 4, 8, 0, 0x2, 0x3, None) == bad
+    assert lib.e4b_router_topk(None, 4, 8, 2, 0x2, 0x3, None) == bad
+    assert lib.e4b_router_topk(None, 0, 8, 2, None, None, None) == L.E4B_OK
+    assert lib.e4b_router_bwd(0x1, 0x2, 0x3, -1, 8, 2, 0x4, None) == bad
+    assert lib.e4b_router_bwd(0x1, None, 0x3, 4, 8, 2, 0x4, None) == bad
+    assert lib.e4b_router_bwd(None, None, None, 0, 8, 2, None, None) == L.E4B_OK
+
+
 def test_no_cpu_fallback_in_product():
     """The product package never imports the oracle."""
     pkg = os.path.join(ROOT, "grouped_nf4_gemm_amd")

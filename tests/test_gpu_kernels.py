@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from grouped_nf4_gemm_amd import QStack, route
+from grouped_nf4_gemm_amd import QStack, route, router_bwd, router_topk
 from tests.gpu_helpers import require_gpu
 
 pytestmark = pytest.mark.gpu
@@ -101,3 +101,52 @@ def test_route_skewed_loads():
     g = route(torch.from_numpy(inp.ids).cuda(), s.E)
     for ref, got in zip([cnt, off, perm, inv], g):
         assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------- router
+
+ROUTER_CASES = [
+    # T, E, k, distinct logit levels (None: continuous)
+    (37, 8, 2, None),
+    (64, 8, 1, None),
+    (16, 64, 64, None),        # k = E = one wave
+    (9, 1024, 8, None),        # 16 logits per lane
+    (50, 128, 8, 2),           # many ties
+    (33, 257, 5, 3),           # E not a multiple of 64
+]
+
+
+@pytest.mark.parametrize("T,E,k,levels", ROUTER_CASES)
+def test_router_parity(T, E, k, levels):
+    """ids bit-exact against the oracle; weights and logit gradients to fp32 rounding."""
+    print(f"router T={T} E={E} k={k} levels={levels}", flush=True)
+    rng = np.random.default_rng(T * 1000 + E + k)
+    l = rng.standard_normal((T, E)).astype(np.float32)
+    if levels:
+        l = (np.round(l * levels) / levels).astype(np.float32)
+    ids_ref, w_ref = oracle.router_topk(l, k)
+    ids, w = router_topk(torch.from_numpy(l).cuda(), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 2e-6
+    dw = rng.standard_normal((T, k)).astype(np.float32)
+    d_ref = oracle.router_bwd(w_ref, dw, ids_ref, E)
+    d = router_bwd(torch.from_numpy(w_ref).cuda(), torch.from_numpy(dw).cuda(), torch.from_numpy(ids_ref).cuda(), E)
+    torch.cuda.synchronize()
+    dn = d.cpu().numpy()
+    assert np.max(np.abs(dn - d_ref)) <= 1e-5 * max(1.0, np.abs(d_ref).max())
+    mask = np.ones((T, E), bool)
+    np.put_along_axis(mask, ids_ref.astype(np.int64), False, axis=1)
+    assert np.all(dn[mask] == 0)
+
+
+def test_router_matches_harness_routing():
+    """The device router reproduces the routing the workloads are built with."""
+    s = synth.WORKLOADS["many-small"]
+    rng = np.random.default_rng(77)
+    l = rng.standard_normal((256, s.E)).astype(np.float32)
+    ids_h, w_h = synth.route(l, s.k)
+    ids, w = router_topk(torch.from_numpy(l).cuda(), s.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_h)
+    assert np.max(np.abs(w.cpu().numpy() - w_h)) <= 2e-6
