@@ -205,6 +205,35 @@ def read_traffic(family: str, workload: str):
     return None
 
 
+def router_timing(s, reps: int = 50) -> dict:
+    """The router step on this workload's T x E fp32 logits (outside the timed layer step):
+    average of `reps` launches each of e4b_router_topk and e4b_router_bwd, HIP events on the
+    launch stream; HBM bytes = logits (+ d logits) + ids and weights."""
+    import torch
+    from grouped_nf4_gemm_amd import router_bwd, router_topk
+    if s.T == 0:
+        return {}
+    g = torch.Generator(device="cuda").manual_seed(5)
+    logits = torch.randn(s.T, s.E, device="cuda", generator=g)
+    ids, w = router_topk(logits, s.k)
+    dw = torch.randn(s.T, s.k, device="cuda", generator=g)
+    res = {}
+    for name, fn, nbytes in (("fwd", lambda: router_topk(logits, s.k), s.T * s.E * 4 + s.T * s.k * 8),
+                             ("bwd", lambda: router_bwd(w, dw, ids, s.E), s.T * s.k * 12 + s.T * s.E * 4)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name + "_us"] = us
+        res[name + "_hbm_frac"] = nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS
+    return res
+
+
 def main():
     a = parse()
     if a.summarize_stats:
@@ -359,6 +388,7 @@ def main():
         "roofline": roof,
         "kernels_ms_per_step": {k: v[1] / a.steps for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1][1])},
     }
+    out["router"] = router_timing(s)
     del layer, layers, w_gu, w_dn
     torch.cuda.empty_cache()
     if not a.no_cpu_baseline:

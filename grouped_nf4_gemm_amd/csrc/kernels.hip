@@ -792,16 +792,17 @@ __device__ __forceinline__ float wave_sum_fixed(float v) {
   return __shfl(v, 0);  // lane 0's sum, the same tree for every call
 }
 
+template <int QN>  // logits per lane: E <= 64 QN
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int T, int E, int k,
                                                           int32_t *__restrict__ ids, float *__restrict__ w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *l = logits + (int64_t)t * E;
-  float v[16];
+  float v[QN];
   uint32_t taken = 0;  // bit q: logit lane + 64 q is chosen or past E
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < QN; ++q) {
     const int e = lane + 64 * q;
     v[q] = e < E ? l[e] : 0.0f;
     if (e >= E) taken |= 1u << q;
@@ -812,7 +813,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
     float bv = 0.0f;
     int bi = -1;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < QN; ++q) {
       const int e = lane + 64 * q;
       if (!((taken >> q) & 1u) && (bi < 0 || v[q] > bv)) bv = v[q], bi = e;  // ascending e: ties keep the lower
     }
@@ -836,7 +837,12 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 
 bool launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t s) {
   if (T == 0) return true;
-  router_topk_kernel<<<cdiv(T, 4), 256, 0, s>>>(logits, T, E, k, ids, w);
+  if (E > 1024) return false;
+  const dim3 grid(cdiv(T, 4));
+  if (E <= 64) router_topk_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 128) router_topk_kernel<2><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
+  else if (E <= 256) router_topk_kernel<4><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
+  else router_topk_kernel<16><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
   return hipGetLastError() == hipSuccess;
 }
 
