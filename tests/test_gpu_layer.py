@@ -205,3 +205,40 @@ def test_expanded_stacks_bitwise(shape):
         vb = b[key].view(torch.int32) if b[key].dtype == torch.float32 else b[key].view(torch.int16)
         assert torch.equal(va, vb), key
     _check_all(Case(inp, expand=True), a)
+
+
+@pytest.mark.parametrize("T", [1, 8, 40])
+def test_decode_forward_graph_replay(T):
+    """The few-token forward is graph-capturable: no host synchronisation and no memset nodes.
+    A captured forward is replayed several times, with other eager work between the replays
+    (a forward on different tokens into another buffer), and every replay equals the eager
+    forward bit for bit."""
+    s = synth.custom(6, 256, 384, T, 2, 16, 32.0, "nf4", name=f"graph-t{T}")
+    case = Case(synth.make_inputs(s, seed=90 + T), train=False)
+    other = synth.make_inputs(s, seed=190 + T)
+    x2 = torch.from_numpy(other.x.view(np.int16)).view(torch.bfloat16).cuda()
+    ids2 = torch.from_numpy(other.ids).cuda()
+    w2 = torch.from_numpy(other.topw).cuda()
+    print(f"graph replay T={T}", flush=True)
+    y = torch.empty(T, s.H, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y)
+    case.layer.forward(case.x, case.ids, case.topw, y)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        case.layer.forward(case.x, case.ids, case.topw, y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        case.layer.forward(case.x, case.ids, case.topw, y)
+    for _ in range(3):
+        y.zero_()
+        case.layer.forward(x2, ids2, w2, y2)  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
+    del graph
+    _check_all(case, {"y": ref})
