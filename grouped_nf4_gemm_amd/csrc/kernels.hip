@@ -742,14 +742,12 @@ bool launch_wgrad(const WgradArgs &a, hipStream_t s) {
 
 // =============================================================== combine and friends
 // y[t] = bf16(sum_j w[t,j] * O[inv[t*k+j]]), fp32 sum in j order.
+template <int U>  // 1024-column chunks per workgroup
 __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t split_stride,
                                const int32_t *__restrict__ inv, const float *__restrict__ topw, int k,
                                int H, uint16_t *__restrict__ y) {
-  // block (t, chunk of 1024 columns); thread -> 4 columns
+  // block (t, U chunks of 1024 columns); thread -> 4 columns of each chunk
   const int t = blockIdx.x;
-  const int h = blockIdx.y * 1024 + threadIdx.x * 4;
-  if (h >= H) return;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   // the rows and weights of up to 8 choices first, then per choice the loads of all its
   // split partial sums at once (added in split order), so that the latencies overlap
   constexpr int KP = 8;
@@ -760,25 +758,31 @@ __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t 
     pj[j] = j < k ? inv[(int64_t)t * k + j] : -1;
     wj[j] = j < k ? topw[(int64_t)t * k + j] : 0.f;
   }
-  for (int j = 0; j < k; ++j) {
-    const int p = j < KP ? pj[j] : inv[(int64_t)t * k + j];
-    if (p < 0) continue;
-    const float w = j < KP ? wj[j] : topw[(int64_t)t * k + j];
-    f32x4 ov[COMBINE_MAX_SPLITS];
 #pragma unroll
-    for (int c = 0; c < COMBINE_MAX_SPLITS; ++c)
-      if (c < nsplit) ov[c] = *(const f32x4 *)(O + c * split_stride + (int64_t)p * H + h);
-    f32x4 o = ov[0];
+  for (int u = 0; u < U; ++u) {
+    const int h = (blockIdx.y * U + u) * 1024 + threadIdx.x * 4;
+    if (h >= H) break;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int p = j < KP ? pj[j] : inv[(int64_t)t * k + j];
+      if (p < 0) continue;
+      const float w = j < KP ? wj[j] : topw[(int64_t)t * k + j];
+      f32x4 ov[COMBINE_MAX_SPLITS];
 #pragma unroll
-    for (int c = 1; c < COMBINE_MAX_SPLITS; ++c)
-      if (c < nsplit) o += ov[c];
-    a0 += w * o[0];
-    a1 += w * o[1];
-    a2 += w * o[2];
-    a3 += w * o[3];
+      for (int c = 0; c < COMBINE_MAX_SPLITS; ++c)
+        if (c < nsplit) ov[c] = *(const f32x4 *)(O + c * split_stride + (int64_t)p * H + h);
+      f32x4 o = ov[0];
+#pragma unroll
+      for (int c = 1; c < COMBINE_MAX_SPLITS; ++c)
+        if (c < nsplit) o += ov[c];
+      a0 += w * o[0];
+      a1 += w * o[1];
+      a2 += w * o[2];
+      a3 += w * o[3];
+    }
+    u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+    *(u32x2 *)(y + (int64_t)t * H + h) = out;
   }
-  u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-  *(u32x2 *)(y + (int64_t)t * H + h) = out;
 }
 
 // ================================================================ router
@@ -887,7 +891,9 @@ bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int3
   if (T == 0) return true;
   if (nsplit < 1 || nsplit > COMBINE_MAX_SPLITS) return false;
   LaunchScope ls(FAM_COMBINE, s);
-  combine_kernel<<<dim3(T, cdiv(H, 1024)), 256, 0, s>>>(O, nsplit, split_stride, inv, topw, k, H, y);
+  // many tokens: a workgroup per token covers up to 4 chunks (fewer, longer workgroups)
+  if (T >= 1024) combine_kernel<4><<<dim3(T, cdiv(H, 4096)), 256, 0, s>>>(O, nsplit, split_stride, inv, topw, k, H, y);
+  else combine_kernel<1><<<dim3(T, cdiv(H, 1024)), 256, 0, s>>>(O, nsplit, split_stride, inv, topw, k, H, y);
   return last_launch_ok();
 }
 
