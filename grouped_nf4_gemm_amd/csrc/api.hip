@@ -290,6 +290,9 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.Bd = l_gu->A; a.b_estride = (int64_t)r1 * H; a.ldb = H;
     a.C = z1; a.ldc = r1; a.alpha = l_gu->scaling;
     a.part = part; a.nsplit = lora_a_splits(M, E, a.N, a.K);
+    // few rows: the LoRA-A kernel also writes the gathered rows of x into the O region
+    // (written only later, by down), so gate_up reads them without a dependent gather
+    if (small) a.xg_out = (uint16_t *)O;
     E4B_LAUNCH(lora_a(a));
   }
   {  // h = silu(G_gate) * G_up, G = W1 x + B1 z1
@@ -297,6 +300,10 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
     a.off = off; a.E = E; a.M = M; a.N = I; a.K = H;
     a.A = x; a.lda = H; a.a_gather = perm; a.a_gdiv = d.topk;
     a.a_bytes = (uint32_t)((int64_t)d.T * H * 2);
+    if (small && r1) {  // the gathered copy: M rows in sorted order
+      a.A = (const uint16_t *)O, a.a_gather = nullptr, a.a_gdiv = 1;
+      a.a_bytes = (uint32_t)((int64_t)M * H * 2);
+    }
     a.q = qstack(w_gu);
     a.Bx = W1x; a.bx_estride = (int64_t)2 * I * H; a.bx_bytes = (uint32_t)(a.bx_estride * 2);
     a.xa = z1; a.ldxa = r1; a.xb = r1 ? l_gu->B : nullptr; a.xb_estride = (int64_t)2 * I * r1;

@@ -79,6 +79,9 @@ struct GroupedArgs {
   // fp32 partial sums [nsplit][M][N] go to `part`, then are added in split order
   float *part;
   int nsplit;
+  // few-row LoRA-A only (nullable): also write the gathered activation rows, [M][K] in
+  // sorted-row order, for the GEMM that follows
+  uint16_t *xg_out;
 };
 
 enum BKind : int { B_QNK = 0, B_QKN = 1, B_DENSE = 2 };

@@ -877,6 +877,8 @@ __global__ __launch_bounds__(256) void small_lora_a_kernel(GroupedArgs g) {
       const int k = k0 + u * 2048;
       const bool ok = k < g.K;
       xv[u] = ok ? *(const u32x4 *)(xr + k) : u32x4{0, 0, 0, 0};
+      // the first workgroup of the row keeps the gathered row for the gate_up GEMM
+      if (ok && g.xg_out && blockIdx.y == 0) *(u32x4 *)(g.xg_out + (int64_t)p * g.K + k) = xv[u];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) bv[u][jj] = ok ? *(const u32x4 *)(br[jj] + k) : u32x4{0, 0, 0, 0};
     }
