@@ -331,8 +331,12 @@ __device__ __forceinline__ uint32_t pair_bf16(float x0, float x1, bool odd) {
   const float recv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, false));
   return pack_bf16x2(odd ? recv : x0, odd ? x1 : recv);
 }
+// The tile epilogues' outputs (h, G, O, dG, dXp) are each larger than the last-level cache
+// and are read back only by later kernels: their stores carry the non-temporal hint (cache
+// policy bit 1, `nt`), which measured 1-2% faster on the GEMMs that write them.
+constexpr int EPI_STORE_CPOL = 2;
 __device__ __forceinline__ void bstore32u(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t voff) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, 0, EPI_STORE_CPOL);
 }
 __device__ __forceinline__ uint32_t lane_swap1(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
@@ -344,7 +348,7 @@ __device__ __forceinline__ void bstore_pair_f32(__amdgpu_buffer_rsrc_t r, float 
   const float recv = __uint_as_float(lane_swap1(__float_as_uint(send)));
   typedef int i32x2 __attribute__((ext_vector_type(2)));
   const i32x2 d = {(int)__float_as_uint(odd ? recv : x0), (int)__float_as_uint(odd ? x1 : recv)};
-  __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)voff, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)voff, 0, EPI_STORE_CPOL);
 }
 // The inverse for loads: the even lane loaded row r and the odd lane row r+1, each as the
 // dword of columns (c, c+1) of its pair; returns this lane's column at rows r (lo) and r+1
