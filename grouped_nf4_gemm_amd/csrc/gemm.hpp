@@ -310,6 +310,12 @@ __device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t vof
 __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
+// Packed weight codes are read exactly once per launch in the decode kernels: load them with
+// the non-temporal cache policy so they do not evict the activations and scales that are reused.
+constexpr int CODE_LOAD_CPOL = 2;
+__device__ __forceinline__ u32x4 bload128_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, CODE_LOAD_CPOL));
+}
 __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
       // chunk past kb1 read bytes that their zero scale cancels)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        cw[slot][s][i] = bload128(rc, voffc[i], ((uint32_t)(c * SM_CB) * 32) | (c < nchunks ? 0u : OOB));
+        cw[slot][s][i] = bload128_stream(rc, voffc[i], ((uint32_t)(c * SM_CB) * 32) | (c < nchunks ? 0u : OOB));
       const uint32_t dead = c < nchunks ? 0u : OOB;
       const uint32_t step = FMT == FMT_NF4 ? SM_CB * 4 : FMT == FMT_NF4_DQ ? SM_CB : SM_CB * 2;
       uint32_t win = OOB, sh = 0;
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       const uint32_t dead = j < nblk ? 0u : OOB;
       if (slot % CH == 0) {  // the codes of blocks j .. j+CH-1, 32 rows
 #pragma unroll
-        for (int i = 0; i < NI; ++i) craw[slot / CH][i] = bload128(rc, voffc[i], ((uint32_t)j * 32) | dead);
+        for (int i = 0; i < NI; ++i) craw[slot / CH][i] = bload128_stream(rc, voffc[i], ((uint32_t)j * 32) | dead);
       }
       if (slot % 4 == 0) {  // the scales of blocks j .. j+3
         const uint32_t step = FMT == FMT_NF4 ? 16u : FMT == FMT_NF4_DQ ? 4u : 8u;
