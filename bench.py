@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_TXT"),
                    help="write per-kernel HBM traffic from two rocprofv3 --pmc runs and exit")
     p.add_argument("--command", default="", help="command line recorded in a summary")
+    p.add_argument("--expand", action="store_true",
+                   help="large calls: the forward streams bf16 copies of the stacks instead of decoding them in the tile")
     p.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                    help="time forward-only steps as replays of one captured HIP graph "
                         "(auto: on for the decode-shaped workloads)")
@@ -174,12 +176,12 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out_path: str, command: str) -
 
 
 # kernel family (as the library's event timing names it) -> kernel symbol fragments: the
-# kernel over bf16 copies of the stacks (large batches) and the one that decodes in the tile
+# kernel that decodes in the tile, and the one over bf16 copies of the stacks (--expand)
 FAMILY_SYMBOL = {
-    "gemm_gate_up": ("gemm_x_kernel<false, 2,", "gemm_large_kernel<0, 2,"),
-    "gemm_down": ("gemm_x_kernel<false, 0,", "gemm_large_kernel<0, 0,"),
-    "gemm_down_dgrad": ("gemm_x_kernel<true, 3,", "gemm_large_kernel<1, 3,"),
-    "gemm_gate_up_dgrad": ("gemm_x_kernel<true, 0,", "gemm_large_kernel<1, 0,"),
+    "gemm_gate_up": ("gemm_ws_kernel<0, 2,", "gemm_x_kernel<false, 2,"),
+    "gemm_down": ("gemm_ws_kernel<0, 0,", "gemm_x_kernel<false, 0,"),
+    "gemm_down_dgrad": ("gemm_ws_kernel<1, 3,", "gemm_x_kernel<true, 3,"),
+    "gemm_gate_up_dgrad": ("gemm_ws_kernel<1, 0,", "gemm_x_kernel<true, 0,"),
 }
 
 
@@ -276,7 +278,7 @@ def main():
     # (> 2 GB in all), so the 256 MB last-level cache cannot serve the weights of a step
     # from the previous ones; every copy holds the same bytes.
     ncopy = 1 if with_bwd else max(1, -(-2_500_000_000 // (w_gu.codes.numel() + w_dn.codes.numel())))
-    layers = [MoELayer(w_gu, w_dn, l_gu, l_dn, s.T, s.k, train=with_bwd)]
+    layers = [MoELayer(w_gu, w_dn, l_gu, l_dn, s.T, s.k, train=with_bwd, expand=a.expand)]
     for _ in range(ncopy - 1):
         cq = lambda q: QStack(q.fmt, q.E, q.N, q.K, q.codes.clone(), q.scale.clone(),
                               None if q.scale2 is None else q.scale2.clone())

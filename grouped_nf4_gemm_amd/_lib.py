@@ -15,14 +15,12 @@ E4B_OK, E4B_ERR_INVALID_ARG, E4B_ERR_UNSUPPORTED, E4B_ERR_WORKSPACE, E4B_ERR_HIP
 FMT = {"nf4": 0, "nf4_dq": 1, "mxfp4": 2}
 E4B_TRAIN = 1
 E4B_EXPAND = 2
-E4B_NO_EXPAND = 4
 
 EXPORTS = [
     "e4b_version", "e4b_status_str", "e4b_moe_workspace_size", "e4b_moe_fwd", "e4b_moe_dgrad",
     "e4b_lora_wgrad", "e4b_moe_route", "e4b_dequant", "e4b_quantize", "e4b_moe_check",
     "e4b_get_stats", "e4b_reset_stats", "e4b_timing_enable", "e4b_timing_read",
-    "e4b_router_topk", "e4b_router_bwd",
-]
+    "e4b_router_topk", "e4b_router_bwd",]
 
 
 class E4BError(RuntimeError):
@@ -34,7 +32,7 @@ class E4BError(RuntimeError):
 class QWeight(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("scale2", ctypes.c_void_p)]
+                ("scale2", ctypes.c_void_p), ("dq_table", ctypes.c_void_p), ("codebook", ctypes.c_void_p)]
 
 
 class Lora(ctypes.Structure):
@@ -51,7 +49,7 @@ class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "launches_total", "route", "lora_a", "gemm_gate_up", "gemm_down", "combine",
         "combine_bwd", "gemm_down_dgrad", "gemm_gate_up_dgrad", "unpermute", "wgrad", "quant",
-        "dequant", "expand", "fallbacks")]
+        "dequant", "expand", "router", "fallbacks")]
 
 
 _lib = None

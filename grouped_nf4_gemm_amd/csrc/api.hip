@@ -22,6 +22,7 @@ struct TimedLaunch {
   int fam;
 };
 static std::vector<TimedLaunch> g_pending;
+
 static int64_t g_tl[FAM_COUNT];
 static double g_tms[FAM_COUNT];
 
@@ -30,7 +31,7 @@ const char *family_name(int f) {
                                          "gemm_down",      "combine",      "combine_bwd",
                                          "gemm_down_dgrad", "gemm_gate_up_dgrad", "unpermute",
                                          "wgrad",          "quant",        "dequant",
-                                         "transpose",      "expand"};
+                                         "transpose",      "expand",       "router"};
   return (f >= 0 && f < FAM_COUNT) ? names[f] : "?";
 }
 
@@ -68,18 +69,15 @@ static constexpr size_t NONE = ~(size_t)0;
 // below 2 GiB (32-bit per-lane byte offsets).
 static constexpr int64_t BUF_LIMIT = ((int64_t)1 << 31) - 1;
 
-// Large batches: with many row tiles per expert, the large-tile GEMMs would decode every
-// weight once per row tile.  Above EXPAND_MIN_ROWS routed rows per expert on average the
-// forward instead writes bf16 copies of both stacks into the workspace once (kept for the
-// dgrad of a training forward) and the GEMMs load those directly.  E4B_EXPAND and
-// E4B_NO_EXPAND override the choice; the decode-shaped path (few rows) never expands.
-static constexpr int64_t EXPAND_MIN_ROWS = 1024;
+// The large-tile GEMMs decode the packed stacks inside the tile, once per 256-row tile, in the
+// forward and again in the dgrad (nothing dequantised is held between the calls).  A caller
+// can ask the forward to write bf16 copies of both stacks into the workspace first and stream
+// those (E4B_EXPAND: 2 bytes per weight of workspace); the results are bit-identical.  The
+// decode-shaped path (few rows) never expands.
 static bool use_expand(const e4b_moe_desc &d) {
   const int64_t M = (int64_t)d.T * d.topk;
-  if (M <= SMALL_M_MAX || (d.flags & E4B_NO_EXPAND)) return false;
-  if ((int64_t)2 * d.I * d.H * 2 > BUF_LIMIT) return false;  // one expert's copy: 32-bit offsets
-  if (d.flags & E4B_EXPAND) return true;
-  return M >= EXPAND_MIN_ROWS * d.E;
+  if (M <= SMALL_M_MAX || !(d.flags & E4B_EXPAND)) return false;
+  return (int64_t)2 * d.I * d.H * 2 <= BUF_LIMIT;  // one expert's copy: 32-bit offsets
 }
 
 static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
@@ -160,8 +158,7 @@ static e4b_status check_desc(const e4b_moe_desc *d) {
   const int64_t M = (int64_t)d->T * d->topk;
   if ((int64_t)d->T * d->H * 2 > BUF_LIMIT || M * d->H * 4 > BUF_LIMIT || M * 2 * d->I * 2 > BUF_LIMIT)
     return E4B_ERR_INVALID_ARG;
-  if (d->flags & ~(E4B_TRAIN | E4B_EXPAND | E4B_NO_EXPAND)) return E4B_ERR_INVALID_ARG;
-  if ((d->flags & E4B_EXPAND) && (d->flags & E4B_NO_EXPAND)) return E4B_ERR_INVALID_ARG;
+  if (d->flags & ~(E4B_TRAIN | E4B_EXPAND)) return E4B_ERR_INVALID_ARG;
   return E4B_OK;
 }
 
@@ -179,6 +176,8 @@ static e4b_status check_q(const e4b_qweight *q, int E, int N, int K) {
   if (!q || !q->codes || !q->scale) return E4B_ERR_INVALID_ARG;
   if (q->fmt < E4B_FMT_NF4 || q->fmt > E4B_FMT_MXFP4) return E4B_ERR_UNSUPPORTED;
   if (q->fmt == E4B_FMT_NF4_DQ && !q->scale2) return E4B_ERR_INVALID_ARG;
+  if (q->fmt != E4B_FMT_NF4_DQ && q->dq_table) return E4B_ERR_INVALID_ARG;
+  if (q->fmt == E4B_FMT_MXFP4 && q->codebook) return E4B_ERR_INVALID_ARG;
   if (q->E != E || q->N != N || q->K != K) return E4B_ERR_INVALID_ARG;
   if ((int64_t)E * N * K / 2 > BUF_LIMIT) return E4B_ERR_INVALID_ARG;
   return E4B_OK;
@@ -189,6 +188,8 @@ static QStack qstack(const e4b_qweight *q) {
   s.codes = q->codes;
   s.scale = q->scale;
   s.scale2 = q->scale2;
+  s.codebook = q->codebook;
+  s.dq_table = q->dq_table;
   s.fmt = q->fmt;
   s.N = q->N;
   s.K = q->K;
@@ -251,10 +252,10 @@ static e4b_status validate_layer(const e4b_moe_desc *d, const e4b_qweight *w_gu,
   return E4B_OK;
 }
 
-e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
-                       const e4b_lora *l_gu, const e4b_lora *l_dn, const uint16_t *x,
-                       const int32_t *ids, const float *topw, uint16_t *y, void *ws,
-                       size_t ws_bytes, void *stream) {
+// The forward as a stream-ordered kernel sequence over a workspace of ws_bytes bytes.
+static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
+                          const e4b_lora *l_gu, const e4b_lora *l_dn, const uint16_t *x, const int32_t *ids,
+                          const float *topw, uint16_t *y, void *ws, size_t ws_bytes, void *stream) {
   int r1, r2;
   E4B_TRY(validate_layer(desc, w_gu, w_dn, l_gu, l_dn, &r1, &r2));
   const e4b_moe_desc &d = *desc;
@@ -343,6 +344,13 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
   return E4B_OK;
 }
 
+e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
+                       const e4b_lora *l_gu, const e4b_lora *l_dn, const uint16_t *x,
+                       const int32_t *ids, const float *topw, uint16_t *y, void *ws,
+                       size_t ws_bytes, void *stream) {
+  return moe_fwd(desc, w_gu, w_dn, l_gu, l_dn, x, ids, topw, y, ws, ws_bytes, stream);
+}
+
 e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
                          const e4b_lora *l_gu, const e4b_lora *l_dn, const int32_t *ids,
                          const float *topw, const uint16_t *dy, uint16_t *dx, float *d_topw,
@@ -365,9 +373,9 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
   float *part = L.part == NONE ? nullptr : at<float>(ws, L.part);
   uint16_t *A1T = at<uint16_t>(ws, L.A1T), *B1T = at<uint16_t>(ws, L.B1T);
   uint16_t *A2T = at<uint16_t>(ws, L.A2T), *B2T = at<uint16_t>(ws, L.B2T);
-  // bf16 copies of the stacks that the training forward wrote (expanded calls only)
-  const uint16_t *W1x = L.W1x == NONE ? nullptr : at<uint16_t>(ws, L.W1x);
-  const uint16_t *W2x = L.W2x == NONE ? nullptr : at<uint16_t>(ws, L.W2x);
+  // the base is decoded from the packed stacks again (the forward's bf16 copies, if it made
+  // any, are not read)
+  const uint16_t *W1x = nullptr, *W2x = nullptr;
 
   E4B_LAUNCH(launch_combine_bwd(dy, O, inv, topw, d.T, d.topk, H, dO, d_topw, s));
   if (r2) {
@@ -560,6 +568,7 @@ e4b_status e4b_get_stats(e4b_stats *out) {
   out->quant = g_count[FAM_QUANT].load();
   out->dequant = g_count[FAM_DEQUANT].load();
   out->expand = g_count[FAM_EXPAND].load();
+  out->router = g_count[FAM_ROUTER].load();
   out->fallbacks = 0;
   return E4B_OK;
 }

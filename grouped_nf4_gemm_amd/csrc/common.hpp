@@ -33,6 +33,14 @@ __device__ __forceinline__ float nf4_value(uint32_t q) {
   for (int i = 14; i >= 0; --i) r = q == (uint32_t)i ? v[i] : r;
   return r;
 }
+// Code value q of a stack: its own table, or the built-in one.
+__device__ __forceinline__ float code_value(const float *codebook, uint32_t q) {
+  return codebook ? codebook[q] : nf4_value(q);
+}
+// Absmax code c of a double-quantised stack: its own table, or the built-in fp32(c / 255).
+__device__ __forceinline__ float dq_value(const float *dq_table, uint32_t c) {
+  return dq_table ? dq_table[c] : (float)c / 255.0f;
+}
 
 // Logistic sigmoid 1 / (1 + e^-x) from the hardware base-2 exponential and reciprocal
 // (each within about one ulp); saturates to 0 and 1 for large |x|.
@@ -56,13 +64,17 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t X) {
   return X == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(X << 23);
 }
 
-// Per-workgroup decode tables in LDS.
-//  cb2[b]  = {nf4[b >> 4], nf4[b & 15]}: the two NF4 values of code byte b, element 2j
+// Per-workgroup decode tables in LDS, filled from the stack's own tables (or the built-in
+// ones when it passes none).
+//  cb2[b]  = {nf4[b >> 4], nf4[b & 15]}: the two code values of code byte b, element 2j
 //            (high nibble) first, so one 8-byte LDS read serves two codes.
-//  tab8[c] = fp32(c / 255): the 8-bit absmax code of the double-quantised format.
+//  tab8[c] = the 8-bit absmax code table of the double-quantised format (built-in:
+//            fp32(c / 255)).
+//  cb[q]   = the sixteen code values, read by the register (byte-plane) decode.
 struct DecodeTables {
   float2 cb2[256];
   float tab8[256];
+  float cb[16];
 };
 
 // The NF4 values of the 8 codes of one 32-bit word (bytes in memory order; element 2j in
@@ -89,12 +101,11 @@ __device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, cons
   return nf4_scale_pack(v, absmax);
 }
 
-// Register-resident decode table of one NF4 block: the sixteen values e[q] = bf16(nf4[q] *
+// Register-resident decode table of one NF4 block: the sixteen values e[q] = bf16(v[q] *
 // absmax) (the same rounding as nf4_scale_pack) split into byte planes, pl[i] = low bytes of
 // e[4i .. 4i+3] and pl[4 + i] = their high bytes (i < 4), so that byte permutes can look up
-// four codes at a time without touching LDS.
-__device__ __forceinline__ void nf4_planes(float absmax, uint32_t (&pl)[8]) {
-  constexpr float v[16] = E4B_NF4_VALUES;
+// four codes at a time without touching LDS.  v: the code values of the stack.
+__device__ __forceinline__ void nf4_planes(float absmax, const float *v, uint32_t (&pl)[8]) {
   uint32_t e[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) e[k] = pack_bf16x2(v[2 * k] * absmax, v[2 * k + 1] * absmax);
@@ -142,6 +153,8 @@ struct QStack {
   const uint8_t *codes;
   const void *scale;
   const float *scale2;
+  const float *codebook;  // NF4 formats: 16 code values (nullptr: the built-in NormalFloat table)
+  const float *dq_table;  // NF4_DQ: 256 absmax code values (nullptr: the built-in c / 255)
   int fmt;
   int N, K;  // per-expert matrix [N, K], K contiguous
   uint32_t codes_bytes, scale_bytes, scale2_bytes;  // extents (buffer range checks)

@@ -283,20 +283,18 @@ struct Mma {
 }  // namespace e4b
 
 // =====================================================================================
-// Large-tile variant: 256 x 256 output per workgroup, 256 threads = 4 wave64s laid out
-// 2 x 2, each wave owning 128 x 128 as 4 x 4 tiles of 32x32x16 MFMAs (256 accumulator
-// registers; one wave per SIMD).  Software pipeline over K slabs of 64: A rows arrive by
-// direct-to-LDS buffer loads, the 4-bit B operand by buffer loads into registers two
-// slabs ahead; it is decoded and written into LDS between the MFMA k-steps of the slab
-// before it is used.  Buffer loads keep a wave-uniform 64-bit base in SGPRs and a 32-bit
-// per-lane offset (the slab step goes in the scalar offset), and rows past the end of a
-// segment read as zero through the buffer's range check.
+// Large-tile building blocks: 256 x 256 outputs per workgroup, accumulated by eight waves
+// (two per SIMD) of 128 x 64 each as 4 x 2 tiles of 32x32x16 MFMAs.  K runs in slabs of
+// 64: A rows arrive by direct-to-LDS buffer loads, the 4-bit B operand by buffer loads into
+// registers two slabs ahead, decoded and written into LDS a slab before it is used (the
+// kernels that assemble these are in kernels.hip).  Buffer loads keep a wave-uniform
+// 64-bit base in SGPRs and a 32-bit per-lane offset (the slab step goes in the scalar
+// offset), and rows past the end of a segment read as zero through the buffer's range check.
 // =====================================================================================
 namespace e4b {
 
-// Large tile: 256 x 256 outputs per workgroup of eight waves, two per SIMD, so one wave's
-// decode and address work issues while the other wave's MFMAs run.  Wave w owns rows
-// (w >> 2) * 128 .. +127 and columns (w & 3) * 64 .. +63 of the tile.
+// Wave w (< 8) of the accumulating waves owns rows (w >> 2) * 128 .. +127 and columns
+// (w & 3) * 64 .. +63 of the tile.
 constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
 constexpr int KN_STRIDE = L_BN + 16;  // [k][n] B tile row: 272 bf16 (544 bytes = 32 mod 128)
 constexpr uint32_t OOB = 0x80000000u;  // per-lane offset that reads as zero
@@ -319,8 +317,8 @@ __device__ __forceinline__ u32x4 bload128_stream(__amdgpu_buffer_rsrc_t r, uint3
 __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
 }
-__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint16_t v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)voff, 0, 0);
@@ -416,16 +414,19 @@ union BBuf {
 };
 
 // A: 256 rows x 64 k of a row-major bf16 matrix (optionally gathered rows) loaded
-// straight into LDS.  Wave w, instruction i fills the 1 KB block of rows 8*(4w+i) ..
-// +7: lane l reads row 8*(4w+i) + l/8, the logical chunk that lands at physical chunk l%8.
-struct LDirectA {
-  uint32_t voff[4];
-  __device__ __forceinline__ void init(int rows, int64_t row0, const int32_t *__restrict__ gather,
+// straight into LDS by NW waves.  Loading wave v (0 .. NW-1), instruction i fills the 1 KB
+// block of rows 8*(NI*v+i) .. +7: lane l reads row 8*(NI*v+i) + l/8, the logical chunk that
+// lands at physical chunk l%8.
+template <int NW>
+struct LDirectAN {
+  static constexpr int NI = 32 / NW;  // 1 KB blocks per loading wave
+  uint32_t voff[NI];
+  __device__ __forceinline__ void init(int v, int rows, int64_t row0, const int32_t *__restrict__ gather,
                                        int gdiv, int64_t ld) {
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int l = threadIdx.x & 63;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (w * 4 + i) * 8 + (l >> 3);
+    for (int i = 0; i < NI; ++i) {
+      const int r = (v * NI + i) * 8 + (l >> 3);
       const int lc = swz_chunk(r, l & 7);  // the swizzle is its own inverse
       if (r < rows) {
         const int64_t s = gather ? (int64_t)(gather[row0 + r] / gdiv) : row0 + r;
@@ -436,12 +437,21 @@ struct LDirectA {
     }
   }
   // soff: byte offset of the slab's first column (OOB: the slab reads as zero)
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, ATile &t, uint32_t soff) {
-    const int w = threadIdx.x >> 6;
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, ATile &t, uint32_t soff, int v) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void *)&t.v[(w * 4 + i) * 8 * BK], 16, voff[i], soff, 0, 0);
+          r, (__attribute__((address_space(3))) void *)&t.v[(v * NI + i) * 8 * BK], 16, voff[i], soff, 0, 0);
+  }
+};
+// All eight waves of a 512-thread workgroup load.
+struct LDirectA : LDirectAN<8> {
+  __device__ __forceinline__ void init(int rows, int64_t row0, const int32_t *__restrict__ gather, int gdiv,
+                                       int64_t ld) {
+    LDirectAN<8>::init(threadIdx.x >> 6, rows, row0, gather, gdiv, ld);
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, ATile &t, uint32_t soff) {
+    LDirectAN<8>::issue(r, t, soff, threadIdx.x >> 6);
   }
 };
 
@@ -529,7 +539,7 @@ struct GroupDecoder {
   uint32_t pl[8];
   __device__ __forceinline__ void prepare(uint32_t raw, float s2, const DecodeTables &tb) {
     sc = group_scale<FMT>(raw, s2, tb);
-    if constexpr (FMT != FMT_MXFP4) nf4_planes(sc, pl);
+    if constexpr (FMT != FMT_MXFP4) nf4_planes(sc, tb.cb, pl);
   }
   __device__ __forceinline__ u32x4 operator()(uint32_t w) const {
     if constexpr (FMT == FMT_MXFP4) return mxfp4_word_to_bf16(w, sc);
@@ -550,46 +560,6 @@ __device__ __forceinline__ void fetch_scale(__amdgpu_buffer_rsrc_t rs, __amdgpu_
   }
 }
 
-// B from a 4-bit stack stored [N, K] (K contiguous): thread -> tile row tid % 256 (one
-// weight row) and half tid / 256 of the slab (32 k): one 16-byte code load and one block
-// scale (an NF4 block of 64 spans both halves; an MXFP4 block of 32 is exactly one half).
-// Stored as four 16-byte LDS pieces, one per k-step part.
-template <int FMT>
-struct LQuantNK {
-  u32x4 codes;
-  uint32_t sraw;
-  float s2;
-  GroupDecoder<FMT> dec;
-  uint32_t cvoff, svoff;  // byte offsets at k0 = 0
-  int64_t blk0;
-  __device__ __forceinline__ void init(const QStack &q, int e, const RowMap &map, int Nrows) {
-    const int n = map(threadIdx.x & 255), hh = threadIdx.x >> 8;
-    if (n < Nrows) {
-      const int64_t el = ((int64_t)e * q.N + n) * q.K;
-      cvoff = (uint32_t)(el / 2) + 16 * hh;
-      blk0 = el >> 6;
-      svoff = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blk0 : (uint32_t)(el >> 5) + hh;
-    } else {
-      cvoff = svoff = OOB;
-      blk0 = 0;
-    }
-  }
-  // dead = OOB for a slab past the end (every load then reads zero), else 0
-  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                        __amdgpu_buffer_rsrc_t rs2, int k0, uint32_t dead) {
-    codes = bload128(rc, cvoff, ((uint32_t)k0 / 2) | dead);
-    const uint32_t soff = FMT == FMT_NF4 ? (uint32_t)(k0 / 64) * 4 : FMT == FMT_NF4_DQ ? (uint32_t)(k0 / 64)
-                                                                                       : (uint32_t)(k0 / 32);
-    fetch_scale<FMT>(rs, rs2, svoff, soff, blk0 + k0 / 64, dead, sraw, s2);
-  }
-  __device__ __forceinline__ void prepare(const DecodeTables &tb) { dec.prepare(sraw, s2, tb); }
-  // decode code word `part` (8 k) and write it into the tile
-  __device__ __forceinline__ void store(LTile &t, int part) const {
-    const int row = threadIdx.x & 255;
-    st_lds16(&t.v[row][bswz(row, (threadIdx.x >> 8) * 4 + part)], dec(codes[part]));
-  }
-};
-
 // B from a 4-bit stack reduced over its STORED row axis: LDS tile [64 k][256 n], k =
 // stored rows k0..k0+63, n = stored columns n0..n0+255.  Thread -> stored row tid / 8 and
 // 32 stored columns (tid % 8): one 16-byte code load and one block scale (32 aligned
@@ -604,8 +574,8 @@ struct LQuantKN {
   GroupDecoder<FMT> dec;
   uint32_t cvoff, svoff, crow, srow;  // offsets at k0 = 0 of this thread's stored row; per-row steps
   int64_t blk0, blkrow;
-  __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout) {
-    const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
+  __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout, int vt) {
+    const int kb = vt >> 3, nb = vt & 7;
     const int n = n0 + nb * 32;
     crow = (uint32_t)(q.K / 2);
     blkrow = q.K / 64;
@@ -626,9 +596,69 @@ struct LQuantKN {
     fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)k0 * srow, blk0 + (int64_t)k0 * blkrow, dead, sraw, s2);
   }
   __device__ __forceinline__ void prepare(const DecodeTables &tb) { dec.prepare(sraw, s2, tb); }
-  __device__ __forceinline__ void store(LTileKN &t, int part) const {
-    const int kb = threadIdx.x >> 3, nb = threadIdx.x & 7;
+  __device__ __forceinline__ void store(LTileKN &t, int part, int vt) const {
+    const int kb = vt >> 3, nb = vt & 7;
     st_lds16(&t.v[kb][knswz(nb * 32 + part * 8)], dec(w[part]));
+  }
+};
+
+// B from a 4-bit stack stored [N, K] for the producer waves: thread p (0..255) -> tile row p
+// (weight row map(p)) and the whole 64-k slab: two 16-byte code loads (32 contiguous bytes),
+// one block scale (NF4 formats: the slab is one block of 64) or two (MXFP4: blocks of 32),
+// decoded into the eight 16-byte pieces of the tile row.
+template <int FMT>
+struct LQuantRow {
+  u32x4 c0, c1;
+  uint32_t sraw;
+  float s2;
+  uint32_t cvoff, svoff;  // byte offsets at k0 = 0
+  int64_t blk0;
+  __device__ __forceinline__ void init(const QStack &q, int e, const RowMap &map, int Nrows, int p) {
+    const int n = map(p);
+    if (n < Nrows) {
+      const int64_t el = ((int64_t)e * q.N + n) * q.K;
+      cvoff = (uint32_t)(el / 2);
+      blk0 = el >> 6;
+      svoff = FMT == FMT_NF4 ? (uint32_t)(blk0 * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blk0 : (uint32_t)(el >> 5);
+    } else {
+      cvoff = svoff = OOB;
+      blk0 = 0;
+    }
+  }
+  // loads of one slab: 2 code loads + 1 scale load (+ the second-level scale for NF4_DQ)
+  static constexpr int LOADS = FMT == FMT_NF4_DQ ? 4 : 3;
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                        __amdgpu_buffer_rsrc_t rs2, int k0, uint32_t dead) {
+    c0 = bload128(rc, cvoff, ((uint32_t)k0 / 2) | dead);
+    c1 = bload128(rc, cvoff + 16, ((uint32_t)k0 / 2) | dead);
+    if constexpr (FMT == FMT_NF4) {
+      sraw = bload32(rs, svoff, ((uint32_t)(k0 / 64) * 4) | dead);
+    } else if constexpr (FMT == FMT_NF4_DQ) {
+      sraw = bload8(rs, svoff, (uint32_t)(k0 / 64) | dead);
+      s2 = __uint_as_float(bload32(rs2, (uint32_t)((blk0 + k0 / 64) >> 8) * 4, dead));
+    } else {  // the two E8M0 bytes of the slab's two blocks of 32 (2-byte aligned)
+      sraw = bload16(rs, svoff + (uint32_t)(k0 / 32), dead);
+    }
+  }
+  // decode the slab and write tile row p: piece c (8 k) from code word c
+  template <class TileT>
+  __device__ __forceinline__ void decode_store(TileT &t, const DecodeTables &tb, int p) const {
+    if constexpr (FMT == FMT_MXFP4) {
+      const float sa = e8m0_to_f32(sraw & 0xffu), sb = e8m0_to_f32((sraw >> 8) & 0xffu);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t w = c < 4 ? c0[c] : c1[c - 4];
+        st_lds16(&t.v[p][bswz(p, c)], mxfp4_word_to_bf16(w, c < 4 ? sa : sb));
+      }
+    } else {
+      GroupDecoder<FMT> dec;
+      dec.prepare(sraw, s2, tb);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t w = c < 4 ? c0[c] : c1[c - 4];
+        st_lds16(&t.v[p][bswz(p, c)], dec(w));
+      }
+    }
   }
 };
 

@@ -107,11 +107,12 @@ bool launch_route(const int32_t *ids, int M, int E, int32_t *cnt, int32_t *off, 
   return last_launch_ok();
 }
 
-// Per-workgroup LDS decode tables (see DecodeTables).
-__device__ __forceinline__ void init_decode_tables(DecodeTables &t) {
+// Per-workgroup LDS decode tables (see DecodeTables) from the stack's tables.
+__device__ __forceinline__ void init_decode_tables(DecodeTables &t, const QStack &q) {
   for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-    t.cb2[i] = make_float2(nf4_value(i >> 4), nf4_value(i & 15));
-    t.tab8[i] = (float)i / 255.0f;
+    t.cb2[i] = make_float2(code_value(q.codebook, i >> 4), code_value(q.codebook, i & 15));
+    t.tab8[i] = dq_value(q.dq_table, i);
+    if (i < 16) t.cb[i] = code_value(q.codebook, i);
   }
 }
 
@@ -201,15 +202,11 @@ int wgrad_splits(int M, int E, int Na, int Nb) {
   return splits_for(tiles * E, (int64_t)M / E / BK);
 }
 
-// Large-tile grouped GEMM (256 x 256 per workgroup, 8 waves, double-buffered LDS).
-// Software pipeline over K slabs of 64: while the MFMAs consume slab s from LDS buffer
-// s&1, the registers of slab s+1 (loaded two slabs earlier) are decoded and written into
-// the other buffer piece by piece between the MFMA k-steps, and the global loads of slabs
-// s+2 and s+3 are in flight.  One barrier per slab.
-// Direct-to-LDS loads count in vmcnt and are not covered by the barrier: every wave
-// waits for its own before the workgroup barrier that publishes them.  vmcnt(n) waits
-// until at most n vector-memory loads of this wave are outstanding (loads retire in
-// order), so the B loads issued after the A loads can stay in flight.
+// Waits of the large-tile pipelines.  Direct-to-LDS loads count in vmcnt and are not
+// covered by a barrier: every wave waits for its own before the workgroup barrier that
+// publishes them.  vmcnt(n) waits until at most n vector-memory loads of this wave are
+// outstanding (loads retire in order), so loads issued after the ones waited for can stay in
+// flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
@@ -233,111 +230,17 @@ __device__ __forceinline__ void slab_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Vector-memory loads one B fetch issues per thread (see LQuantNK / LQuantKN::fetch).
-template <bool KN, int FMT>
-constexpr int b_fetch_loads() {
-  // one code load + one scale load (+ the second-level scale for NF4_DQ), NK and KN alike
+// Vector-memory loads one K-major B fetch issues per thread (see LQuantKN::fetch): one code
+// load + one scale load (+ the second-level scale for NF4_DQ).
+template <int FMT>
+constexpr int kn_fetch_loads() {
   return FMT == FMT_NF4_DQ ? 3 : 2;
 }
 
-template <int BKIND, int FMT>
-struct LargePipe {
-  static constexpr bool KN = BKIND == B_QKN;
-  using BLoader = typename std::conditional<KN, LQuantKN<FMT>, LQuantNK<FMT>>::type;
-  using BTile = typename std::conditional<KN, LTileKN, LTile>::type;
-  DecodeTables &tb;
-  ATile &A0, &A1;
-  BBuf &B0, &B1;
-  const GroupedArgs &g;
-  __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
-  LDirectA la;
-  BLoader lb[3];  // B register ring: slab t lives in lb[t % 3]
-  LMma mma;
-
-  // Members are set here, never zero-filled as an aggregate: a memset over the buffer
-  // resources would keep them in memory and make every buffer load a per-lane loop.
-  __device__ __forceinline__ LargePipe(DecodeTables &tb_, ATile &a0, ATile &a1, BBuf &b0, BBuf &b1,
-                                       const GroupedArgs &g_)
-      : tb(tb_), A0(a0), A1(a1), B0(b0), B1(b1), g(g_),
-        ra(make_rsrc(g_.A, g_.a_bytes)),
-        rc(make_rsrc(g_.q.codes, g_.q.codes_bytes)),
-        rs(make_rsrc(g_.q.scale, g_.q.scale_bytes)),
-        rs2(make_rsrc(g_.q.scale2, g_.q.scale2_bytes)) {}
-
-  template <int P>
-  __device__ __forceinline__ ATile &atile() {
-    if constexpr (P == 0) return A0;
-    else return A1;
-  }
-  template <int P>
-  __device__ __forceinline__ BTile &btile() {
-    BBuf &b = P == 0 ? B0 : B1;
-    if constexpr (KN) return b.kn;
-    else return b.nk;
-  }
-  // Loads of a slab past the end read zero (scalar offset pushed out of range), so every
-  // load is issued unconditionally and the loop body is straight-line code.
-  __device__ __forceinline__ static uint32_t dead(int slab, int nmain) { return slab < nmain ? 0u : OOB; }
-  __device__ __forceinline__ void fetch_b(int stage, int slab, int nmain) {
-    lb[stage].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
-  }
-  __device__ __forceinline__ void issue_a(ATile &t, int slab, int nmain) {
-    la.issue(ra, t, (uint32_t)(slab * BK * 2) | dead(slab, nmain));
-  }
-  // Slab s (LDS buffers P = s % 2) computes while slab s+1 is completed into buffers P^1:
-  // its A rows by direct loads issued now, its B decoded from registers lb[(s+1) % 3]
-  // between the k-steps.  The B loads of slab s+3 go into lb[s % 3], so B codes arrive two
-  // slabs before they are decoded.  Every body runs its MFMAs, so the accumulators follow
-  // one path; a slab past the end has zero A and B.
-  template <int P, int Q>
-  __device__ __forceinline__ void body(int s, int nmain) {
-    constexpr int QD = (Q + 1) % 3;
-    // The scheduler keeps the issue order: the A rows first, then the B loads, whose
-    // count is the vmcnt the closing barrier leaves outstanding.
-    issue_a(atile<P ^ 1>(), s + 1, nmain);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch_b(Q, s + 3, nmain);
-    __builtin_amdgcn_sched_barrier(0);
-    lb[QD].prepare(tb);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      mma.template kstep<KN>(atile<P>(), btile<P>(), ks);
-      lb[QD].store(btile<P ^ 1>(), ks);
-    }
-    slab_barrier<b_fetch_loads<KN, FMT>()>();  // the A rows of slab s+1 have landed
-  }
-  __device__ __forceinline__ void run(int nmain) {
-    issue_a(A0, 0, nmain);
-    fetch_b(0, 0, nmain);
-    fetch_b(1, 1, nmain);
-    fetch_b(2, 2, nmain);
-    lb[0].prepare(tb);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) lb[0].store(btile<0>(), p);
-    wait_lds_dma();
-    __syncthreads();
-    // six bodies cycle both the LDS buffer parity and the register stage
-    for (int s = 0;; s += 6) {
-      body<0, 0>(s, nmain);
-      if (s + 1 >= nmain) break;
-      body<1, 1>(s + 1, nmain);
-      if (s + 2 >= nmain) break;
-      body<0, 2>(s + 2, nmain);
-      if (s + 3 >= nmain) break;
-      body<1, 0>(s + 3, nmain);
-      if (s + 4 >= nmain) break;
-      body<0, 1>(s + 4, nmain);
-      if (s + 5 >= nmain) break;
-      body<1, 2>(s + 5, nmain);
-      if (s + 6 >= nmain) break;
-    }
-  }
-};
-
 // The same main loop over a bf16 copy of the stack (written by expand_kernel with the same
 // decode functions): A and B both go HBM -> LDS by direct loads, with no decode work, and
-// the MFMA sequence over identical LDS contents is that of LargePipe, so the two give
-// bit-identical accumulators.  The A rows land one slab ahead; the weight tiles, which
+// the MFMA sequence over identical LDS contents is that of the producer / consumer tiles,
+// so the two give bit-identical accumulators.  The A rows land one slab ahead; the weight tiles, which
 // other workgroups on the same L2 rarely share, land two slabs ahead in a ring of three
 // LDS tiles.
 union XBuf {
@@ -442,10 +345,10 @@ struct XPipe {
 };
 
 // After the main loop: the LoRA K-extension into the same accumulator (through the A0 /
-// B0 tiles), then the epilogue.
-template <int EPI>
-__device__ __forceinline__ void large_finish(LMma &mma, const GroupedArgs &g, const TileM &tm, int e, int n0,
-                                             const RowMap &map, int Nrows, ATile &A0, LTile &B0) {
+// B0 tiles) by the 512 threads that hold the accumulators; any other waves of the
+// workgroup take part in its barriers only (lora_barriers).
+__device__ __forceinline__ void lora_extension(LMma &mma, const GroupedArgs &g, const TileM &tm, int e,
+                                               const RowMap &map, int Nrows, ATile &A0, LTile &B0) {
   if (g.r > 0) {  // LoRA rank as a K-extension of the same accumulator
     LRegA lx;
     LDenseNK lbd;
@@ -460,6 +363,27 @@ __device__ __forceinline__ void large_finish(LMma &mma, const GroupedArgs &g, co
       __syncthreads();
     }
   }
+}
+__device__ __forceinline__ void lora_barriers(const GroupedArgs &g) {
+  for (int k0 = 0; k0 < g.r; k0 += BK) {
+    __syncthreads();
+    __syncthreads();
+  }
+}
+
+template <int EPI>
+__device__ __forceinline__ void large_epilogue(LMma &mma, const GroupedArgs &g, const TileM &tm, int n0);
+
+template <int EPI>
+__device__ __forceinline__ void large_finish(LMma &mma, const GroupedArgs &g, const TileM &tm, int e, int n0,
+                                             const RowMap &map, int Nrows, ATile &A0, LTile &B0) {
+  lora_extension(mma, g, tm, e, map, Nrows, A0, B0);
+  large_epilogue<EPI>(mma, g, tm, n0);
+}
+
+// The tile epilogue of the 512 accumulator threads.
+template <int EPI>
+__device__ __forceinline__ void large_epilogue(LMma &mma, const GroupedArgs &g, const TileM &tm, int n0) {
 
   // Outputs go through buffer resources over exactly this tile's rows, so the range check
   // drops the stores of rows past the tile; a lane whose column is past the end gets an
@@ -567,35 +491,6 @@ __device__ __forceinline__ void large_finish(LMma &mma, const GroupedArgs &g, co
   }
 }
 
-template <int BKIND, int EPI, bool SWIGLU, int FMT>
-__global__ __launch_bounds__(L_THREADS) void gemm_large_kernel(GroupedArgs g) {
-  // separate LDS objects, so the compiler can tell the A tiles that direct loads fill
-  // from the B tiles and tables that ordinary LDS stores write
-  // (the largest alignment places the tables at LDS address 0, so table offsets fit the
-  // 16-bit immediate of the LDS reads)
-  __shared__ DecodeTables tb;
-  __shared__ ATile A0, A1;
-  __shared__ BBuf B0, B1;
-  __shared__ int tile_sh[4];
-  init_decode_tables(tb);
-  TileM tm;
-  if (!find_tile(g.off, g.E, L_BM, blockIdx.y, tm, tile_sh)) return;
-  const int e = tm.e;
-  const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
-  const RowMap map{n0, g.I, SWIGLU};
-  const int Nrows = SWIGLU ? 2 * g.I : g.N;
-
-  LargePipe<BKIND, FMT> pipe(tb, A0, A1, B0, B1, g);
-  pipe.mma.zero();
-  pipe.la.init(tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
-  if constexpr (BKIND == B_QKN) pipe.lb[0].init(g.q, e, n0, g.N);
-  else pipe.lb[0].init(g.q, e, map, Nrows);
-  pipe.lb[1] = pipe.lb[0];
-  pipe.lb[2] = pipe.lb[0];
-  pipe.run(g.K / BK);
-  large_finish<EPI>(pipe.mma, g, tm, e, n0, map, Nrows, A0, B0.nk);
-}
-
 // The large tile over a bf16 copy of the stack (XPipe).  Its LDS is the two A tiles and
 // the three B tiles (160 KB): the tile lookup runs in every wave instead of through LDS.
 template <bool KN, int EPI, bool SWIGLU>
@@ -618,6 +513,180 @@ __global__ __launch_bounds__(L_THREADS) void gemm_x_kernel(GroupedArgs g) {
   large_finish<EPI>(pipe.mma, g, tm, e, n0, map, Nrows, A0, B0.nk);
 }
 
+
+// =============================================================== producer / consumer tiles
+// The large tile with the work split by wave: eight consumer waves (two per SIMD) hold the
+// 256 x 256 accumulators and only read MFMA fragments from LDS and issue MFMAs; four
+// producer waves (one per SIMD) stream the A rows straight into LDS and load, decode and
+// write the 4-bit B slab.  The decode's VALU work then issues beside the other waves' MFMAs
+// instead of in the same instruction stream.  One workgroup barrier per slab: past barrier
+// s, slab s is in LDS buffers s % 2, every consumer has finished slab s-1, and the
+// producers fill buffers (s+1) % 2 with slab s+1 while the consumers compute slab s.  The
+// B codes are loaded two slabs before they are decoded, in a register ring of three.
+constexpr int WS_CONSUMERS = 512, WS_THREADS = 768;
+
+// Workgroup barrier of the consumer waves: their LDS reads (MFMA fragments) completed.
+__device__ __forceinline__ void consumer_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int BKIND, int FMT>
+struct WSProducer {
+  static constexpr bool KN = BKIND == B_QKN;
+  // vector-memory loads of one B slab per producer thread (two K-major loaders, or one row)
+  static constexpr int LOADS = KN ? 2 * kn_fetch_loads<FMT>() : LQuantRow<FMT>::LOADS;
+  using BTile = typename std::conditional<KN, LTileKN, LTile>::type;
+  DecodeTables &tb;
+  ATile &A0, &A1;
+  BBuf &B0, &B1;
+  __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
+  LDirectAN<4> la;
+  int v, p;  // producer wave (0..3) and thread (0..255)
+  LQuantRow<FMT> nk[3];    // NK ring: slab t in nk[t % 3]
+  LQuantKN<FMT> kn[3][2];  // KN ring: two K-major loaders (virtual threads p, p + 256)
+
+  __device__ __forceinline__ WSProducer(DecodeTables &tb_, ATile &a0, ATile &a1, BBuf &b0, BBuf &b1,
+                                        const GroupedArgs &g)
+      : tb(tb_), A0(a0), A1(a1), B0(b0), B1(b1),
+        ra(make_rsrc(g.A, g.a_bytes)),
+        rc(make_rsrc(g.q.codes, g.q.codes_bytes)),
+        rs(make_rsrc(g.q.scale, g.q.scale_bytes)),
+        rs2(make_rsrc(g.q.scale2, g.q.scale2_bytes)),
+        v((int)(threadIdx.x - WS_CONSUMERS) >> 6),
+        p((int)threadIdx.x - WS_CONSUMERS) {}
+
+  template <int P>
+  __device__ __forceinline__ ATile &atile() {
+    if constexpr (P == 0) return A0;
+    else return A1;
+  }
+  template <int P>
+  __device__ __forceinline__ BTile &btile() {
+    BBuf &b = P == 0 ? B0 : B1;
+    if constexpr (KN) return b.kn;
+    else return b.nk;
+  }
+  __device__ __forceinline__ static uint32_t dead(int slab, int nmain) { return slab < nmain ? 0u : OOB; }
+  template <int Q>
+  __device__ __forceinline__ void fetch_b(int slab, int nmain) {
+    if constexpr (KN) {
+      kn[Q][0].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
+      kn[Q][1].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
+    } else {
+      nk[Q].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
+    }
+  }
+  template <int Q, int P>
+  __device__ __forceinline__ void decode() {
+    if constexpr (KN) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        kn[Q][h].prepare(tb);
+#pragma unroll
+        for (int part = 0; part < 4; ++part) kn[Q][h].store(btile<P>(), part, p + 256 * h);
+      }
+    } else {
+      nk[Q].decode_store(btile<P>(), tb, p);
+    }
+  }
+  __device__ __forceinline__ void issue_a(ATile &t, int slab, int nmain) {
+    la.issue(ra, t, (uint32_t)(slab * BK * 2) | dead(slab, nmain), v);
+  }
+  // iteration s: the A rows of slab s+1, the B codes of slab s+3, and the decode of slab s+1
+  // (codes loaded at iteration s-2) into buffers P = (s+1) % 2; Q = s % 3
+  template <int P, int Q>
+  __device__ __forceinline__ void body(int s, int nmain) {
+    issue_a(atile<P>(), s + 1, nmain);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_b<Q>(s + 3, nmain);
+    __builtin_amdgcn_sched_barrier(0);
+    decode<(Q + 1) % 3, P>();
+    slab_barrier<LOADS>();  // A rows of slab s+1 landed; only the B codes of slab s+3 in flight
+  }
+  __device__ __forceinline__ void run(const GroupedArgs &g, int e, int n0, const RowMap &map, int Nrows,
+                                      const TileM &tm, int nmain) {
+    la.init(v, tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
+    if constexpr (KN) {
+      kn[0][0].init(g.q, e, n0, g.N, p);
+      kn[0][1].init(g.q, e, n0, g.N, p + 256);
+      kn[1][0] = kn[2][0] = kn[0][0];
+      kn[1][1] = kn[2][1] = kn[0][1];
+    } else {
+      nk[0].init(g.q, e, map, Nrows, p);
+      nk[1] = nk[2] = nk[0];
+    }
+    issue_a(A0, 0, nmain);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_b<0>(0, nmain);
+    fetch_b<1>(1, nmain);
+    fetch_b<2>(2, nmain);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * LOADS>();  // A rows and B codes of slab 0
+    decode<0, 0>();
+    slab_barrier<2 * LOADS>();
+    for (int s = 0;; s += 6) {
+      body<1, 0>(s, nmain);
+      if (s + 1 >= nmain) break;
+      body<0, 1>(s + 1, nmain);
+      if (s + 2 >= nmain) break;
+      body<1, 2>(s + 2, nmain);
+      if (s + 3 >= nmain) break;
+      body<0, 0>(s + 3, nmain);
+      if (s + 4 >= nmain) break;
+      body<1, 1>(s + 4, nmain);
+      if (s + 5 >= nmain) break;
+      body<0, 2>(s + 5, nmain);
+      if (s + 6 >= nmain) break;
+    }
+    wait_vmcnt<0>();  // nothing in flight past the main loop
+  }
+};
+
+template <int BKIND, int EPI, bool SWIGLU, int FMT>
+__global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
+  __shared__ DecodeTables tb;
+  __shared__ ATile A0, A1;
+  __shared__ BBuf B0, B1;
+  __shared__ int tile_sh[4];
+  constexpr bool KN = BKIND == B_QKN;
+  init_decode_tables(tb, g.q);
+  TileM tm;
+  if (!find_tile(g.off, g.E, L_BM, blockIdx.y, tm, tile_sh)) return;
+  const int e = tm.e;
+  const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
+  const RowMap map{n0, g.I, SWIGLU};
+  const int Nrows = SWIGLU ? 2 * g.I : g.N;
+  const int nmain = g.K / BK;
+  if (threadIdx.x >= WS_CONSUMERS) {
+    WSProducer<BKIND, FMT> pr(tb, A0, A1, B0, B1, g);
+    pr.run(g, e, n0, map, Nrows, tm, nmain);
+    lora_barriers(g);
+    return;
+  }
+  LMma mma;
+  mma.zero();
+  auto bt = [&](BBuf &b) -> auto & {
+    if constexpr (KN) return b.kn;
+    else return b.nk;
+  };
+  consumer_barrier();  // slab 0
+  for (int s = 0;; s += 2) {
+    mma.step<KN>(A0, bt(B0), 4);
+    consumer_barrier();
+    if (s + 1 >= nmain) break;
+    mma.step<KN>(A1, bt(B1), 4);
+    consumer_barrier();
+    if (s + 2 >= nmain) break;
+  }
+  lora_extension(mma, g, tm, e, map, Nrows, A0, B0.nk);
+  large_epilogue<EPI>(mma, g, tm, n0);
+}
+
 template <int BKIND, int EPI, bool SWIGLU>
 static void launch_large(const GroupedArgs &a, dim3 grid, hipStream_t s) {
   if (a.Bx) {  // bf16 copy of the stack: no decode in the GEMM
@@ -625,9 +694,9 @@ static void launch_large(const GroupedArgs &a, dim3 grid, hipStream_t s) {
     return;
   }
   switch (a.q.fmt) {
-    case FMT_NF4: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_NF4><<<grid, L_THREADS, 0, s>>>(a); break;
-    case FMT_NF4_DQ: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_NF4_DQ><<<grid, L_THREADS, 0, s>>>(a); break;
-    default: gemm_large_kernel<BKIND, EPI, SWIGLU, FMT_MXFP4><<<grid, L_THREADS, 0, s>>>(a); break;
+    case FMT_NF4: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_NF4><<<grid, WS_THREADS, 0, s>>>(a); break;
+    case FMT_NF4_DQ: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_NF4_DQ><<<grid, WS_THREADS, 0, s>>>(a); break;
+    default: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_MXFP4><<<grid, WS_THREADS, 0, s>>>(a); break;
   }
 }
 
@@ -842,12 +911,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 bool launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t s) {
   if (T == 0) return true;
   if (E > 1024) return false;
+  LaunchScope ls(FAM_ROUTER, s);
   const dim3 grid(cdiv(T, 4));
   if (E <= 64) router_topk_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
   else if (E <= 128) router_topk_kernel<2><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
   else if (E <= 256) router_topk_kernel<4><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
   else router_topk_kernel<16><<<grid, 256, 0, s>>>(logits, T, E, k, ids, w);
-  return hipGetLastError() == hipSuccess;
+  return last_launch_ok();
 }
 
 // d_logit[ids[t, j]] = w_j (dw_j - sum_i w_i dw_i), zero elsewhere: one wave per token.
@@ -882,8 +952,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float *__restrict
 bool launch_router_bwd(const float *w, const float *dw, const int32_t *ids, int T, int E, int k, float *dl,
                        hipStream_t s) {
   if (T == 0) return true;
+  LaunchScope ls(FAM_ROUTER, s);
   router_bwd_kernel<<<cdiv(T, 4), 256, 0, s>>>(w, dw, ids, T, E, k, dl);
-  return hipGetLastError() == hipSuccess;
+  return last_launch_ok();
 }
 
 bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int32_t *inv, const float *topw,
@@ -1116,7 +1187,7 @@ bool launch_quantize(int fmt, int64_t n, const float *w, uint8_t *codes, void *s
 __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *__restrict__ f32,
                                uint16_t *__restrict__ b16) {
   __shared__ DecodeTables tb;
-  init_decode_tables(tb);
+  init_decode_tables(tb, q);
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nwords) return;
@@ -1140,8 +1211,9 @@ __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *_
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t byte = (w >> (8 * j)) & 0xffu;
-      vals[2 * j] = kNF4[byte >> 4] * am;
-      vals[2 * j + 1] = kNF4[byte & 15u] * am;
+      const float2 cv = tb.cb2[byte];
+      vals[2 * j] = cv.x * am;
+      vals[2 * j + 1] = cv.y * am;
     }
   }
   if (f32) {
@@ -1159,8 +1231,8 @@ __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *_
 template <int FMT>
 __global__ __launch_bounds__(256) void expand_kernel(QStack q, int64_t nwords, uint16_t *__restrict__ out) {
   __shared__ DecodeTables tb;
-  if constexpr (FMT == FMT_NF4_DQ) {
-    init_decode_tables(tb);
+  if constexpr (FMT != FMT_MXFP4) {
+    init_decode_tables(tb, q);
     __syncthreads();
   }
   const int64_t w0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;

@@ -25,6 +25,7 @@ enum Family : int {
   FAM_DEQUANT,
   FAM_TRANSPOSE,
   FAM_EXPAND,
+  FAM_ROUTER,
   FAM_COUNT
 };
 const char *family_name(int f);

@@ -40,10 +40,10 @@ struct SmallTables {
 // Thread t of the 512 computes entry t / 2 once and writes 8 of its 16 pieces (16 bytes
 // each, copies 4p .. 4p+3).  In the k-th store lane t writes piece (k + t / 2 + 8 (t & 1))
 // mod 16: the 16 lanes of one store pass write 16 different pieces, so their banks differ.
-__device__ __forceinline__ void init_small_tables(SmallTables &t) {
+__device__ __forceinline__ void init_small_tables(SmallTables &t, const float *codebook) {
   static_assert(SM_THREADS == 512, "two threads per table entry");
   const uint32_t b = threadIdx.x >> 1;
-  const uint32_t v = pack_bf16x2(nf4_value(b >> 4), nf4_value(b & 15));
+  const uint32_t v = pack_bf16x2(code_value(codebook, b >> 4), code_value(codebook, b & 15));
   const uint32_t p0 = b + 8 * (threadIdx.x & 1);
 #pragma unroll
   for (uint32_t k = 0; k < 8; ++k) *(u32x4 *)&t.cp[b][4 * ((p0 + k) & 15)] = u32x4{v, v, v, v};
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   __shared__ __attribute__((aligned(16))) WithTable<NF4ISH, Rest> sm;
   SmallTables &tb = table_of(sm);
   SmallX &xs = sm.rest.xs;
-  if constexpr (NF4ISH) init_small_tables(tb);
+  if constexpr (NF4ISH) init_small_tables(tb, g.q.codebook);
   TileM tm;
   if (!find_tile_wave(g.off, g.E, SM_BMT, blockIdx.y, tm)) return;  // the same for every wave
   const int e = tm.e;
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     } else if constexpr (FMT == FMT_NF4_DQ) {
       const uint32_t code = byte_at(cs[slot][s].raw, cs[slot][s].sh + b);
       const bool second = ((blk0[s] + c * SM_CB + b) >> 8) != ((blk0[s] + c * SM_CB) >> 8);
-      return ((float)code / 255.0f) * (second ? cs[slot][s].s2b : cs[slot][s].s2a);
+      return dq_value(g.q.dq_table, code) * (second ? cs[slot][s].s2b : cs[slot][s].s2a);
     } else {
       return e8m0_to_f32(byte_at(cs[slot][s].raw, cs[slot][s].sh + 2 * b));
     }
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       } else if constexpr (FMT == FMT_NF4_DQ) {
         const uint32_t code = byte_at(q.raw, q.sh + b);
         const bool second = ((blk0 + j) >> 8) != ((blk0 + j - b) >> 8);
-        return ((float)code / 255.0f) * (second ? q.s2b : q.s2a);
+        return dq_value(g.q.dq_table, code) * (second ? q.s2b : q.s2a);
       } else {
         return e8m0_to_f32(byte_at(q.raw, q.sh + 2 * b));
       }
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       load_blk(d, d);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NF4ISH) init_small_tables(tb);
+    if constexpr (NF4ISH) init_small_tables(tb, g.q.codebook);
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int i = threadIdx.x + u * SM_THREADS;

@@ -12,7 +12,7 @@ import dataclasses
 import torch
 
 from . import _lib
-from ._lib import FMT, E4B_EXPAND, E4B_NO_EXPAND, E4B_TRAIN, check
+from ._lib import FMT, E4B_EXPAND, E4B_TRAIN, check
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -23,6 +23,22 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     if not t.is_contiguous():
         raise ValueError("contiguous tensor expected")
     return t.data_ptr()
+
+
+def _arg(t, name: str, dtype: torch.dtype, shape: tuple, device: torch.device) -> torch.Tensor:
+    """Check one tensor argument before its pointer goes to the library: a wrong dtype,
+    shape or device would make the kernels read or write outside the allocation."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: tensor expected")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: {dtype} expected, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(shape)} expected, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: tensor on {device} expected, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: contiguous tensor expected")
+    return t
 
 
 def _stream() -> int:
@@ -39,10 +55,15 @@ class QStack:
     codes: torch.Tensor          # uint8 [E*N*K/2]
     scale: torch.Tensor          # fp32 / uint8
     scale2: torch.Tensor | None  # fp32 (NF4_DQ)
+    dq_table: torch.Tensor | None = None  # fp32 [256] (NF4_DQ; None = built-in c / 255)
+    codebook: torch.Tensor | None = None  # fp32 [16] (NF4 formats; None = built-in NF4 table)
 
     def c(self) -> _lib.QWeight:
+        for name, t, n in (("dq_table", self.dq_table, 256), ("codebook", self.codebook, 16)):
+            if t is not None and (t.dtype != torch.float32 or t.numel() != n):
+                raise ValueError(f"{name}: float32 tensor of {n} values expected")
         return _lib.QWeight(FMT[self.fmt], self.E, self.N, self.K, _ptr(self.codes), _ptr(self.scale),
-                            _ptr(self.scale2))
+                            _ptr(self.scale2), _ptr(self.dq_table), _ptr(self.codebook))
 
     @staticmethod
     def empty(fmt: str, E: int, N: int, K: int, device="cuda") -> "QStack":
@@ -60,9 +81,10 @@ class QStack:
         return QStack(fmt, E, N, K, codes, scale, scale2)
 
     @staticmethod
-    def from_host(fmt: str, E: int, N: int, K: int, codes, scale, scale2=None, device="cuda") -> "QStack":
+    def from_host(fmt: str, E: int, N: int, K: int, codes, scale, scale2=None, device="cuda",
+                  dq_table=None, codebook=None) -> "QStack":
         t = lambda a: None if a is None else torch.from_numpy(a).to(device)
-        return QStack(fmt, E, N, K, t(codes), t(scale), t(scale2))
+        return QStack(fmt, E, N, K, t(codes), t(scale), t(scale2), t(dq_table), t(codebook))
 
     @staticmethod
     def quantize(fmt: str, w: torch.Tensor) -> "QStack":
@@ -107,6 +129,7 @@ def route(ids: torch.Tensor, E: int):
     T, k = ids.shape
     M = T * k
     dev = ids.device
+    _arg(ids, "ids", torch.int32, (T, k), dev)
     cnt = torch.empty(E + 1, dtype=torch.int32, device=dev)
     off = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(max(M, 1), dtype=torch.int32, device=dev)
@@ -120,8 +143,8 @@ def route(ids: torch.Tensor, E: int):
 def router_topk(logits: torch.Tensor, k: int):
     """Top-k expert ids [T, k] (larger logit first, ties to the lower id) and the softmax
     weights over them [T, k], from fp32 logits [T, E]."""
-    logits = logits.contiguous()
     T, E = logits.shape
+    _arg(logits, "logits", torch.float32, (T, E), logits.device)
     ids = torch.empty(max(T, 1), k, dtype=torch.int32, device=logits.device)
     w = torch.empty(max(T, 1), k, dtype=torch.float32, device=logits.device)
     check(_lib.lib().e4b_router_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream()), "e4b_router_topk")
@@ -131,31 +154,50 @@ def router_topk(logits: torch.Tensor, k: int):
 def router_bwd(topw: torch.Tensor, d_topw: torch.Tensor, ids: torch.Tensor, E: int) -> torch.Tensor:
     """d logits [T, E] from d topw [T, k], the chosen ids held fixed."""
     T, k = topw.shape
-    out = torch.empty(max(T, 1), E, dtype=torch.float32, device=topw.device)
-    check(_lib.lib().e4b_router_bwd(_ptr(topw.contiguous()), _ptr(d_topw.contiguous()), _ptr(ids.contiguous()), T, E,
-                                    k, _ptr(out), _stream()), "e4b_router_bwd")
+    dev = topw.device
+    _arg(topw, "topw", torch.float32, (T, k), dev)
+    _arg(d_topw, "d_topw", torch.float32, (T, k), dev)
+    _arg(ids, "ids", torch.int32, (T, k), dev)
+    out = torch.empty(max(T, 1), E, dtype=torch.float32, device=dev)
+    check(_lib.lib().e4b_router_bwd(_ptr(topw), _ptr(d_topw), _ptr(ids), T, E, k, _ptr(out), _stream()),
+          "e4b_router_bwd")
     return out[:T]
 
 
 class MoELayer:
     """One routed-expert layer: frozen stacks w_gu [E, 2I, H], w_dn [E, H, I] plus
     optional adapters on each.  Owns its workspace (caller-side allocation).
-    expand: None lets the library choose between decoding the stacks inside the GEMM
-    tiles and streaming bf16 copies of them (large batches); True / False force it."""
+    expand=True asks the forward of a large batch to stream bf16 copies of the stacks
+    (written into the workspace) instead of decoding them inside the GEMM tiles."""
 
     def __init__(self, w_gu: QStack, w_dn: QStack, l_gu: LoRA | None, l_dn: LoRA | None,
                  T: int, topk: int, train: bool = True, expand: bool | None = None):
         self.w_gu, self.w_dn, self.l_gu, self.l_dn = w_gu, w_dn, l_gu, l_dn
         self.E, self.H, self.I = w_gu.E, w_gu.K, w_dn.K
+        dev = w_gu.codes.device
+        E, H, I = self.E, self.H, self.I
+        for name, q, N, K in (("w_gu", w_gu, 2 * I, H), ("w_dn", w_dn, H, I)):
+            if (q.E, q.N, q.K) != (E, N, K):
+                raise ValueError(f"{name}: stack [{E}, {N}, {K}] expected, got [{q.E}, {q.N}, {q.K}]")
+            n = E * N * K
+            _arg(q.codes, f"{name}.codes", torch.uint8, (n // 2,), dev)
+            nscale = n // 32 if q.fmt == "mxfp4" else n // 64
+            _arg(q.scale, f"{name}.scale", torch.float32 if q.fmt == "nf4" else torch.uint8, (nscale,), dev)
+            if q.fmt == "nf4_dq":
+                _arg(q.scale2, f"{name}.scale2", torch.float32, ((n // 64 + 255) // 256,), dev)
+        for name, l, N, K in (("l_gu", l_gu, 2 * I, H), ("l_dn", l_dn, H, I)):
+            if l is not None:
+                _arg(l.A, f"{name}.A", torch.bfloat16, (E, l.r, K), dev)
+                _arg(l.B, f"{name}.B", torch.bfloat16, (E, N, l.r), dev)
         self.T, self.topk = T, topk
-        self.flags = (E4B_TRAIN if train else 0) | (
-            0 if expand is None else E4B_EXPAND if expand else E4B_NO_EXPAND)
+        self.flags = (E4B_TRAIN if train else 0) | (E4B_EXPAND if expand else 0)
         self.desc = _lib.Desc(self.E, self.H, self.I, T, topk, self.flags)
         n = ctypes.c_size_t()
         check(_lib.lib().e4b_moe_workspace_size(ctypes.byref(self.desc), _lora_c(l_gu), _lora_c(l_dn),
                                                 ctypes.byref(n)), "e4b_moe_workspace_size")
         self.ws_bytes = n.value
-        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=w_gu.codes.device)
+        self.device = w_gu.codes.device
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=self.device)
         self._qgu, self._qdn = w_gu.c(), w_dn.c()
         self._lgu = l_gu.c() if l_gu is not None else None
         self._ldn = l_dn.c() if l_dn is not None else None
@@ -163,9 +205,17 @@ class MoELayer:
     def _l(self, x):
         return ctypes.byref(x) if x is not None else None
 
+    def _routing(self, ids, topw):
+        _arg(ids, "ids", torch.int32, (self.T, self.topk), self.device)
+        _arg(topw, "topw", torch.float32, (self.T, self.topk), self.device)
+
     def forward(self, x, ids, topw, y=None):
+        rows = (self.T, self.H)
+        _arg(x, "x", torch.bfloat16, rows, self.device)
+        self._routing(ids, topw)
         if y is None:
-            y = torch.empty(self.T, self.H, dtype=torch.bfloat16, device=x.device)
+            y = torch.empty(rows, dtype=torch.bfloat16, device=self.device)
+        _arg(y, "y", torch.bfloat16, rows, self.device)
         check(_lib.lib().e4b_moe_fwd(ctypes.byref(self.desc), ctypes.byref(self._qgu),
                                      ctypes.byref(self._qdn), self._l(self._lgu), self._l(self._ldn),
                                      _ptr(x), _ptr(ids), _ptr(topw), _ptr(y), _ptr(self.ws),
@@ -173,10 +223,16 @@ class MoELayer:
         return y
 
     def dgrad(self, ids, topw, dy, dx=None, d_topw=None, want_d_topw=True):
+        rows = (self.T, self.H)
+        _arg(dy, "dy", torch.bfloat16, rows, self.device)
+        self._routing(ids, topw)
         if dx is None:
-            dx = torch.empty(self.T, self.H, dtype=torch.bfloat16, device=dy.device)
+            dx = torch.empty(rows, dtype=torch.bfloat16, device=self.device)
+        _arg(dx, "dx", torch.bfloat16, rows, self.device)
         if d_topw is None and want_d_topw:
-            d_topw = torch.empty(self.T, self.topk, dtype=torch.float32, device=dy.device)
+            d_topw = torch.empty(self.T, self.topk, dtype=torch.float32, device=self.device)
+        if d_topw is not None:
+            _arg(d_topw, "d_topw", torch.float32, (self.T, self.topk), self.device)
         check(_lib.lib().e4b_moe_dgrad(ctypes.byref(self.desc), ctypes.byref(self._qgu),
                                        ctypes.byref(self._qdn), self._l(self._lgu), self._l(self._ldn),
                                        _ptr(ids), _ptr(topw), _ptr(dy), _ptr(dx), _ptr(d_topw),
@@ -184,8 +240,9 @@ class MoELayer:
         return dx, d_topw
 
     def wgrad(self, x, out=None):
-        dev = x.device
+        dev = self.device
         E, H, I = self.E, self.H, self.I
+        _arg(x, "x", torch.bfloat16, (self.T, H), dev)
         if out is None:
             out = {}
             if self.l_gu is not None:
@@ -196,6 +253,13 @@ class MoELayer:
                 r = self.l_dn.r
                 out["dA_dn"] = torch.empty(E, r, I, dtype=torch.float32, device=dev)
                 out["dB_dn"] = torch.empty(E, H, r, dtype=torch.float32, device=dev)
+        shapes = {}
+        if self.l_gu is not None:
+            shapes.update(dA_gu=(E, self.l_gu.r, H), dB_gu=(E, 2 * I, self.l_gu.r))
+        if self.l_dn is not None:
+            shapes.update(dA_dn=(E, self.l_dn.r, I), dB_dn=(E, H, self.l_dn.r))
+        for k, shp in shapes.items():
+            _arg(out.get(k), k, torch.float32, shp, dev)
         check(_lib.lib().e4b_lora_wgrad(ctypes.byref(self.desc), self._l(self._lgu), self._l(self._ldn),
                                         _ptr(x), _ptr(self.ws), self.ws_bytes, _ptr(out.get("dA_gu")),
                                         _ptr(out.get("dB_gu")), _ptr(out.get("dA_dn")),

@@ -56,16 +56,28 @@ typedef enum {
  *          per 32 consecutive elements along K: w = e2m1[q] * 2^(X - 127). */
 typedef enum { E4B_FMT_NF4 = 0, E4B_FMT_NF4_DQ = 1, E4B_FMT_MXFP4 = 2 } e4b_fmt;
 
-/* A frozen stack [E, N, K] (K contiguous) in one of the formats above.
- *  codes : uint8 [E, N, K/2]
- *  scale : NF4: float [E, N, K/64]; NF4_DQ: uint8 [E, N, K/64]; MXFP4: uint8 [E, N, K/32]
- *  scale2: NF4_DQ only: float [ceil(E*N*K/64 / 256)]; NULL otherwise. */
+/* A frozen stack [E, N, K] (K contiguous) in one of the formats above: the packed codes
+ * plus per-block scales that the method page ("The abstraction that fails, and what
+ * replaces it") names as the frozen packed base.  All pointers are device pointers owned
+ * by the caller.
+ *  codes   : uint8 [E, N, K/2]
+ *  scale   : NF4: float [E, N, K/64]; NF4_DQ: uint8 [E, N, K/64]; MXFP4: uint8 [E, N, K/32]
+ *  scale2  : NF4_DQ only: float [ceil(E*N*K/64 / 256)]; NULL otherwise.
+ *  dq_table: NF4_DQ only: float [256], the value of each 8-bit absmax code:
+ *            absmax = fp32(dq_table[c] * scale2[b / 256]).  NULL = the built-in linear
+ *            code fp32(c / 255).  Must be NULL for the other formats.
+ *  codebook: NF4 and NF4_DQ: float [16], the value of each 4-bit code,
+ *            w = bf16(fp32(codebook[q] * absmax)).  NULL = the built-in NormalFloat
+ *            table.  Must be NULL for MXFP4 (its E2M1 values are fixed by the format).
+ * A non-NULL table for a format that has none is E4B_ERR_INVALID_ARG. */
 typedef struct {
   int32_t fmt;
   int32_t E, N, K;
   const uint8_t *codes;
   const void *scale;
   const float *scale2;
+  const float *dq_table;
+  const float *codebook;
 } e4b_qweight;
 
 /* Stacked per-expert adapter of one projection [E, N, K]:
@@ -79,14 +91,13 @@ typedef struct {
 } e4b_lora;
 
 #define E4B_TRAIN 1u /* forward keeps what dgrad and wgrad read, in the workspace */
-/* The 4-bit GEMMs of a call with more than 256 routed rows either decode the stacks
- * inside the GEMM tiles, once per 256-row tile, or -- by default when there are at
- * least 1024 routed rows per expert on average -- first write bf16 copies of both
- * stacks into the workspace (decoded by the same rules; 2 bytes per weight, kept from a
- * training forward for its dgrad) and stream those.  Results are bit-identical either
- * way.  These flags force the choice (not both; ignored at 256 rows or fewer). */
+/* The 4-bit GEMMs decode the packed stacks inside the GEMM tiles (README, "The package
+ * family"), in the forward and again in the dgrad, so no dequantised copy of the base is
+ * held between the calls (method page, "Why it happens").  E4B_EXPAND asks a forward with
+ * more than 256 routed rows to first write bf16 copies of both stacks into the workspace
+ * (2 bytes per weight; workspace_size grows accordingly) and stream those instead; the
+ * results are bit-identical, and the dgrad still decodes the packed stacks. */
 #define E4B_EXPAND 2u
-#define E4B_NO_EXPAND 4u
 
 typedef struct {
   int32_t E, H, I, T, topk;
@@ -178,6 +189,7 @@ typedef struct {
   int64_t route, lora_a, gemm_gate_up, gemm_down, combine;
   int64_t combine_bwd, gemm_down_dgrad, gemm_gate_up_dgrad, unpermute, wgrad, quant, dequant;
   int64_t expand;    /* bf16 copies of stacks written by large-batch calls */
+  int64_t router;    /* e4b_router_topk and e4b_router_bwd launches */
   int64_t fallbacks; /* always 0: there is no slower path to fall back to */
 } e4b_stats;
 e4b_status e4b_get_stats(e4b_stats *out);

@@ -37,7 +37,7 @@ def build(force: bool = True) -> str:
 class _QW(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("scale2", ctypes.c_void_p)]
+                ("scale2", ctypes.c_void_p), ("dq_table", ctypes.c_void_p), ("codebook", ctypes.c_void_p)]
 
 
 class _Layer(ctypes.Structure):
@@ -86,15 +86,27 @@ def bf16_round(a: np.ndarray) -> np.ndarray:
 
 
 class QWeight:
-    """A quantised stack [E, N, K] (K contiguous) in one of the three formats."""
+    """A quantised stack [E, N, K] (K contiguous) in one of the three formats.  dq_table
+    (fp32 [256], NF4_DQ) and codebook (fp32 [16], NF4 formats) replace the built-in code
+    tables when given."""
 
-    def __init__(self, fmt: str, E: int, N: int, K: int, codes, scale, scale2=None):
+    def __init__(self, fmt: str, E: int, N: int, K: int, codes, scale, scale2=None, dq_table=None,
+                 codebook=None):
         self.fmt, self.E, self.N, self.K = fmt, E, N, K
         self.codes, self.scale, self.scale2 = codes, scale, scale2
+        self.dq_table = None if dq_table is None else np.ascontiguousarray(dq_table, np.float32)
+        self.codebook = None if codebook is None else np.ascontiguousarray(codebook, np.float32)
+        assert self.dq_table is None or self.dq_table.shape == (256,)
+        assert self.codebook is None or self.codebook.shape == (16,)
+
+    def with_tables(self, dq_table=None, codebook=None) -> "QWeight":
+        """The same bytes read through other code tables."""
+        return QWeight(self.fmt, self.E, self.N, self.K, self.codes, self.scale, self.scale2,
+                       dq_table, codebook)
 
     def struct(self) -> _QW:
         return _QW(_FMT[self.fmt], self.E, self.N, self.K, _p(self.codes), _p(self.scale),
-                   _p(self.scale2))
+                   _p(self.scale2), _p(self.dq_table), _p(self.codebook))
 
 
 def quantize(fmt: str, w: np.ndarray) -> QWeight:
@@ -132,7 +144,7 @@ def dequant(q: QWeight, want_f32: bool = True, want_bf16: bool = True):
     f32 = np.zeros(n, np.float32) if want_f32 else None
     b16 = np.zeros(n, np.uint16) if want_bf16 else None
     lib().orc_dequant(ctypes.c_int32(_FMT[q.fmt]), ctypes.c_int64(n), _p(q.codes), _p(q.scale),
-                      _p(q.scale2), _p(f32), _p(b16))
+                      _p(q.scale2), _p(q.dq_table), _p(q.codebook), _p(f32), _p(b16))
     shp = (q.E, q.N, q.K)
     return (None if f32 is None else f32.reshape(shp)), (None if b16 is None else b16.reshape(shp))
 

@@ -23,7 +23,10 @@
  *    in the high nibble; nearest code with ties to the lower index; zero block ->
  *    code 7 and absmax 0.  Dequant = one fp32 multiply fp32(code) * absmax.
  *  - Double quantisation: absmax codes c = rne(255 * absmax/scale2) per group of
- *    256 blocks, scale2 = group max; absmax' = fp32(c/255) * scale2.
+ *    256 blocks, scale2 = group max; absmax' = fp32(c/255) * scale2.  A stack may
+ *    carry its own 8-bit code table instead (absmax' = fp32(table[c] * scale2), e.g.
+ *    QLoRA's dynamic 8-bit code) and its own sixteen 4-bit code values; the
+ *    quantisers always target the built-in tables.
  *  - MXFP4: E2M1 elements (element 2j in the low nibble), one E8M0 scale per 32
  *    elements along the reduction axis, scale exponent floor(log2(amax)) - 2.
  *  - scaling s = alpha / r; gate = rows [0, I) of gate_up, up = rows [I, 2I).
@@ -171,7 +174,7 @@ void orc_quant_mxfp4(const float *w, int64_t n, uint8_t *codes, uint8_t *scales)
 /* ------------------------------------------------------------------- dequant */
 
 static float deq_one(int32_t fmt, int64_t i, const uint8_t *codes, const void *scale,
-                     const float *scale2) {
+                     const float *scale2, const float *dq_table, const float *codebook) {
   uint8_t byte = codes[i >> 1];
   if (fmt == ORC_FMT_MXFP4) {
     uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);
@@ -186,17 +189,20 @@ static float deq_one(int32_t fmt, int64_t i, const uint8_t *codes, const void *s
   if (fmt == ORC_FMT_NF4) {
     amax = ((const float *)scale)[b];
   } else {
-    float t = (float)((const uint8_t *)scale)[b] / 255.0f;
+    uint8_t qa = ((const uint8_t *)scale)[b];
+    float t = dq_table ? dq_table[qa] : (float)qa / 255.0f;
     amax = t * scale2[b / 256];
   }
-  return NF4[c] * amax;
+  float v = codebook ? codebook[c] : NF4[c];
+  return v * amax;
 }
 
 void orc_dequant(int32_t fmt, int64_t n, const uint8_t *codes, const void *scale,
-                 const float *scale2, float *out_f32, uint16_t *out_bf16) {
+                 const float *scale2, const float *dq_table, const float *codebook,
+                 float *out_f32, uint16_t *out_bf16) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
-    float v = deq_one(fmt, i, codes, scale, scale2);
+    float v = deq_one(fmt, i, codes, scale, scale2, dq_table, codebook);
     if (out_f32) out_f32[i] = v;
     if (out_bf16) out_bf16[i] = bf16_rne(v);
   }
@@ -338,7 +344,8 @@ static const float *expert_weights_any(const float *dense, const orc_qweight *q,
   if (dense) return dense + (int64_t)e * per;
   int64_t base = (int64_t)e * per;
 #pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < per; ++i) buf[i] = deq_one(q->fmt, base + i, q->codes, q->scale, q->scale2);
+  for (int64_t i = 0; i < per; ++i)
+    buf[i] = deq_one(q->fmt, base + i, q->codes, q->scale, q->scale2, q->dq_table, q->codebook);
   return buf;
 }
 

@@ -32,6 +32,8 @@ typedef struct {
   const uint8_t *codes;   /* [E*N*K/2] */
   const void *scale;      /* NF4: float[E*N*K/64]; NF4_DQ: uint8[E*N*K/64]; MXFP4: uint8[E*N*K/32] */
   const float *scale2;    /* NF4_DQ: float[ceil(E*N*K/64/256)]; else unused */
+  const float *dq_table;  /* NF4_DQ: value of each 8-bit absmax code [256]; NULL = c/255 */
+  const float *codebook;  /* NF4 formats: value of each 4-bit code [16]; NULL = NormalFloat */
 } orc_qweight;
 
 /* The layer: weights either packed (w_gu/w_dn) or dense fp32 (W1f/W2f, for
@@ -59,9 +61,11 @@ void orc_bf16_round(const float *in, uint16_t *out, int64_t n);
 void orc_quant_nf4(const float *w, int64_t n, uint8_t *codes, float *absmax);
 void orc_quant_nf4_dq(const float *w, int64_t n, uint8_t *codes, uint8_t *qabsmax, float *scale2);
 void orc_quant_mxfp4(const float *w, int64_t n, uint8_t *codes, uint8_t *scales);
-/* Dequantise n elements (flat) to fp32 and/or bf16 (either pointer may be NULL). */
+/* Dequantise n elements (flat) to fp32 and/or bf16 (either pointer may be NULL).
+ * dq_table / codebook: the stack's own code tables (NULL = the built-in ones). */
 void orc_dequant(int32_t fmt, int64_t n, const uint8_t *codes, const void *scale,
-                 const float *scale2, float *out_f32, uint16_t *out_bf16);
+                 const float *scale2, const float *dq_table, const float *codebook,
+                 float *out_f32, uint16_t *out_bf16);
 
 void orc_route(int32_t T, int32_t k, int32_t E, const int32_t *ids,
                int32_t *cnt, int32_t *off, int32_t *perm, int32_t *inv);

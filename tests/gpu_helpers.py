@@ -49,14 +49,20 @@ def assert_close(gpu, ref, name: str):
 class Case:
     """One layer call: host inputs, oracle-quantised stacks, and device copies."""
 
-    def __init__(self, inp: synth.LayerInputs, lora: bool = True, train: bool = True, expand=None):
+    def __init__(self, inp: synth.LayerInputs, lora: bool = True, train: bool = True, expand=None,
+                 dq_table=None, codebook=None):
+        """dq_table / codebook (fp32 numpy arrays): the stacks' own code tables, read by
+        both sides in place of the built-in ones (the bytes are quantised against the
+        built-in tables either way)."""
         s = inp.shape
         self.inp, self.s = inp, s
-        self.q1 = oracle.quantize(s.fmt, inp.W1)
-        self.q2 = oracle.quantize(s.fmt, inp.W2)
+        self.q1 = oracle.quantize(s.fmt, inp.W1).with_tables(dq_table, codebook)
+        self.q2 = oracle.quantize(s.fmt, inp.W2).with_tables(dq_table, codebook)
         dev = "cuda"
-        self.w_gu = QStack.from_host(s.fmt, s.E, 2 * s.I, s.H, self.q1.codes, self.q1.scale, self.q1.scale2)
-        self.w_dn = QStack.from_host(s.fmt, s.E, s.H, s.I, self.q2.codes, self.q2.scale, self.q2.scale2)
+        self.w_gu = QStack.from_host(s.fmt, s.E, 2 * s.I, s.H, self.q1.codes, self.q1.scale, self.q1.scale2,
+                                     dq_table=dq_table, codebook=codebook)
+        self.w_dn = QStack.from_host(s.fmt, s.E, s.H, s.I, self.q2.codes, self.q2.scale, self.q2.scale2,
+                                     dq_table=dq_table, codebook=codebook)
         b16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         self.l_gu = LoRA(b16(inp.A1), b16(inp.B1), s.scaling) if lora else None
         self.l_dn = LoRA(b16(inp.A2), b16(inp.B2), s.scaling) if lora else None

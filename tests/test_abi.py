@@ -63,22 +63,20 @@ def test_workspace_size_valid(L):
 
 
 def test_expanded_stacks_workspace(L):
-    """Large calls (more than 256 routed rows) reserve the bf16 copies of both stacks:
-    E*2I*H + E*H*I bf16 values, by default from 1024 routed rows per expert on average or
-    when forced; calls of at most 256 rows never do."""
+    """Large calls (more than 256 routed rows) reserve bf16 copies of both stacks (E*2I*H +
+    E*H*I bf16 values) only when the caller asks for them with E4B_EXPAND; by default the
+    stacks are decoded inside the GEMM tiles and no copy exists.  Calls of at most 256 rows
+    never expand."""
     E, H, I = 4, 128, 256
     copies = 2 * (E * 2 * I * H + E * H * I)
-    TRAIN, EXPAND, NO_EXPAND = 1, 2, 4
-    _, big_default = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN))      # 1024 rows/expert
-    _, big_off = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN | NO_EXPAND))
-    assert big_default - big_off >= copies
-    _, mid_default = _ws(L, _desc(L, E=E, H=H, I=I, T=1024, k=2, flags=TRAIN))      # 512 rows/expert
-    _, mid_forced = _ws(L, _desc(L, E=E, H=H, I=I, T=1024, k=2, flags=TRAIN | EXPAND))
-    assert mid_forced - mid_default >= copies
+    TRAIN, EXPAND = 1, 2
+    _, big_default = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN))
+    _, big_forced = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN | EXPAND))
+    assert big_forced - big_default >= copies
     _, small_default = _ws(L, _desc(L, E=E, H=H, I=I, T=128, k=2, flags=TRAIN))     # 256 rows
     _, small_forced = _ws(L, _desc(L, E=E, H=H, I=I, T=128, k=2, flags=TRAIN | EXPAND))
     assert small_forced == small_default
-    st, _ = _ws(L, _desc(L, flags=TRAIN | EXPAND | NO_EXPAND))
+    st, _ = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN | 4))  # unknown flag bit
     assert st == L.E4B_ERR_INVALID_ARG
 
 
@@ -176,3 +174,42 @@ def test_no_cpu_fallback_in_product():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle.h" not in text and "liboracle" not in text, f
+
+
+def test_layer_argument_checks_cpu():
+    """The Python layer checks dtype, shape and device of every tensor before its pointer
+    reaches the library (a wrong dtype or a short tensor would make a kernel read or write
+    past the allocation)."""
+    import torch
+
+    from grouped_nf4_gemm_amd.layer import _arg
+
+    dev = torch.device("cpu")
+    ok = torch.zeros(4, 2, dtype=torch.int32)
+    assert _arg(ok, "ids", torch.int32, (4, 2), dev) is ok
+    with pytest.raises(ValueError, match="int32"):
+        _arg(ok.to(torch.int64), "ids", torch.int32, (4, 2), dev)  # torch.topk's default dtype
+    with pytest.raises(ValueError, match="shape"):
+        _arg(ok[:3], "ids", torch.int32, (4, 2), dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        _arg(torch.zeros(2, 4, dtype=torch.int32).t(), "ids", torch.int32, (4, 2), dev)
+    with pytest.raises(ValueError, match="tensor"):
+        _arg(None, "x", torch.bfloat16, (4, 2), dev)
+
+
+def test_code_table_rejections(L):
+    """A code table that the format has no use for is refused before any launch: an absmax
+    table on a plain NF4 or MXFP4 stack, a 4-bit codebook on an MXFP4 stack."""
+    lib = L.lib()
+    L.reset_stats()
+    cases = [L.QWeight(0, 1, 8, 64, 0x1, 0x2, None, 0x3, None),        # NF4 + dq_table
+             L.QWeight(2, 1, 8, 64, 0x1, 0x2, None, 0x3, None),        # MXFP4 + dq_table
+             L.QWeight(2, 1, 8, 64, 0x1, 0x2, None, None, 0x4)]        # MXFP4 + codebook
+    for q in cases:
+        assert lib.e4b_dequant(ctypes.byref(q), 0, 0x10, None, None) == L.E4B_ERR_INVALID_ARG
+    ok = L.QWeight(1, 1, 8, 64, 0x1, 0x2, 0x5, 0x3, 0x4)               # NF4_DQ + both tables
+    d = L.Desc(1, 64, 64, 0, 1, 0)
+    n = ctypes.c_size_t()
+    assert lib.e4b_moe_workspace_size(ctypes.byref(d), None, None, ctypes.byref(n)) == 0
+    assert L.get_stats()["launches_total"] == 0
+    del ok

@@ -65,6 +65,58 @@ def test_dequant_every_code(fmt):
     assert np.array_equal(b16.view(torch.int16).cpu().numpy().view(np.uint16), b_ref.reshape(N, K))
 
 
+def _tables(seed):
+    """A signed, non-linear 8-bit absmax code and a permuted 4-bit codebook."""
+    c = np.arange(256, dtype=np.float64)
+    dq = (np.sign(c - 127.5) * ((c - 127.5) / 128.0) ** 2).astype(np.float32)
+    cb = oracle.codebook()[np.random.default_rng(seed).permutation(16)].copy()
+    return dq, cb
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq"])
+def test_dequant_stack_tables(fmt):
+    """The stack's own code tables replace the built-in ones bit for bit: every code
+    byte, a non-linear signed absmax code (NF4_DQ) and a permuted codebook."""
+    E, N, K = 2, 64, 512
+    rng = np.random.default_rng(8)
+    codes = np.tile(np.arange(256, dtype=np.uint8), E * N * K // 2 // 256)
+    dq, cb = _tables(9)
+    if fmt == "nf4":
+        q = oracle.QWeight(fmt, E, N, K, codes, rng.uniform(0, 3, E * N * K // 64).astype(np.float32),
+                           codebook=cb)
+    else:
+        q = oracle.QWeight(fmt, E, N, K, codes, rng.integers(0, 256, E * N * K // 64).astype(np.uint8),
+                           rng.uniform(0.01, 2, (E * N * K // 64 + 255) // 256).astype(np.float32),
+                           dq_table=dq, codebook=cb)
+    f_ref, b_ref = oracle.dequant(q)
+    d = QStack.from_host(fmt, E, N, K, q.codes, q.scale, q.scale2, dq_table=q.dq_table, codebook=q.codebook)
+    f32, b16 = d.dequant(-1)
+    assert np.array_equal(f32.cpu().numpy().view(np.uint32), f_ref.reshape(E * N, K).view(np.uint32))
+    assert np.array_equal(b16.view(torch.int16).cpu().numpy().view(np.uint16), b_ref.reshape(E * N, K))
+
+
+@pytest.mark.parametrize("T", [24, 150])
+def test_layer_stack_tables(T):
+    """The layer over NF4_DQ stacks read through their own tables (few routed rows: the
+    weight-streaming kernels; many: the large tiles) matches the oracle reading the same
+    tables, and differs from the built-in reading."""
+    from tests.gpu_helpers import Case, assert_close, bf16_to_np
+
+    s = synth.custom(4, 192, 320, T, 2, 16, 32.0, "nf4_dq", name=f"tables-t{T}")
+    inp = synth.make_inputs(s, seed=300 + T)
+    dq, cb = _tables(10)
+    case = Case(inp, dq_table=dq, codebook=cb)
+    out = case.run()
+    L = case.oracle_layer()
+    y_ref = oracle.moe_fwd(L)
+    g = oracle.moe_bwd(L, inp.dy)
+    assert_close(bf16_to_np(out["y"]), y_ref, "y")
+    assert_close(bf16_to_np(out["dx"]), g["dx"], "dx")
+    assert_close(out["dA_gu"].cpu().numpy(), g["dA1"], "dA_gu")
+    plain = Case(inp).run(dgrad=False)
+    assert not torch.equal(plain["y"], out["y"])
+
+
 @pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
 def test_quantize_bitexact(fmt):
     E, N, K = 3, 80, 2880

@@ -242,3 +242,27 @@ def test_decode_forward_graph_replay(T):
         assert torch.equal(y.view(torch.int16), ref.view(torch.int16))
     del graph
     _check_all(case, {"y": ref})
+
+
+def test_layer_rejects_bad_arguments():
+    """Tensors of the wrong dtype, shape or device are refused before any launch: int64 ids
+    (torch.topk's default) would be read as pairs of int32, and a short or fp32 x would be
+    read past its end."""
+    inp = synth.make_inputs(synth.custom(4, 64, 64, 16, 2, 8, 16.0), seed=3)
+    case = Case(inp)
+    lay = case.layer
+    reset_stats()
+    bad = [
+        lambda: lay.forward(case.x, case.ids.long(), case.topw),
+        lambda: lay.forward(case.x.float(), case.ids, case.topw),
+        lambda: lay.forward(case.x[:8].contiguous(), case.ids, case.topw),
+        lambda: lay.forward(case.x.cpu(), case.ids, case.topw),
+        lambda: lay.forward(case.x, case.ids, case.topw.double()),
+        lambda: lay.forward(case.x, case.ids, case.topw, y=torch.empty(8, 64, dtype=torch.bfloat16, device="cuda")),
+        lambda: lay.dgrad(case.ids, case.topw, case.dy[:, :32].contiguous()),
+        lambda: lay.wgrad(case.x.t().contiguous().t()),
+    ]
+    for f in bad:
+        with pytest.raises(ValueError):
+            f()
+    assert get_stats()["launches_total"] == 0

@@ -136,6 +136,50 @@ def test_nf4_dq_scheme(orc):
     assert np.array_equal(f32.ravel().view(np.uint32), want.view(np.uint32))
 
 
+def test_stack_code_tables_reduce_to_builtin(orc):
+    """A stack may carry its own code tables.  Passing the built-in values explicitly
+    changes no bit; a 4-bit codebook permuted by p, read through codes relabelled by the
+    inverse of p, decodes to the same weights; an absmax table scaled by 2 (exact in
+    fp32) doubles every weight exactly."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((2, 32, 256)) * 0.02).astype(np.float32)
+    q = orc.quantize("nf4_dq", w)
+    base_f, base_b = orc.dequant(q)
+    cb = np.loadtxt(os.path.join(GOLD, "nf4_codebook.txt")).astype(np.float32)
+    lin = (np.arange(256, dtype=np.float32) / np.float32(255.0)).astype(np.float32)
+    f, b = orc.dequant(q.with_tables(dq_table=lin, codebook=cb))
+    assert np.array_equal(f.view(np.uint32), base_f.view(np.uint32))
+    assert np.array_equal(b, base_b)
+    perm = rng.permutation(16)
+    inv = np.argsort(perm)  # perm[inv[c]] = c
+    hi, lo = inv[q.codes >> 4], inv[q.codes & 15]
+    relabelled = ((hi << 4) | lo).astype(np.uint8)
+    qp = orc.QWeight("nf4_dq", q.E, q.N, q.K, relabelled, q.scale, q.scale2, codebook=cb[perm])
+    f, _ = orc.dequant(qp)
+    assert np.array_equal(f.view(np.uint32), base_f.view(np.uint32))
+    f, _ = orc.dequant(q.with_tables(dq_table=(2 * lin).astype(np.float32)))
+    assert np.array_equal(f, 2 * base_f)
+
+
+def test_dq_table_reduces_to_plain_nf4(orc):
+    """A double-quantised stack read through any absmax table equals the plain NF4 stack
+    whose fp32 absmax of block b is fp32(table[c_b] * scale2[b / 256]): the table only
+    changes how the absmax is rebuilt (here a signed, non-linear 8-bit code)."""
+    rng = np.random.default_rng(12)
+    w = (rng.standard_normal((1, 48, 640)) * 0.02).astype(np.float32)  # 480 blocks: 2 groups
+    q = orc.quantize("nf4_dq", w)
+    c = np.arange(256, dtype=np.float64)
+    table = (np.sign(c - 127.5) * ((c - 127.5) / 128.0) ** 2).astype(np.float32)
+    s2 = np.repeat(q.scale2, 256)[: q.scale.size]
+    amax = (table[q.scale] * s2).astype(np.float32)
+    plain = orc.QWeight("nf4", q.E, q.N, q.K, q.codes, amax)
+    want_f, want_b = orc.dequant(plain)
+    got_f, got_b = orc.dequant(q.with_tables(dq_table=table))
+    assert np.array_equal(got_f.view(np.uint32), want_f.view(np.uint32))
+    assert np.array_equal(got_b, want_b)
+    assert np.any(got_f < 0) and not np.array_equal(got_f, orc.dequant(q)[0])
+
+
 # ----------------------------------------------------------------------------- MXFP4
 
 E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
