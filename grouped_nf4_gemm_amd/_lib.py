@@ -20,7 +20,9 @@ EXPORTS = [
     "e4b_version", "e4b_status_str", "e4b_moe_workspace_size", "e4b_moe_fwd", "e4b_moe_dgrad",
     "e4b_lora_wgrad", "e4b_moe_route", "e4b_dequant", "e4b_quantize", "e4b_moe_check",
     "e4b_get_stats", "e4b_reset_stats", "e4b_timing_enable", "e4b_timing_read",
-    "e4b_router_topk", "e4b_router_bwd",]
+    "e4b_router_topk", "e4b_router_bwd", "e4b_moe_fwd_noalloc",
+]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class E4BError(RuntimeError):
@@ -71,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.e4b_moe_fwd.restype = i32
         L.e4b_moe_fwd.argtypes = [P(Desc), P(QWeight), P(QWeight), P(Lora), P(Lora), vp, vp, vp, vp,
                                   vp, sz, vp]
+        L.e4b_moe_fwd_noalloc.restype = i32
+        L.e4b_moe_fwd_noalloc.argtypes = [P(Desc), P(QWeight), P(QWeight), P(Lora), P(Lora), vp, vp, vp, vp, vp]
         L.e4b_moe_dgrad.restype = i32
         L.e4b_moe_dgrad.argtypes = [P(Desc), P(QWeight), P(QWeight), P(Lora), P(Lora), vp, vp, vp, vp,
                                     vp, vp, sz, vp]

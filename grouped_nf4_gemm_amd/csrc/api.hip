@@ -22,7 +22,9 @@ struct TimedLaunch {
   int fam;
 };
 static std::vector<TimedLaunch> g_pending;
-
+// Set on the calling thread for the duration of an allocation-free call: its launches are
+// counted but not bracketed by events (creating events is left to calls that may allocate).
+static thread_local bool t_noalloc = false;
 static int64_t g_tl[FAM_COUNT];
 static double g_tms[FAM_COUNT];
 
@@ -38,7 +40,7 @@ const char *family_name(int f) {
 LaunchScope::LaunchScope(int f, hipStream_t st) : fam(f), s(st), slot(-1) {
   g_count[f]++;
   g_total++;
-  if (g_timing) {
+  if (g_timing && !t_noalloc) {
     TimedLaunch t{};
     t.fam = f;
     if (hipEventCreate(&t.a) == hipSuccess && hipEventCreate(&t.b) == hipSuccess &&
@@ -349,6 +351,47 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const 
                        const int32_t *ids, const float *topw, uint16_t *y, void *ws,
                        size_t ws_bytes, void *stream) {
   return moe_fwd(desc, w_gu, w_dn, l_gu, l_dn, x, ids, topw, y, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ allocation-free forward
+// One device-resident scratch array per GPU takes the place of the caller's workspace.  In
+// host code the array's name is not a device address: its address on a device is looked up
+// once, with that device current (hipGetSymbolAddress), kept in g_scratch, and only that
+// address is handed to the kernels.
+static __device__ __align__(256) unsigned char scratch[E4B_NOALLOC_SCRATCH_BYTES];
+static constexpr int MAX_DEVICES = 64;
+static void *g_scratch[MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+static e4b_status scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return E4B_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return E4B_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return E4B_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return E4B_OK;
+}
+
+e4b_status e4b_moe_fwd_noalloc(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
+                               const e4b_lora *l_gu, const e4b_lora *l_dn, const uint16_t *x,
+                               const int32_t *ids, const float *topw, uint16_t *y, void *stream) {
+  int r1, r2;
+  E4B_TRY(validate_layer(desc, w_gu, w_dn, l_gu, l_dn, &r1, &r2));
+  if (desc->flags != 0) return E4B_ERR_INVALID_ARG;  // inference only, no bf16 stack copies
+  if (layout(*desc, r1, r2).total > (size_t)E4B_NOALLOC_SCRATCH_BYTES) return E4B_ERR_WORKSPACE;
+  if (desc->T > 0 && (!x || !ids || !topw || !y)) return E4B_ERR_INVALID_ARG;
+  void *ws = nullptr;
+  E4B_TRY(scratch_of_current_device(&ws));
+  t_noalloc = true;
+  const e4b_status st = moe_fwd(desc, w_gu, w_dn, l_gu, l_dn, x, ids, topw, y, ws,
+                                (size_t)E4B_NOALLOC_SCRATCH_BYTES, stream);
+  t_noalloc = false;
+  return st;
 }
 
 e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,

@@ -222,6 +222,19 @@ class MoELayer:
                                      self.ws_bytes, _stream()), "e4b_moe_fwd")
         return y
 
+    def forward_noalloc(self, x, ids, topw, y):
+        """The forward through e4b_moe_fwd_noalloc: the library's per-GPU scratch array in place
+        of this layer's workspace (inference layers only; y is caller-allocated)."""
+        rows = (self.T, self.H)
+        _arg(x, "x", torch.bfloat16, rows, self.device)
+        self._routing(ids, topw)
+        _arg(y, "y", torch.bfloat16, rows, self.device)
+        check(_lib.lib().e4b_moe_fwd_noalloc(ctypes.byref(self.desc), ctypes.byref(self._qgu),
+                                             ctypes.byref(self._qdn), self._l(self._lgu), self._l(self._ldn),
+                                             _ptr(x), _ptr(ids), _ptr(topw), _ptr(y), _stream()),
+              "e4b_moe_fwd_noalloc")
+        return y
+
     def dgrad(self, ids, topw, dy, dx=None, d_topw=None, want_d_topw=True):
         rows = (self.T, self.H)
         _arg(dy, "dy", torch.bfloat16, rows, self.device)

@@ -124,6 +124,21 @@ e4b_status e4b_moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu,
                        const uint16_t *x, const int32_t *ids, const float *topw, uint16_t *y,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* Allocation-free forward, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The same forward as
+ * e4b_moe_fwd, inference only (desc->flags must be 0), with its workspace taken from one
+ * device-resident scratch array of E4B_NOALLOC_SCRATCH_BYTES per GPU (held from the first
+ * call on a device until the process ends) instead of a caller buffer.  Layers whose
+ * e4b_moe_workspace_size exceeds it get E4B_ERR_WORKSPACE before any launch.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (different streams, or other
+ * threads) race; calls ordered on one stream do not.  Nothing in the array needs to start at
+ * zero.  The call itself allocates nothing (event timing is skipped for it). */
+#define E4B_NOALLOC_SCRATCH_BYTES (64u << 20)
+e4b_status e4b_moe_fwd_noalloc(const e4b_moe_desc *desc, const e4b_qweight *w_gu,
+                               const e4b_qweight *w_dn, const e4b_lora *l_gu, const e4b_lora *l_dn,
+                               const uint16_t *x, const int32_t *ids, const float *topw, uint16_t *y,
+                               void *stream);
+
 /* Input gradient after a training forward with the same arguments.
  *  dy bf16 [T, H] -> dx bf16 [T, H] (overwritten); d_topw fp32 [T, topk]
  *  (nullable; d(sum dy*y)/d topw).  Writes the dgrad activations that
