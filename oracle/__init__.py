@@ -50,7 +50,8 @@ class _Layer(ctypes.Structure):
                 ("A2", ctypes.c_void_p), ("B2", ctypes.c_void_p), ("r2", ctypes.c_int32),
                 ("s2", ctypes.c_double),
                 ("x", ctypes.c_void_p), ("ids", ctypes.c_void_p), ("topw", ctypes.c_void_p),
-                ("post_act_delta", ctypes.c_int32)]
+                ("post_act_delta", ctypes.c_int32), ("act", ctypes.c_int32), ("alpha", ctypes.c_double),
+                ("limit", ctypes.c_double), ("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
 
 
 _lib = None
@@ -186,7 +187,11 @@ class Layer:
     """Arguments of one layer call, kept alive for the C side."""
 
     def __init__(self, E, H, I, T, k, x, ids, topw, w_gu=None, w_dn=None, W1f=None, W2f=None,
-                 A1=None, B1=None, s1=0.0, A2=None, B2=None, s2=0.0, post_act_delta=False):
+                 A1=None, B1=None, s1=0.0, A2=None, B2=None, s2=0.0, post_act_delta=False,
+                 act=None):
+        """act: None for the stock act(gate) * up, or a dict {alpha, limit, b1, b2} for the
+        clamped GLU over interleaved gate/up rows (b1 bf16 [E, 2I], b2 bf16 [E, H], each
+        nullable)."""
         self.keep = []
 
         def arr(a, dt):
@@ -204,6 +209,8 @@ class Layer:
         self.A2, self.B2 = arr(A2, np.uint16), arr(B2, np.uint16)
         self.r1 = 0 if A1 is None else self.A1.shape[1]
         self.r2 = 0 if A2 is None else self.A2.shape[1]
+        a = act or {}
+        self.b1, self.b2 = arr(a.get("b1"), np.uint16), arr(a.get("b2"), np.uint16)
         self.qgu = w_gu.struct() if w_gu is not None else None
         self.qdn = w_dn.struct() if w_dn is not None else None
         self.keep += [w_gu, w_dn]
@@ -212,18 +219,20 @@ class Layer:
                         ctypes.pointer(self.qdn) if self.qdn else None,
                         _p(self.W1f), _p(self.W2f), _p(self.A1), _p(self.B1), self.r1, float(s1),
                         _p(self.A2), _p(self.B2), self.r2, float(s2),
-                        _p(self.x), _p(self.ids), _p(self.topw), int(post_act_delta))
+                        _p(self.x), _p(self.ids), _p(self.topw), int(post_act_delta),
+                        1 if act else 0, float(a.get("alpha", 0.0)), float(a.get("limit", 0.0)),
+                        _p(self.b1), _p(self.b2))
         self.E, self.H, self.I, self.T, self.k = E, H, I, T, k
 
 
-def layer_from_inputs(inp, w_gu=None, w_dn=None, dense=False, lora=True, post_act_delta=False):
+def layer_from_inputs(inp, w_gu=None, w_dn=None, dense=False, lora=True, post_act_delta=False, act=None):
     s = inp.shape
     return Layer(s.E, s.H, s.I, s.T, s.k, inp.x, inp.ids, inp.topw,
                  w_gu=w_gu, w_dn=w_dn,
                  W1f=inp.W1 if dense else None, W2f=inp.W2 if dense else None,
                  A1=inp.A1 if lora else None, B1=inp.B1 if lora else None, s1=s.scaling,
                  A2=inp.A2 if lora else None, B2=inp.B2 if lora else None, s2=s.scaling,
-                 post_act_delta=post_act_delta)
+                 post_act_delta=post_act_delta, act=act)
 
 
 def _mask(L: Layer, tokens):

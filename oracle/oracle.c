@@ -30,6 +30,13 @@
  *  - MXFP4: E2M1 elements (element 2j in the low nibble), one E8M0 scale per 32
  *    elements along the reduction axis, scale exponent floor(log2(amax)) - 2.
  *  - scaling s = alpha / r; gate = rows [0, I) of gate_up, up = rows [I, 2I).
+ *  - gpt-oss experts (README "Scope": MXFP4 experts with per-expert biases and a
+ *    clamped GLU; project record "limitations": the faithful clamped GLU and biases):
+ *    the pages give no formula, so the reading is that model family's published expert
+ *    function: gate/up interleaved by row (2i, 2i+1), biases added before the clamp,
+ *    gate clamped from above and up from both sides at `limit`, h = (up + 1) * gate *
+ *    sigmoid(alpha * gate), down bias added after the down projection.  The LoRA delta
+ *    enters before the activation as for the stock epilogue; the biases are frozen.
  *  - Routing grouped by expert, stable in the flat index t*k + j.
  *
  * Precision: weights dequantise exactly per the fp32 contract; everything after
@@ -241,6 +248,7 @@ void orc_route(int32_t T, int32_t k, int32_t E, const int32_t *ids,
 typedef struct {
   const float *W1, *W2; /* this expert, dense fp32: [2I, H], [H, I] */
   const uint16_t *A1, *B1, *A2, *B2;
+  const uint16_t *b1, *b2; /* this expert's biases [2I], [H] (clamped GLU only; nullable) */
 } expert_view;
 
 /* Router (the frozen router of the method page, "Which project solves it": top-k expert
@@ -285,6 +293,18 @@ void orc_router_bwd(int32_t T, int32_t E, int32_t k, const float *w, const float
 static double silu(double g) { return g / (1.0 + exp(-g)); }
 static double sigm(double g) { return 1.0 / (1.0 + exp(-g)); }
 
+/* Clamped GLU (act == 1): h and its partial derivatives at (gate, up).  The clamps pass the
+ * gradient where the argument lies inside the closed interval. */
+static double cglu(const orc_layer *L, double g, double u, double *dh_dg, double *dh_du) {
+  const double gc = g < L->limit ? g : L->limit;
+  const double uc = u < -L->limit ? -L->limit : (u > L->limit ? L->limit : u);
+  const double sg = sigm(L->alpha * gc);
+  if (dh_dg) *dh_dg = g <= L->limit ? (uc + 1.0) * (sg + L->alpha * gc * sg * (1.0 - sg)) : 0.0;
+  if (dh_du) *dh_du = (u >= -L->limit && u <= L->limit) ? gc * sg : 0.0;
+  return (uc + 1.0) * gc * sg;
+}
+static double bias_of(const uint16_t *b, int64_t i) { return b ? bf16_to_double(b[i]) : 0.0; }
+
 /* Forward of one routed row.  Fills z1[r1], gu[2I], hh[I], z2[r2], o[H]. */
 static void row_forward(const orc_layer *L, const expert_view *X, const double *x,
                         double *z1, double *gu, double *hh, double *z2, double *o) {
@@ -304,10 +324,13 @@ static void row_forward(const orc_layer *L, const expert_view *X, const double *
     double d = 0.0;
     for (int j = 0; j < r1 && lora1; ++j) d += bf16_to_double(X->B1[(int64_t)n * r1 + j]) * z1[j];
     gu[n] = L->post_act_delta ? acc : acc + L->s1 * d; /* planted variant re-adds it below */
+    if (L->act == 1) gu[n] += bias_of(X->b1, n);
   }
-  /* h = silu(gate) * up */
+  /* h = silu(gate) * up, or the clamped GLU over interleaved rows */
   for (int i = 0; i < I; ++i) {
-    if (!L->post_act_delta) {
+    if (L->act == 1) {
+      hh[i] = cglu(L, gu[2 * i], gu[2 * i + 1], NULL, NULL);
+    } else if (!L->post_act_delta) {
       hh[i] = silu(gu[i]) * gu[I + i];
     } else {
       /* planted variant: act(W x) + d on the activated half */
@@ -333,6 +356,7 @@ static void row_forward(const orc_layer *L, const expert_view *X, const double *
     double d = 0.0;
     for (int j = 0; j < r2 && lora2; ++j) d += bf16_to_double(X->B2[(int64_t)n * r2 + j]) * z2[j];
     o[n] = acc + L->s2 * d;
+    if (L->act == 1) o[n] += bias_of(X->b2, n);
   }
 }
 
@@ -357,6 +381,8 @@ static expert_view make_view(const orc_layer *L, int e, const float *W1, const f
   v.B1 = L->A1 ? L->B1 + (int64_t)e * 2 * L->I * L->r1 : NULL;
   v.A2 = L->A2 ? L->A2 + (int64_t)e * L->r2 * L->I : NULL;
   v.B2 = L->A2 ? L->B2 + (int64_t)e * L->H * L->r2 : NULL;
+  v.b1 = L->b1 ? L->b1 + (int64_t)e * 2 * L->I : NULL;
+  v.b2 = L->b2 ? L->b2 + (int64_t)e * L->H : NULL;
   return v;
 }
 
@@ -490,11 +516,18 @@ int32_t orc_moe_bwd(const orc_layer *L, const uint8_t *tok_mask, const uint16_t 
         }
         for (int j = 0; j < R2 && lora2; ++j)
           for (int i = 0; i < I; ++i) dhh[i] += bf16_to_double(V.A2[(int64_t)j * I + i]) * dz2[j];
-        /* SwiGLU backward */
+        /* activation backward */
         for (int i = 0; i < I; ++i) {
-          double g = gu[i], u = gu[I + i], sg = sigm(g);
-          dgu[i] = dhh[i] * u * sg * (1.0 + g * (1.0 - sg));
-          dgu[I + i] = dhh[i] * silu(g);
+          if (L->act == 1) {
+            double dg, du;
+            (void)cglu(L, gu[2 * i], gu[2 * i + 1], &dg, &du);
+            dgu[2 * i] = dhh[i] * dg;
+            dgu[2 * i + 1] = dhh[i] * du;
+          } else {
+            double g = gu[i], u = gu[I + i], sg = sigm(g);
+            dgu[i] = dhh[i] * u * sg * (1.0 + g * (1.0 - sg));
+            dgu[I + i] = dhh[i] * silu(g);
+          }
         }
         /* gate_up: u1 = B1^T dgu, dz1 = s1 u1, dx_row = W1^T dgu + A1^T dz1 */
         for (int j = 0; j < R1 && lora1; ++j) {

@@ -52,6 +52,14 @@ typedef struct {
   const int32_t *ids;       /* [T, k] */
   const float *topw;        /* [T, k] */
   int32_t post_act_delta;   /* test hook: 1 = act(Wx) + delta instead of act(Wx + delta) */
+  /* Expert activation.  0: stock act(gate) * up with gate rows [0, I), up rows [I, 2I).
+   * 1: the clamped GLU of gpt-oss's experts: gate = row 2i, up = row 2i+1 (interleaved),
+   *    g' = min(gate, limit), u' = clamp(up, -limit, limit), h = (u' + 1) * g' * sigmoid(alpha g'),
+   *    with per-expert biases b1 [E, 2I] (added before the activation, with the LoRA delta)
+   *    and b2 [E, H] (added to the down projection); bf16, either may be NULL. */
+  int32_t act;
+  double alpha, limit;
+  const uint16_t *b1, *b2;
 } orc_layer;
 
 int32_t orc_version(void);

@@ -553,3 +553,133 @@ def test_router_bwd_finite_differences(orc):
     mask = np.ones((T, E), bool)
     np.put_along_axis(mask, ids.astype(np.int64), False, axis=1)
     assert np.all(got[mask] == 0)
+
+
+# ----------------------------------------------------------------------------- clamped GLU (gpt-oss experts)
+
+def _glu_case(seed, limit=1e30, alpha=2.0, gate_bias=0.0, up_bias=0.0, b2=True, T=10):
+    inp = _small(E=3, H=64, I=64, T=T, k=2, r=4, alpha=8.0, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    s = inp.shape
+    b1 = rng.normal(0, 0.05, (s.E, 2 * s.I)).astype(np.float32)
+    b1[:, 0::2] += np.float32(gate_bias)
+    b1[:, 1::2] += np.float32(up_bias)
+    act = dict(alpha=alpha, limit=limit, b1=synth.to_bf16_bits(b1),
+               b2=synth.to_bf16_bits(rng.normal(0, 0.05, (s.E, s.H)).astype(np.float32)) if b2 else None)
+    return inp, act
+
+
+def test_clamped_glu_reduces_to_stock_swiglu(orc):
+    """With the clamp out of reach, the clamped GLU over interleaved rows equals the stock
+    SwiGLU layer after a change of variables: de-interleave the rows, carry the gate_up
+    biases and the +1 on up in one extra constant input feature, and absorb alpha by scaling
+    the gate rows by alpha and the up rows by 1/alpha (exact for alpha = 2).  Gradients map
+    back by the same change of variables."""
+    inp, act = _glu_case(31, b2=False)
+    s = inp.shape
+    E, H, I, a = s.E, s.H, s.I, act["alpha"]
+    Lg = orc.layer_from_inputs(inp, dense=True, act=act)
+    y_g = orc.moe_fwd(Lg)
+    g_g = orc.moe_bwd(Lg, inp.dy)
+    H2 = H + 1
+    one = synth.to_bf16_bits(np.float32([1.0]))[0]
+    x2 = np.zeros((s.T, H2), np.uint16)
+    x2[:, :H] = inp.x
+    x2[:, H] = one
+    b1 = synth.bf16_bits_to_f32(act["b1"])
+    W1 = inp.W1
+    W1s = np.zeros((E, 2 * I, H2), np.float32)
+    W1s[:, :I, :H] = a * W1[:, 0::2, :]
+    W1s[:, I:, :H] = W1[:, 1::2, :] / np.float32(a)
+    W1s[:, :I, H] = a * b1[:, 0::2]
+    W1s[:, I:, H] = (b1[:, 1::2] + np.float32(1.0)) / np.float32(a)  # exact in fp32
+    A1s = np.zeros((E, s.r, H2), np.uint16)
+    A1s[:, :, :H] = inp.A1
+    B1 = synth.bf16_bits_to_f32(inp.B1)
+    B1s = synth.to_bf16_bits(np.concatenate([a * B1[:, 0::2, :], B1[:, 1::2, :] / np.float32(a)], axis=1))
+    W2s = np.zeros((E, H2, I), np.float32)
+    W2s[:, :H] = inp.W2
+    B2s = np.zeros((E, H2, s.r), np.uint16)
+    B2s[:, :H] = inp.B2
+    Ls = orc.Layer(E, H2, I, s.T, s.k, x2, inp.ids, inp.topw, W1f=W1s, W2f=W2s, A1=A1s, B1=B1s,
+                   s1=s.scaling, A2=inp.A2, B2=B2s, s2=s.scaling)
+    y_s = orc.moe_fwd(Ls)
+    assert np.allclose(y_s[:, :H], y_g, rtol=1e-9, atol=1e-12 * np.abs(y_g).max())
+    assert np.all(y_s[:, H] == 0)
+    dy2 = np.zeros((s.T, H2), np.uint16)
+    dy2[:, :H] = inp.dy
+    g_s = orc.moe_bwd(Ls, dy2)
+    close = lambda u, v: np.allclose(u, v, rtol=1e-8, atol=1e-11 * np.abs(v).max())
+    assert close(g_s["dx"][:, :H], g_g["dx"])
+    assert close(g_s["dw"], g_g["dw"])
+    assert close(g_s["dA1"][:, :, :H], g_g["dA1"])
+    assert close(a * g_s["dB1"][:, :I], g_g["dB1"][:, 0::2])
+    assert close(g_s["dB1"][:, I:] / a, g_g["dB1"][:, 1::2])
+    assert close(g_s["dA2"], g_g["dA2"]) and close(g_s["dB2"][:, :H], g_g["dB2"])
+
+
+def test_clamped_glu_clamp_out_of_reach_is_bitwise_unclamped(orc):
+    inp, act = _glu_case(32, limit=1e30)
+    L1 = orc.layer_from_inputs(inp, dense=True, act=act)
+    L2 = orc.layer_from_inputs(inp, dense=True, act=dict(act, limit=40.0))
+    assert np.array_equal(orc.moe_fwd(L1), orc.moe_fwd(L2))
+    g1, g2 = orc.moe_bwd(L1, inp.dy), orc.moe_bwd(L2, inp.dy)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("half", ["gate", "up"])
+def test_clamped_glu_saturates(orc, half):
+    """Pre-activations beyond the limit (a bias of 60 against a limit of 7): the output no
+    longer depends on that half's weights (doubling them changes no bit) and its LoRA-B
+    gradient rows are exactly zero."""
+    inp, act = _glu_case(33, limit=7.0, gate_bias=60.0 if half == "gate" else 0.0,
+                         up_bias=60.0 if half == "up" else 0.0)
+    rows = slice(0, None, 2) if half == "gate" else slice(1, None, 2)
+    L1 = orc.layer_from_inputs(inp, dense=True, act=act)
+    y1 = orc.moe_fwd(L1)
+    g1 = orc.moe_bwd(L1, inp.dy)
+    assert np.all(g1["dB1"][:, rows] == 0) and np.abs(g1["dB1"]).max() > 0
+    inp.W1[:, rows, :] *= 2.0
+    y2 = orc.moe_fwd(orc.layer_from_inputs(inp, dense=True, act=act))
+    assert np.array_equal(y1, y2)
+
+
+def test_clamped_glu_down_bias_is_additive(orc):
+    """The down bias adds sum_j w[t,j] * b2[ids[t,j]] to y."""
+    inp, act = _glu_case(34)
+    y_b = orc.moe_fwd(orc.layer_from_inputs(inp, dense=True, act=act))
+    y_0 = orc.moe_fwd(orc.layer_from_inputs(inp, dense=True, act=dict(act, b2=None)))
+    b2 = synth.bf16_bits_to_f32(act["b2"]).astype(np.float64)
+    want = np.einsum("tj,tjh->th", inp.topw.astype(np.float64), b2[inp.ids])
+    assert np.allclose(y_b - y_0, want, rtol=1e-12, atol=1e-15)
+
+
+def test_clamped_glu_backward_finite_differences(orc):
+    """Central one-ulp differences of the loss, with a limit that clamps part of the gates and
+    ups (alpha = 1.702, limit 0.6)."""
+    inp, act = _glu_case(35, limit=0.6, alpha=1.702, T=6)
+    inp.W1 *= 5.0
+    dy64 = _f64(inp.dy)
+    g = orc.moe_bwd(orc.layer_from_inputs(inp, dense=True, act=act), inp.dy)
+
+    def loss():
+        return float((orc.moe_fwd(orc.layer_from_inputs(inp, dense=True, act=act)) * dy64).sum())
+
+    def central(arr, idx):
+        keep = arr[idx]
+        up, dn, step = _bf16_neighbours(keep)
+        arr[idx] = up
+        lp = loss()
+        arr[idx] = dn
+        lm = loss()
+        arr[idx] = keep
+        return (lp - lm) / step
+
+    scale = {k: np.abs(v).max() for k, v in g.items() if v is not None}
+    for idx in [(0, 3), (4, 10), (5, 63)]:
+        assert abs(central(inp.x, idx) - g["dx"][idx]) <= 2e-3 * scale["dx"]
+    for idx in [(0, 1, 5), (1, 3, 60)]:
+        assert abs(central(inp.A1, idx) - g["dA1"][idx]) <= 2e-3 * scale["dA1"]
+    for idx in [(0, 6, 2), (1, 101, 0), (0, 71, 3)]:
+        assert abs(central(inp.B1, idx) - g["dB1"][idx]) <= 2e-3 * scale["dB1"]
