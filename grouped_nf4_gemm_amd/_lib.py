@@ -42,9 +42,18 @@ class Lora(ctypes.Structure):
                 ("scaling", ctypes.c_float)]
 
 
+ACT = {"swiglu": 0, "clamped_glu": 1}
+
+
+class Act(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("alpha", ctypes.c_float), ("limit", ctypes.c_float),
+                ("b_gu", ctypes.c_void_p), ("b_dn", ctypes.c_void_p)]
+
+
 class Desc(ctypes.Structure):
     _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
-                ("T", ctypes.c_int32), ("topk", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("T", ctypes.c_int32), ("topk", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("act", ctypes.POINTER(Act))]
 
 
 class Stats(ctypes.Structure):

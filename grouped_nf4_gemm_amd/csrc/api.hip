@@ -3,6 +3,7 @@
 // sequences, and the verification / observability exports.
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -161,7 +162,26 @@ static e4b_status check_desc(const e4b_moe_desc *d) {
   if ((int64_t)d->T * d->H * 2 > BUF_LIMIT || M * d->H * 4 > BUF_LIMIT || M * 2 * d->I * 2 > BUF_LIMIT)
     return E4B_ERR_INVALID_ARG;
   if (d->flags & ~(E4B_TRAIN | E4B_EXPAND)) return E4B_ERR_INVALID_ARG;
+  if (const e4b_act *a = d->act) {
+    if (a->kind == E4B_ACT_SWIGLU) {
+      if (a->b_gu || a->b_dn) return E4B_ERR_INVALID_ARG;  // the stock epilogue has no biases
+    } else if (a->kind == E4B_ACT_CLAMPED_GLU) {
+      if (!std::isfinite(a->alpha) || !std::isfinite(a->limit) || !(a->limit > 0.0f)) return E4B_ERR_INVALID_ARG;
+    } else {
+      return E4B_ERR_UNSUPPORTED;
+    }
+  }
   return E4B_OK;
+}
+
+// Activation of the gate_up epilogues, and the biases, into the GEMM arguments.
+static void set_act(const e4b_moe_desc &d, GroupedArgs &a, const uint16_t *bias, int64_t bias_estride) {
+  const e4b_act *act = d.act;
+  a.act = act && act->kind == E4B_ACT_CLAMPED_GLU ? 1 : 0;
+  a.glu_alpha = a.act ? act->alpha : 0.0f;
+  a.glu_limit = a.act ? act->limit : 0.0f;
+  a.bias = bias;
+  a.bias_estride = bias_estride;
 }
 
 static e4b_status check_lora(const e4b_lora *l, int *r) {
@@ -313,6 +333,7 @@ static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, con
     a.ldxb = r1; a.r = r1;
     a.C = h; a.ldc = I; a.alpha = 1.0f;
     a.Gout = G; a.ldg = 2 * I; a.I = I;
+    set_act(d, a, d.act ? d.act->b_gu : nullptr, (int64_t)2 * I);
     E4B_LAUNCH(small ? launch_small_gate_up(a, s) : launch_gemm_gate_up(a, s));
   }
   if (r2) {  // z2 = s2 * A2[e] h
@@ -335,6 +356,7 @@ static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, con
     a.xa = z2; a.ldxa = r2; a.xb = r2 ? l_dn->B : nullptr; a.xb_estride = (int64_t)H * r2;
     a.ldxb = r2; a.r = r2;
     a.C = O; a.ldc = H; a.alpha = 1.0f; a.I = I;
+    set_act(d, a, d.act ? d.act->b_dn : nullptr, H);
     if (small) {
       nsplit = train ? 1 : small_down_splits(M, E, H, I);
       E4B_LAUNCH(launch_small_down(a, nsplit, s));
@@ -442,6 +464,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     a.xa = u2; a.ldxa = r2; a.xb = r2 ? A2T : nullptr; a.xb_estride = (int64_t)I * r2;
     a.ldxb = r2; a.r = r2;
     a.Gin = G; a.Gout = dG; a.ldg = 2 * I; a.I = I;
+    set_act(d, a, nullptr, 0);
     E4B_LAUNCH(launch_gemm_down_dgrad(a, s));
   }
   if (r1) {

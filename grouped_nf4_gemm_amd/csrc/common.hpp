@@ -48,6 +48,27 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
 }
 
+// Weight row of h column c in the gate_up stack: the gate (up = false) or up row.  Stock
+// layout: gate rows [0, I), up rows [I, 2I); interleaved (clamped GLU): rows 2c and 2c + 1.
+__device__ __forceinline__ int gate_up_row(int c, bool up, bool interleaved, int I) {
+  return interleaved ? 2 * c + (up ? 1 : 0) : (up ? I : 0) + c;
+}
+
+// Clamped GLU (gpt-oss experts): h = (u' + 1) * g' * sigmoid(alpha g'), g' = min(g, limit),
+// u' = clamp(u, -limit, limit); its partial derivatives pass through the clamps inside the
+// closed interval.
+__device__ __forceinline__ float glu_clamped(float g, float u, float alpha, float limit) {
+  const float gc = fminf(g, limit), uc = fminf(fmaxf(u, -limit), limit);
+  return (uc + 1.0f) * gc * sigmoid_fast(alpha * gc);
+}
+__device__ __forceinline__ void glu_clamped_bwd(float g, float u, float alpha, float limit, float dh, float &dg,
+                                                float &du) {
+  const float gc = fminf(g, limit), uc = fminf(fmaxf(u, -limit), limit);
+  const float sg = sigmoid_fast(alpha * gc);
+  dg = g <= limit ? dh * (uc + 1.0f) * (sg + alpha * gc * sg * (1.0f - sg)) : 0.0f;
+  du = (u >= -limit && u <= limit) ? dh * gc * sg : 0.0f;
+}
+
 // Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v;

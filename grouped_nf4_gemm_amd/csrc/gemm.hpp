@@ -137,17 +137,18 @@ struct RowLoader {
 
 // ---------------------------------------------------------------- B row mapping
 // Tile row lr of the B operand -> output column (weight row) index.
-// Plain: n0 + lr.  SwiGLU: rows interleave 32 gate rows and 32 up rows so that a
+// Plain: n0 + lr.  Gate/up: tile rows alternate 32 gate rows and 32 up rows so that a
 // wave's two 32-column MFMA tiles hold gate and up of the same h column.
 struct RowMap {
   int n0, I;
   bool swiglu;
+  bool interleaved;  // gate/up rows interleaved (2c, 2c + 1) instead of halves
   // Returns a row past every bound when the tile row falls beyond the last h column.
   __device__ __forceinline__ int operator()(int lr) const {
     if (!swiglu) return n0 + lr;
     const int blk = lr >> 5, o = lr & 31;
     const int hcol = n0 + (blk >> 1) * 32 + o;
-    return hcol < I ? ((blk & 1) ? I : 0) + hcol : 0x7fffffff;
+    return hcol < I ? gate_up_row(hcol, blk & 1, interleaved, I) : 0x7fffffff;
   }
 };
 

@@ -402,7 +402,35 @@ __device__ __forceinline__ void large_epilogue(LMma &mma, const GroupedArgs &g, 
     const __amdgpu_buffer_rsrc_t rh = rows_rsrc(g.C, tm.row0, tm.rows, g.ldc, 2);
     const uint32_t hoff = col < g.I ? (uint32_t)((pr * g.ldc + pc) * 2) : OOB;
     const uint32_t hpitch = (uint32_t)(g.ldc * 2);
-    if (g.Gout) {
+    if (g.act == 1) {
+      // clamped GLU over interleaved rows: this lane's gate and up are stack rows 2 col and
+      // 2 col + 1, so the saved pre-activation keeps the stored order and each (gate, up)
+      // pair of a row is one 4-byte store (row rl + dr, no lane pairing)
+      float bg = 0.0f, bu = 0.0f;
+      if (g.bias && col < g.I) {
+        const uint16_t *b = g.bias + (int64_t)tm.e * g.bias_estride + 2 * col;
+        bg = bf2f(b[0]);
+        bu = bf2f(b[1]);
+      }
+      const __amdgpu_buffer_rsrc_t rg = rows_rsrc(g.Gout, tm.row0, tm.rows, g.ldg, 2);
+      const uint32_t goff = col < g.I ? (uint32_t)((rl * g.ldg + 2 * col) * 2) : OOB;
+      const uint32_t gpitch = (uint32_t)(g.ldg * 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+          const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
+          const float gt0 = mma.acc[i][0][v] + bg, up0 = mma.acc[i][1][v] + bu;
+          const float gt1 = mma.acc[i][0][v + 1] + bg, up1 = mma.acc[i][1][v + 1] + bu;
+          const float h0 = glu_clamped(gt0, up0, g.glu_alpha, g.glu_limit);
+          const float h1 = glu_clamped(gt1, up1, g.glu_alpha, g.glu_limit);
+          bstore32u(rh, pair_bf16(h0, h1, odd), hoff + dr * hpitch);
+          if (g.Gout) {
+            bstore32u(rg, pack_bf16x2(gt0, up0), goff + dr * gpitch);
+            bstore32u(rg, pack_bf16x2(gt1, up1), goff + (dr + 1) * gpitch);
+          }
+        }
+    } else if (g.Gout) {
       const __amdgpu_buffer_rsrc_t rg = rows_rsrc(g.Gout, tm.row0, tm.rows, g.ldg, 2);
       const uint32_t goff = col < g.I ? (uint32_t)((pr * g.ldg + pc) * 2) : OOB;
       const uint32_t gpitch = (uint32_t)(g.ldg * 2), uoff = (uint32_t)(g.I * 2);
@@ -439,12 +467,15 @@ __device__ __forceinline__ void large_epilogue(LMma &mma, const GroupedArgs &g, 
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + LMma::col_of(j);
       const uint32_t off = n < g.N ? (uint32_t)(((rl + (odd ? 1 : 0)) * g.ldc + (n & ~1)) * 4) : OOB;
+      // per-expert bias of this lane's column (clamped GLU experts' down projection)
+      const float bn = (g.bias && n < g.N) ? bf2f(g.bias[(int64_t)tm.e * g.bias_estride + n]) : 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           const uint32_t dr = (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3));
-          bstore_pair_f32(rc, g.alpha * mma.acc[i][j][v], g.alpha * mma.acc[i][j][v + 1], odd, off + dr * pitch);
+          bstore_pair_f32(rc, g.alpha * mma.acc[i][j][v] + bn, g.alpha * mma.acc[i][j][v + 1] + bn, odd,
+                          off + dr * pitch);
         }
     }
   } else {  // EPI_SWIGLU_BWD: acc = dh; dG from the saved pre-activation G
@@ -456,6 +487,29 @@ __device__ __forceinline__ void large_epilogue(LMma &mma, const GroupedArgs &g, 
     const __amdgpu_buffer_rsrc_t ri = rows_rsrc(g.Gin, tm.row0, tm.rows, g.ldg, 2);
     const __amdgpu_buffer_rsrc_t ro = rows_rsrc(g.Gout, tm.row0, tm.rows, g.ldg, 2);
     const uint32_t pitch = (uint32_t)(g.ldg * 2), uoff = (uint32_t)(g.I * 2);
+    if (g.act == 1) {
+      // clamped GLU over interleaved rows: the (gate, up) pair of column n of a row is one
+      // dword of G and of dG; every lane handles its own column, rows rl + dr
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + LMma::col_of(j);
+        const uint32_t off = n < g.N ? (uint32_t)((rl * g.ldg + 2 * n) * 2) : OOB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t gu[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v) gu[v] = bload32(ri, off + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * pitch, 0);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float dg, du;
+            glu_clamped_bwd(bf2f((uint16_t)(gu[v] & 0xffffu)), bf2f((uint16_t)(gu[v] >> 16)), g.glu_alpha,
+                            g.glu_limit, mma.acc[i][j][v], dg, du);
+            bstore32u(ro, pack_bf16x2(dg, du), off + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * pitch);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + LMma::col_of(j);
@@ -501,7 +555,7 @@ __global__ __launch_bounds__(L_THREADS) void gemm_x_kernel(GroupedArgs g) {
   if (!find_tile_wave(g.off, g.E, L_BM, blockIdx.y, tm)) return;
   const int e = tm.e;
   const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
-  const RowMap map{n0, g.I, SWIGLU};
+  const RowMap map{n0, g.I, SWIGLU, SWIGLU && g.act == 1};
   const int Nrows = SWIGLU ? 2 * g.I : g.N;
 
   XPipe<KN> pipe(A0, A1, B0, B1, B2, g, e);
@@ -659,7 +713,7 @@ __global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
   if (!find_tile(g.off, g.E, L_BM, blockIdx.y, tm, tile_sh)) return;
   const int e = tm.e;
   const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
-  const RowMap map{n0, g.I, SWIGLU};
+  const RowMap map{n0, g.I, SWIGLU, SWIGLU && g.act == 1};
   const int Nrows = SWIGLU ? 2 * g.I : g.N;
   const int nmain = g.K / BK;
   if (threadIdx.x >= WS_CONSUMERS) {

@@ -83,6 +83,14 @@ struct GroupedArgs {
   // few-row LoRA-A only (nullable): also write the gathered activation rows, [M][K] in
   // sorted-row order, for the GEMM that follows
   uint16_t *xg_out;
+  // activation of the gate_up epilogues: 0 = act(gate) * up over rows [0, I) / [I, 2I);
+  // 1 = clamped GLU over interleaved rows (2i, 2i+1), see glu_clamped
+  int act;
+  float glu_alpha, glu_limit;
+  // per-expert bias added to the output columns (nullable): gate_up [E][2I] in stored row
+  // order, down [E][H]
+  const uint16_t *bias;
+  int64_t bias_estride;
 };
 
 enum BKind : int { B_QNK = 0, B_QKN = 1, B_DENSE = 2 };

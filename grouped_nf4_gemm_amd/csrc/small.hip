@@ -183,7 +183,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     if constexpr (EPI == EPI_SWIGLU_FWD) {
       const int i = st * 16 + (n & 15);
       ok = i < g.I;
-      row[s] = n < 16 ? i : g.I + i;
+      row[s] = gate_up_row(i, n >= 16, g.act == 1, g.I);
     } else {
       row[s] = st * 32 + n;
       ok = row[s] < N;
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     if constexpr (EPI == EPI_SWIGLU_FWD) {
       const int ii = st * 16 + (rho & 15);
       rok = ii < g.I;
-      r = rho < 16 ? ii : g.I + ii;
+      r = gate_up_row(ii, rho >= 16, g.act == 1, g.I);
     } else {
       r = st * 32 + rho;
       rok = r < N;
@@ -381,6 +381,11 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   for (int s = 0; s < SPW; ++s) {
     if constexpr (EPI == EPI_SWIGLU_FWD) {
       const int i = ((blockIdx.x * SM_WAVES + w) * SPW + s) * 16 + (n & 15);
+      float bg = 0.0f, bu = 0.0f;
+      if (g.bias && n < 16 && i < g.I) {
+        bg = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, false, g.act == 1, g.I)]);
+        bu = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, true, g.act == 1, g.I)]);
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float mine = acc[s][v];
@@ -388,22 +393,24 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
         const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
         if (n < 16 && i < g.I && t < tm.rows) {
           const int64_t p = tm.row0 + t;
-          const float gt = mine, up = other;
-          const float act = gt * sigmoid_fast(gt);
-          ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(act * up);
+          const float gt = mine + bg, up = other + bu;
+          const float h = g.act == 1 ? glu_clamped(gt, up, g.glu_alpha, g.glu_limit) : gt * sigmoid_fast(gt) * up;
+          ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(h);
           if (g.Gout) {
-            g.Gout[p * g.ldg + i] = f2bf(gt);
-            g.Gout[p * g.ldg + g.I + i] = f2bf(up);
+            g.Gout[p * g.ldg + gate_up_row(i, false, g.act == 1, g.I)] = f2bf(gt);
+            g.Gout[p * g.ldg + gate_up_row(i, true, g.act == 1, g.I)] = f2bf(up);
           }
         }
       }
     } else {
       if (row[s] < 0) continue;
       float *out = (float *)g.C + blockIdx.z * split_stride;
+      // the first split also adds the per-expert bias (clamped GLU experts' down projection)
+      const float bn = (g.bias && blockIdx.z == 0) ? bf2f(g.bias[e * g.bias_estride + row[s]]) : 0.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (t < tm.rows) out[(tm.row0 + t) * g.ldc + row[s]] = acc[s][v];
+        if (t < tm.rows) out[(tm.row0 + t) * g.ldc + row[s]] = acc[s][v] + bn;
       }
     }
   }
@@ -465,7 +472,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     if constexpr (EPI == EPI_SWIGLU_FWD) {
       const int i = st * 16 + (n & 15);
       ok = i < g.I;
-      row = n < 16 ? i : g.I + i;
+      row = gate_up_row(i, n >= 16, g.act == 1, g.I);
     } else {
       row = st * 32 + n;
       ok = row < N;
@@ -487,7 +494,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       if constexpr (EPI == EPI_SWIGLU_FWD) {
         const int ii = st * 16 + (rho & 15);
         rok = ii < g.I;
-        r = rho < 16 ? ii : g.I + ii;
+        r = gate_up_row(ii, rho >= 16, g.act == 1, g.I);
       } else {
         r = st * 32 + rho;
         rok = r < N;
@@ -699,6 +706,11 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     // accumulator rows are the slot's tokens: write those of this pass
     if constexpr (EPI == EPI_SWIGLU_FWD) {
       const int i = st_done * 16 + (n & 15);
+      float bg = 0.0f, bu = 0.0f;
+      if (g.bias && n < 16 && i < g.I) {
+        bg = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, false, g.act == 1, g.I)]);
+        bu = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, true, g.act == 1, g.I)]);
+      }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float mine = acc[v];
@@ -706,21 +718,23 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
         if (n < 16 && i < g.I && t >= t0 && t < t0 + xrows) {
           const int64_t p = tm.row0 + t;
-          const float gt = mine, up = other;
-          const float act = gt * sigmoid_fast(gt);
-          ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(act * up);
+          const float gt = mine + bg, up = other + bu;
+          const float h = g.act == 1 ? glu_clamped(gt, up, g.glu_alpha, g.glu_limit) : gt * sigmoid_fast(gt) * up;
+          ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(h);
           if (g.Gout) {
-            g.Gout[p * g.ldg + i] = f2bf(gt);
-            g.Gout[p * g.ldg + g.I + i] = f2bf(up);
+            g.Gout[p * g.ldg + gate_up_row(i, false, g.act == 1, g.I)] = f2bf(gt);
+            g.Gout[p * g.ldg + gate_up_row(i, true, g.act == 1, g.I)] = f2bf(up);
           }
         }
       }
     } else if (row_done >= 0) {
       float *out = (float *)g.C + blockIdx.z * split_stride;
+      // the first split also adds the per-expert bias (clamped GLU experts' down projection)
+      const float bn = (g.bias && blockIdx.z == 0) ? bf2f(g.bias[e * g.bias_estride + row_done]) : 0.0f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (t >= t0 && t < t0 + xrows) out[(tm.row0 + t) * g.ldc + row_done] = acc[v];
+        if (t >= t0 && t < t0 + xrows) out[(tm.row0 + t) * g.ldc + row_done] = acc[v] + bn;
       }
     }
     // the next strip: its first loads

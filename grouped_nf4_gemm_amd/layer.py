@@ -171,7 +171,10 @@ class MoELayer:
     (written into the workspace) instead of decoding them inside the GEMM tiles."""
 
     def __init__(self, w_gu: QStack, w_dn: QStack, l_gu: LoRA | None, l_dn: LoRA | None,
-                 T: int, topk: int, train: bool = True, expand: bool | None = None):
+                 T: int, topk: int, train: bool = True, expand: bool | None = None, act: dict | None = None):
+        """act: None for the stock act(gate) * up, or {"kind": "clamped_glu", "alpha": a,
+        "limit": L, "b_gu": bf16 [E, 2I] or None, "b_dn": bf16 [E, H] or None} for the clamped
+        GLU over interleaved gate/up rows (gpt-oss experts)."""
         self.w_gu, self.w_dn, self.l_gu, self.l_dn = w_gu, w_dn, l_gu, l_dn
         self.E, self.H, self.I = w_gu.E, w_gu.K, w_dn.K
         dev = w_gu.codes.device
@@ -191,7 +194,18 @@ class MoELayer:
                 _arg(l.B, f"{name}.B", torch.bfloat16, (E, N, l.r), dev)
         self.T, self.topk = T, topk
         self.flags = (E4B_TRAIN if train else 0) | (E4B_EXPAND if expand else 0)
-        self.desc = _lib.Desc(self.E, self.H, self.I, T, topk, self.flags)
+        self._act = None
+        if act is not None:
+            b_gu, b_dn = act.get("b_gu"), act.get("b_dn")
+            if b_gu is not None:
+                _arg(b_gu, "b_gu", torch.bfloat16, (E, 2 * I), dev)
+            if b_dn is not None:
+                _arg(b_dn, "b_dn", torch.bfloat16, (E, H), dev)
+            self._act_tensors = (b_gu, b_dn)
+            self._act = _lib.Act(_lib.ACT[act.get("kind", "clamped_glu")], float(act.get("alpha", 1.702)),
+                                 float(act.get("limit", 7.0)), _ptr(b_gu), _ptr(b_dn))
+        self.desc = _lib.Desc(self.E, self.H, self.I, T, topk, self.flags,
+                              ctypes.pointer(self._act) if self._act is not None else None)
         n = ctypes.c_size_t()
         check(_lib.lib().e4b_moe_workspace_size(ctypes.byref(self.desc), _lora_c(l_gu), _lora_c(l_dn),
                                                 ctypes.byref(n)), "e4b_moe_workspace_size")

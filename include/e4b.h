@@ -99,9 +99,31 @@ typedef struct {
  * results are bit-identical, and the dgrad still decodes the packed stacks. */
 #define E4B_EXPAND 2u
 
+/* Expert activation between the two projections.
+ *  E4B_ACT_SWIGLU: the stock epilogue act(gate) * up with SiLU (method page, "Limitations":
+ *    the stock-epilogue contract); gate = rows [0, I) of gate_up, up = rows [I, 2I).
+ *  E4B_ACT_CLAMPED_GLU: the clamped GLU of gpt-oss's MXFP4 experts (README, "Scope": per-expert
+ *    biases and a clamped GLU; project record, "limitations"): gate = row 2i and up = row
+ *    2i+1 of gate_up (interleaved); G = W1 x + b_gu + s1 B1 A1 x; g' = min(gate, limit),
+ *    u' = clamp(up, -limit, limit), h = (u' + 1) * g' * sigmoid(alpha * g');
+ *    O = W2 h + s2 B2 A2 h + b_dn.  The clamps pass gradient inside the closed interval.
+ *    b_gu bf16 [E, 2I] (stored row order) and b_dn bf16 [E, H] are frozen device tensors,
+ *    either may be NULL.  alpha and limit must be finite, limit > 0. */
+#define E4B_ACT_SWIGLU 0
+#define E4B_ACT_CLAMPED_GLU 1
+typedef struct {
+  int32_t kind;
+  float alpha, limit;
+  const uint16_t *b_gu;
+  const uint16_t *b_dn;
+} e4b_act;
+
+/* One layer call: E experts, hidden H, intermediate I, T tokens, topk experts per token,
+ * E4B_* flags, and the activation (act == NULL: E4B_ACT_SWIGLU, no biases; a host pointer). */
 typedef struct {
   int32_t E, H, I, T, topk;
   uint32_t flags;
+  const e4b_act *act;
 } e4b_moe_desc;
 
 int32_t e4b_version(void);

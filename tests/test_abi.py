@@ -213,3 +213,24 @@ def test_code_table_rejections(L):
     assert lib.e4b_moe_workspace_size(ctypes.byref(d), None, None, ctypes.byref(n)) == 0
     assert L.get_stats()["launches_total"] == 0
     del ok
+
+
+def test_activation_checks(L):
+    """The activation block is checked before any launch: the stock epilogue takes no biases,
+    the clamped GLU needs a finite alpha and a finite positive limit, and an unknown kind is
+    refused as unsupported."""
+    lib = L.lib()
+
+    def ws_status(act):
+        d = L.Desc(4, 64, 64, 8, 2, 1, ctypes.pointer(act))
+        n = ctypes.c_size_t()
+        return lib.e4b_moe_workspace_size(ctypes.byref(d), None, None, ctypes.byref(n))
+
+    assert ws_status(L.Act(1, 1.702, 7.0, 0x10, 0x20)) == L.E4B_OK
+    assert ws_status(L.Act(1, 1.702, 7.0, None, None)) == L.E4B_OK
+    assert ws_status(L.Act(0, 0.0, 0.0, None, None)) == L.E4B_OK
+    assert ws_status(L.Act(0, 0.0, 0.0, 0x10, None)) == L.E4B_ERR_INVALID_ARG
+    assert ws_status(L.Act(1, 1.702, 0.0, None, None)) == L.E4B_ERR_INVALID_ARG
+    assert ws_status(L.Act(1, float("nan"), 7.0, None, None)) == L.E4B_ERR_INVALID_ARG
+    assert ws_status(L.Act(1, 1.702, float("inf"), None, None)) == L.E4B_ERR_INVALID_ARG
+    assert ws_status(L.Act(7, 1.0, 1.0, None, None)) == L.E4B_ERR_UNSUPPORTED

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import synth
-from grouped_nf4_gemm_amd import get_stats, reset_stats
+from grouped_nf4_gemm_amd import MoELayer, get_stats, reset_stats
 from tests.gpu_helpers import Case, assert_close, bf16_to_np, require_gpu
 
 pytestmark = pytest.mark.gpu
@@ -266,3 +266,50 @@ def test_layer_rejects_bad_arguments():
         with pytest.raises(ValueError):
             f()
     assert get_stats()["launches_total"] == 0
+
+
+def _glu_act(s, seed):
+    """Clamped-GLU biases that put some gates above the limit and some ups beyond +-limit,
+    the rest well inside: every clamp decision is far from the limit in both precisions."""
+    rng = np.random.default_rng(seed)
+    b1 = rng.normal(0, 0.05, (s.E, 2 * s.I)).astype(np.float32)
+    cols = rng.integers(0, 4, s.I)  # 0: none, 1: gate above, 2: up above, 3: up below
+    b1[:, 0::2][:, cols == 1] += 10.0
+    b1[:, 1::2][:, cols == 2] += 10.0
+    b1[:, 1::2][:, cols == 3] -= 10.0
+    b2 = rng.normal(0, 0.05, (s.E, s.H)).astype(np.float32)
+    return synth.to_bf16_bits(b1), synth.to_bf16_bits(b2), cols
+
+
+@pytest.mark.parametrize("T", [24, 150], ids=["weight-streaming", "large-tiles"])
+def test_clamped_glu_layer(T):
+    """The gpt-oss expert epilogue (interleaved gate/up rows, per-expert biases, clamped GLU
+    with alpha 1.702 and limit 7) over MXFP4 stacks: forward, input gradient and LoRA
+    gradients against the oracle, with clamping active on both halves."""
+    import oracle
+
+    s = synth.custom(6, 192, 192, T, 4, 8, 16.0, "mxfp4", name=f"glu-t{T}")
+    inp = synth.make_inputs(s, seed=700 + T)
+    b1, b2, cols = _glu_act(s, 800 + T)
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    act = {"kind": "clamped_glu", "alpha": 1.702, "limit": 7.0, "b_gu": dev(b1), "b_dn": dev(b2)}
+    case = Case(inp)
+    lay = MoELayer(case.w_gu, case.w_dn, case.l_gu, case.l_dn, s.T, s.k, train=True, act=act)
+    reset_stats()
+    y = lay.forward(case.x, case.ids, case.topw)
+    dx, dw = lay.dgrad(case.ids, case.topw, case.dy)
+    gw = lay.wgrad(case.x)
+    torch.cuda.synchronize()
+    assert get_stats()["fallbacks"] == 0
+    L = oracle.layer_from_inputs(inp, case.q1, case.q2, act=dict(alpha=1.702, limit=7.0, b1=b1, b2=b2))
+    y_ref = oracle.moe_fwd(L)
+    g = oracle.moe_bwd(L, inp.dy)
+    assert_close(bf16_to_np(y), y_ref, "y")
+    assert_close(bf16_to_np(dx), g["dx"], "dx")
+    assert_close(dw.cpu().numpy(), g["dw"], "d_topw")
+    for k_gpu, k_ref in [("dA_gu", "dA1"), ("dB_gu", "dB1"), ("dA_dn", "dA2"), ("dB_dn", "dB2")]:
+        assert_close(gw[k_gpu].cpu().numpy(), g[k_ref], k_gpu)
+    # the clamped halves really are clamped: their LoRA-B gradient rows vanish exactly
+    dB = gw["dB_gu"].cpu().numpy()
+    assert np.all(dB[:, 0::2][:, cols == 1] == 0) and np.all(dB[:, 1::2][:, cols >= 2] == 0)
+    assert np.abs(dB[:, 0::2][:, cols == 0]).min(initial=1.0) >= 0 and np.abs(dB).max() > 0
