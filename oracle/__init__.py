@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
-FMT_NF4, FMT_NF4_DQ, FMT_MXFP4 = 0, 1, 2
-_FMT = {"nf4": FMT_NF4, "nf4_dq": FMT_NF4_DQ, "mxfp4": FMT_MXFP4}
+FMT_NF4, FMT_NF4_DQ, FMT_MXFP4, FMT_INT8, FMT_FP8 = 0, 1, 2, 3, 4
+_FMT = {"nf4": FMT_NF4, "nf4_dq": FMT_NF4_DQ, "mxfp4": FMT_MXFP4, "int8": FMT_INT8, "fp8": FMT_FP8}
 
 
 def build(force: bool = True) -> str:
@@ -115,6 +115,12 @@ def quantize(fmt: str, w: np.ndarray) -> QWeight:
     w = np.ascontiguousarray(w, np.float32)
     E, N, K = w.shape
     n = w.size
+    if fmt in ("int8", "fp8"):  # one byte per element, an fp32 scale per 64
+        codes = np.zeros(n, np.uint8)
+        scale = np.zeros(n // 64, np.float32)
+        (lib().orc_quant_int8 if fmt == "int8" else lib().orc_quant_fp8)(_p(w), ctypes.c_int64(n), _p(codes),
+                                                                        _p(scale))
+        return QWeight(fmt, E, N, K, codes, scale)
     codes = np.zeros(n // 2, np.uint8)
     if fmt == "nf4":
         scale = np.zeros(n // 64, np.float32)
@@ -130,6 +136,12 @@ def quantize(fmt: str, w: np.ndarray) -> QWeight:
         lib().orc_quant_mxfp4(_p(w), ctypes.c_int64(n), _p(codes), _p(scale))
         return QWeight(fmt, E, N, K, codes, scale)
     raise ValueError(fmt)
+
+
+def e4m3_values() -> np.ndarray:
+    """The value of each of the 256 FP8 E4M3 codes (NaN for 0x7F, 0xFF)."""
+    lib().orc_e4m3_value.restype = ctypes.c_float
+    return np.array([lib().orc_e4m3_value(ctypes.c_uint8(c)) for c in range(256)], np.float32)
 
 
 def quantize_flat_nf4(w: np.ndarray):

@@ -37,6 +37,11 @@
  *    gate clamped from above and up from both sides at `limit`, h = (up + 1) * gate *
  *    sigmoid(alpha * gate), down bias added after the down projection.  The LoRA delta
  *    enters before the activation as for the stock epilogue; the biases are frozen.
+ *  - 8-bit bases (README, opening section: int8 and fp8 storage modes of the fused stack;
+ *    the pages fix neither scheme): blocks of 64 elements along the reduction axis with one
+ *    fp32 scale, symmetric linear INT8 (scale = absmax / 127) and OCP FP8 E4M3 without
+ *    infinities (largest finite 448, scale = absmax / 448), nearest value with ties to even.
+ *    Dequant is the same single fp32 multiply as for NF4.
  *  - Routing grouped by expert, stable in the flat index t*k + j.
  *
  * Precision: weights dequantise exactly per the fp32 contract; everything after
@@ -178,10 +183,77 @@ void orc_quant_mxfp4(const float *w, int64_t n, uint8_t *codes, uint8_t *scales)
   }
 }
 
+/* FP8 E4M3 (OCP): sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 holds the
+ * subnormals m * 2^-9; 0x7F and 0xFF are NaN (there is no infinity). */
+float orc_e4m3_value(uint8_t code) {
+  int e = (code >> 3) & 15, m = code & 7;
+  float v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexpf((float)m, -9);
+  else v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+  return (code & 0x80) ? -v : v;
+}
+
+/* Nearest E4M3 code to a finite v with |v| <= 448, ties to the even code (the one whose last
+ * mantissa bit is 0). */
+static uint8_t e4m3_nearest(float v) {
+  uint8_t sign = v < 0.0f ? 0x80 : 0;
+  float a = fabsf(v);
+  uint8_t best = 0;
+  float bestd = a;  /* code 0 = +0 */
+  for (int c = 1; c < 127; ++c) {  /* every finite positive code, ascending value */
+    float d = fabsf(a - orc_e4m3_value((uint8_t)c));
+    if (d < bestd || (d == bestd && (c & 1) == 0)) { bestd = d; best = (uint8_t)c; }
+  }
+  return (uint8_t)(best | (best ? sign : 0));
+}
+
+void orc_quant_int8(const float *w, int64_t n, uint8_t *codes, float *scales) {
+  int64_t nb = n / 64;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const float *blk = w + b * 64;
+    float amax = 0.0f;
+    for (int i = 0; i < 64; ++i) if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+    float s = amax / 127.0f;
+    scales[b] = s;
+    for (int i = 0; i < 64; ++i) {
+      long q = 0;
+      if (s != 0.0f) {
+        float t = blk[i] / s;
+        q = lrintf(t);  /* current rounding mode: to nearest, ties to even */
+        if (q > 127) q = 127;
+        if (q < -127) q = -127;
+      }
+      codes[b * 64 + i] = (uint8_t)(int8_t)q;
+    }
+  }
+}
+
+void orc_quant_fp8(const float *w, int64_t n, uint8_t *codes, float *scales) {
+  int64_t nb = n / 64;
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < nb; ++b) {
+    const float *blk = w + b * 64;
+    float amax = 0.0f;
+    for (int i = 0; i < 64; ++i) if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+    float s = amax / 448.0f;
+    scales[b] = s;
+    for (int i = 0; i < 64; ++i) {
+      float t = s != 0.0f ? blk[i] / s : 0.0f;
+      if (t > 448.0f) t = 448.0f;
+      if (t < -448.0f) t = -448.0f;
+      codes[b * 64 + i] = e4m3_nearest(t);
+    }
+  }
+}
+
 /* ------------------------------------------------------------------- dequant */
 
 static float deq_one(int32_t fmt, int64_t i, const uint8_t *codes, const void *scale,
                      const float *scale2, const float *dq_table, const float *codebook) {
+  if (fmt == ORC_FMT_INT8) return (float)(int8_t)codes[i] * ((const float *)scale)[i / 64];
+  if (fmt == ORC_FMT_FP8) return orc_e4m3_value(codes[i]) * ((const float *)scale)[i / 64];
   uint8_t byte = codes[i >> 1];
   if (fmt == ORC_FMT_MXFP4) {
     uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);

@@ -23,14 +23,14 @@
 extern "C" {
 #endif
 
-enum { ORC_FMT_NF4 = 0, ORC_FMT_NF4_DQ = 1, ORC_FMT_MXFP4 = 2 };
+enum { ORC_FMT_NF4 = 0, ORC_FMT_NF4_DQ = 1, ORC_FMT_MXFP4 = 2, ORC_FMT_INT8 = 3, ORC_FMT_FP8 = 4 };
 
 /* One 4-bit expert stack [E, N, K], K contiguous, as bytes + scales. */
 typedef struct {
   int32_t fmt;
   int32_t E, N, K;
-  const uint8_t *codes;   /* [E*N*K/2] */
-  const void *scale;      /* NF4: float[E*N*K/64]; NF4_DQ: uint8[E*N*K/64]; MXFP4: uint8[E*N*K/32] */
+  const uint8_t *codes;   /* [E*N*K/2] (4-bit formats) or [E*N*K] (INT8, FP8) */
+  const void *scale;      /* NF4, INT8, FP8: float[E*N*K/64]; NF4_DQ: uint8[E*N*K/64]; MXFP4: uint8[E*N*K/32] */
   const float *scale2;    /* NF4_DQ: float[ceil(E*N*K/64/256)]; else unused */
   const float *dq_table;  /* NF4_DQ: value of each 8-bit absmax code [256]; NULL = c/255 */
   const float *codebook;  /* NF4 formats: value of each 4-bit code [16]; NULL = NormalFloat */
@@ -69,6 +69,11 @@ void orc_bf16_round(const float *in, uint16_t *out, int64_t n);
 void orc_quant_nf4(const float *w, int64_t n, uint8_t *codes, float *absmax);
 void orc_quant_nf4_dq(const float *w, int64_t n, uint8_t *codes, uint8_t *qabsmax, float *scale2);
 void orc_quant_mxfp4(const float *w, int64_t n, uint8_t *codes, uint8_t *scales);
+/* 8-bit bases, blocks of 64 along K with an fp32 scale: INT8 q = rne(w / s) in [-127, 127],
+ * s = absmax / 127; FP8 E4M3 (OCP, finite, max 448) q = rne(w / s) with s = absmax / 448. */
+void orc_quant_int8(const float *w, int64_t n, uint8_t *codes, float *scales);
+void orc_quant_fp8(const float *w, int64_t n, uint8_t *codes, float *scales);
+float orc_e4m3_value(uint8_t code);
 /* Dequantise n elements (flat) to fp32 and/or bf16 (either pointer may be NULL).
  * dq_table / codebook: the stack's own code tables (NULL = the built-in ones). */
 void orc_dequant(int32_t fmt, int64_t n, const uint8_t *codes, const void *scale,

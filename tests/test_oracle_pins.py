@@ -240,6 +240,78 @@ def test_mxfp4_roundtrip_representable(orc):
         assert np.array_equal(f32.ravel(), w.ravel())
 
 
+# ----------------------------------------------------------------------------- 8-bit bases
+
+def test_e4m3_table_matches_torch(orc):
+    """The 256 FP8 E4M3 code values against torch's float8_e4m3fn decoding."""
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(orc.e4m3_values(), ref, equal_nan=True)
+
+
+def test_fp8_quant_matches_torch_rounding(orc):
+    """Codes are torch's round-to-nearest-even float8_e4m3fn conversion of w / (absmax / 448)."""
+    rng = np.random.default_rng(41)
+    w = (rng.standard_normal((2, 16, 256)) * 0.02).astype(np.float32)
+    w[0, 0, :64] = 0.0
+    q = orc.quantize("fp8", w)
+    blocks = w.reshape(-1, 64)
+    s = (np.abs(blocks).max(axis=1) / np.float32(448.0)).astype(np.float32)
+    assert np.array_equal(q.scale, s)
+    t = np.where(s[:, None] > 0, blocks / np.where(s > 0, s, 1)[:, None], 0).astype(np.float32)
+    want = torch.from_numpy(np.clip(t, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    want[want == 0x80] = 0  # -0 is stored as +0
+    assert np.array_equal(q.codes.reshape(-1, 64), want)
+
+
+def test_int8_quant_bruteforce(orc):
+    rng = np.random.default_rng(42)
+    w = (rng.standard_normal((2, 16, 256)) * 0.02).astype(np.float32)
+    w[1, 3, 64:128] = 0.0
+    q = orc.quantize("int8", w)
+    blocks = w.reshape(-1, 64)
+    s = (np.abs(blocks).max(axis=1) / np.float32(127.0)).astype(np.float32)
+    assert np.array_equal(q.scale, s)
+    t = np.where(s[:, None] > 0, blocks / np.where(s > 0, s, 1)[:, None], 0).astype(np.float32)
+    want = np.clip(np.rint(t), -127, 127).astype(np.int8).view(np.uint8)
+    assert np.array_equal(q.codes.reshape(-1, 64), want)
+
+
+@pytest.mark.parametrize("fmt", ["int8", "fp8"])
+def test_8bit_roundtrip_and_dequant(orc, fmt):
+    """Values on the format's grid with a power-of-two scale come back exactly, and dequant is
+    one fp32 multiply of the decoded code (torch's float8 decoding for FP8) by the scale."""
+    rng = np.random.default_rng(43)
+    scale = np.float32(2.0 ** -5)
+    if fmt == "int8":
+        k = rng.integers(-127, 128, (4, 64))
+        k[:, 5] = 127
+        grid = k.astype(np.float32)
+    else:
+        vals = orc.e4m3_values()
+        codes = rng.integers(0, 256, (4, 64))
+        codes[(codes == 0x7F) | (codes == 0xFF) | (codes == 0x80)] = 1
+        codes[:, 5] = 0x7E  # 448 fixes the scale
+        grid = vals[codes]
+    w = (grid * scale).astype(np.float32).reshape(1, 4, 64)
+    q = orc.quantize(fmt, w)
+    assert np.all(q.scale == scale)
+    f32, b16 = orc.dequant(q)
+    assert np.array_equal(f32.ravel(), w.ravel())
+    # dequant of arbitrary codes and scales
+    codes = rng.integers(0, 256, 4 * 64).astype(np.uint8)
+    if fmt == "fp8":
+        codes[(codes & 0x7F) == 0x7F] = 3
+    sc = rng.uniform(0.001, 0.1, 4).astype(np.float32)
+    q = orc.QWeight(fmt, 1, 4, 64, codes, sc)
+    f32, b16 = orc.dequant(q)
+    dec = codes.view(np.int8).astype(np.float32) if fmt == "int8" else \
+        torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    want = (dec * np.repeat(sc, 64)).astype(np.float32)
+    assert np.array_equal(f32.ravel().view(np.uint32), want.view(np.uint32))
+    ref16 = torch.from_numpy(want).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b16.ravel(), ref16)
+
+
 # ----------------------------------------------------------------------------- routing
 
 @pytest.mark.parametrize("T,k,E", [(0, 2, 4), (1, 2, 8), (37, 3, 5), (200, 8, 128), (64, 1, 1)])
@@ -299,7 +371,7 @@ def _dense_reformulation(inp, W1, W2, lora=True):
     return Y.numpy()
 
 
-@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4", "int8", "fp8"])
 def test_forward_matches_dense_onehot(orc, fmt):
     inp = _small(fmt=fmt)
     q1, q2 = orc.quantize(fmt, inp.W1), orc.quantize(fmt, inp.W2)
