@@ -12,7 +12,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 SO_PATH = os.path.join(_PKG, "libe4b.so")
 
 E4B_OK, E4B_ERR_INVALID_ARG, E4B_ERR_UNSUPPORTED, E4B_ERR_WORKSPACE, E4B_ERR_HIP = range(5)
-FMT = {"nf4": 0, "nf4_dq": 1, "mxfp4": 2}
+FMT = {"nf4": 0, "nf4_dq": 1, "mxfp4": 2, "int8": 3, "fp8": 4}
 E4B_TRAIN = 1
 E4B_EXPAND = 2
 

@@ -196,12 +196,12 @@ static e4b_status check_lora(const e4b_lora *l, int *r) {
 
 static e4b_status check_q(const e4b_qweight *q, int E, int N, int K) {
   if (!q || !q->codes || !q->scale) return E4B_ERR_INVALID_ARG;
-  if (q->fmt < E4B_FMT_NF4 || q->fmt > E4B_FMT_MXFP4) return E4B_ERR_UNSUPPORTED;
+  if (q->fmt < E4B_FMT_NF4 || q->fmt > E4B_FMT_FP8) return E4B_ERR_UNSUPPORTED;
   if (q->fmt == E4B_FMT_NF4_DQ && !q->scale2) return E4B_ERR_INVALID_ARG;
   if (q->fmt != E4B_FMT_NF4_DQ && q->dq_table) return E4B_ERR_INVALID_ARG;
-  if (q->fmt == E4B_FMT_MXFP4 && q->codebook) return E4B_ERR_INVALID_ARG;
+  if (q->fmt != E4B_FMT_NF4 && q->fmt != E4B_FMT_NF4_DQ && q->codebook) return E4B_ERR_INVALID_ARG;
   if (q->E != E || q->N != N || q->K != K) return E4B_ERR_INVALID_ARG;
-  if ((int64_t)E * N * K / 2 > BUF_LIMIT) return E4B_ERR_INVALID_ARG;
+  if ((int64_t)E * N * K / (fmt_8bit(q->fmt) ? 1 : 2) > BUF_LIMIT) return E4B_ERR_INVALID_ARG;
   return E4B_OK;
 }
 
@@ -216,8 +216,8 @@ static QStack qstack(const e4b_qweight *q) {
   s.N = q->N;
   s.K = q->K;
   const int64_t n = (int64_t)q->E * q->N * q->K;
-  s.codes_bytes = (uint32_t)(n / 2);
-  s.scale_bytes = (uint32_t)(q->fmt == E4B_FMT_NF4 ? n / 64 * 4 : q->fmt == E4B_FMT_NF4_DQ ? n / 64 : n / 32);
+  s.codes_bytes = (uint32_t)(fmt_8bit(q->fmt) ? n : n / 2);
+  s.scale_bytes = (uint32_t)(q->fmt == E4B_FMT_NF4_DQ ? n / 64 : q->fmt == E4B_FMT_MXFP4 ? n / 32 : n / 64 * 4);
   s.scale2_bytes = q->fmt == E4B_FMT_NF4_DQ ? (uint32_t)((n / 64 + 255) / 256 * 4) : 0;
   return s;
 }
@@ -302,7 +302,7 @@ static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, con
     E4B_LAUNCH(launch_expand(qstack(w_dn), E, W2x, s));
   }
   // few routed rows: weight-streaming kernels (small.hip); otherwise the large tiles
-  const bool small = M <= SMALL_M_MAX;
+  const bool small = M <= SMALL_M_MAX && !fmt_8bit(w_gu->fmt);  // 8-bit bases: large tiles at any size
   const bool train = d.flags & E4B_TRAIN;
   auto lora_a = [&](const GroupedArgs &a) { return small ? launch_small_lora_a(a, s) : launch_lora_a(a, s); };
 
@@ -595,7 +595,7 @@ e4b_status e4b_dequant(const e4b_qweight *w, int32_t expert, float *out_f32, uin
 
 e4b_status e4b_quantize(int32_t fmt, int32_t E, int32_t N, int32_t K, const float *w, uint8_t *codes,
                         void *scale, float *scale2, void *stream) {
-  if (fmt < E4B_FMT_NF4 || fmt > E4B_FMT_MXFP4) return E4B_ERR_UNSUPPORTED;
+  if (fmt < E4B_FMT_NF4 || fmt > E4B_FMT_FP8) return E4B_ERR_UNSUPPORTED;
   if (E < 1 || N < 1 || K < 64 || K % 64) return E4B_ERR_INVALID_ARG;
   if (!w || !codes || !scale || (fmt == E4B_FMT_NF4_DQ && !scale2)) return E4B_ERR_INVALID_ARG;
   const int64_t n = (int64_t)E * N * K;

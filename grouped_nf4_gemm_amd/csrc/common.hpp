@@ -13,7 +13,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Fmt : int { FMT_NF4 = 0, FMT_NF4_DQ = 1, FMT_MXFP4 = 2 };
+enum Fmt : int { FMT_NF4 = 0, FMT_NF4_DQ = 1, FMT_MXFP4 = 2, FMT_INT8 = 3, FMT_FP8 = 4 };
+// One byte per element (INT8, FP8 E4M3) rather than a 4-bit code.
+constexpr bool fmt_8bit(int fmt) { return fmt == FMT_INT8 || fmt == FMT_FP8; }
 
 // NormalFloat-4 code values (QLoRA), index 0..15.
 #define E4B_NF4_VALUES                                                                    \
@@ -169,7 +171,31 @@ __device__ __forceinline__ u32x4 mxfp4_word_to_bf16(uint32_t w, float scale) {
   return r;
 }
 
-// A frozen 4-bit stack as the kernels see it.
+// The 4 elements of one 32-bit word of an 8-bit stack (element 4j + b in byte b) times the
+// block scale, as 4 bf16 values: bf16(fp32(code) * scale).
+//  INT8: (byte ^ 0x80) read unsigned is q + 128, and fma(u, s, -128 s) rounds (u - 128) s
+//        exactly once (-128 s is exact), which is the fp32 product q * s.
+//  FP8 (OCP E4M3): the hardware conversion of two codes to fp32 (exact), then the product.
+template <int FMT>
+__device__ __forceinline__ u32x2 byte_word_to_bf16(uint32_t w, float sc) {
+  float f[4];
+  if constexpr (FMT == FMT_INT8) {
+    const uint32_t x = w ^ 0x80808080u;
+    const float nb = -128.0f * sc;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[b] = __builtin_fmaf((float)((x >> (8 * b)) & 0xffu), sc, nb);
+  } else {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo[0] * sc;
+    f[1] = lo[1] * sc;
+    f[2] = hi[0] * sc;
+    f[3] = hi[1] * sc;
+  }
+  return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+}
+
+// A frozen stack (4-bit or 8-bit codes) as the kernels see it.
 struct QStack {
   const uint8_t *codes;
   const void *scale;

@@ -569,6 +569,7 @@ __device__ __forceinline__ void fetch_scale(__amdgpu_buffer_rsrc_t rs, __amdgpu_
 // LDS load.
 template <int FMT>
 struct LQuantKN {
+  static constexpr int LOADS = FMT == FMT_NF4_DQ ? 3 : 2;  // one code load, the scale (+ second level)
   u32x4 w;
   uint32_t sraw;
   float s2;
@@ -660,6 +661,81 @@ struct LQuantRow {
         st_lds16(&t.v[p][bswz(p, c)], dec(w));
       }
     }
+  }
+};
+
+// 8-bit stacks (INT8, FP8) for the producer waves, stored [N, K]: thread p -> tile row p
+// (weight row map(p)) and the whole 64-k slab: four 16-byte code loads (64 contiguous bytes)
+// and the block's fp32 scale, decoded into the eight 16-byte pieces of the tile row.
+template <int FMT>
+struct LQuantRow8 {
+  static constexpr int LOADS = 5;
+  u32x4 c[4];
+  uint32_t sraw;
+  uint32_t cvoff, svoff;  // byte offsets at k0 = 0
+  __device__ __forceinline__ void init(const QStack &q, int e, const RowMap &map, int Nrows, int p) {
+    const int n = map(p);
+    if (n < Nrows) {
+      const int64_t el = ((int64_t)e * q.N + n) * q.K;
+      cvoff = (uint32_t)el;
+      svoff = (uint32_t)((el >> 6) * 4);
+    } else {
+      cvoff = svoff = OOB;
+    }
+  }
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                        __amdgpu_buffer_rsrc_t, int k0, uint32_t dead) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = bload128(rc, cvoff + 16 * i, (uint32_t)k0 | dead);
+    sraw = bload32(rs, svoff, ((uint32_t)(k0 / 64) * 4) | dead);
+  }
+  template <class TileT>
+  __device__ __forceinline__ void decode_store(TileT &t, const DecodeTables &, int p) const {
+    const float sc = __uint_as_float(sraw);
+#pragma unroll
+    for (int pc = 0; pc < 8; ++pc) {
+      const u32x2 a = byte_word_to_bf16<FMT>(c[pc >> 1][2 * (pc & 1)], sc);
+      const u32x2 b = byte_word_to_bf16<FMT>(c[pc >> 1][2 * (pc & 1) + 1], sc);
+      st_lds16(&t.v[p][bswz(p, pc)], u32x4{a[0], a[1], b[0], b[1]});
+    }
+  }
+};
+
+// 8-bit stacks reduced over their stored row axis (dgrad), LDS tile [64 k][256 n]: virtual
+// thread vt -> stored row vt / 8 and 32 stored columns (vt % 8): two 16-byte code loads and
+// the scale of the 64-column block they lie in, written as four 16-byte row pieces.
+template <int FMT>
+struct LQuantKN8 {
+  static constexpr int LOADS = 3;
+  u32x4 w[2];
+  uint32_t sraw;
+  float sc;
+  uint32_t cvoff, svoff, crow, srow;
+  __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout, int vt) {
+    const int kb = vt >> 3, nb = vt & 7;
+    const int n = n0 + nb * 32;
+    crow = (uint32_t)q.K;
+    srow = (uint32_t)(q.K / 64 * 4);
+    if (n < Nout) {
+      const int64_t el = ((int64_t)e * q.N + kb) * q.K + n;
+      cvoff = (uint32_t)el;
+      svoff = (uint32_t)((el >> 6) * 4);
+    } else {
+      cvoff = svoff = OOB;
+    }
+  }
+  __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                        __amdgpu_buffer_rsrc_t, int k0, uint32_t dead) {
+    w[0] = bload128(rc, cvoff, ((uint32_t)k0 * crow) | dead);
+    w[1] = bload128(rc, cvoff + 16, ((uint32_t)k0 * crow) | dead);
+    sraw = bload32(rs, svoff, ((uint32_t)k0 * srow) | dead);
+  }
+  __device__ __forceinline__ void prepare(const DecodeTables &) { sc = __uint_as_float(sraw); }
+  __device__ __forceinline__ void store(LTileKN &t, int part, int vt) const {
+    const int kb = vt >> 3, nb = vt & 7;
+    const u32x2 a = byte_word_to_bf16<FMT>(w[part >> 1][2 * (part & 1)], sc);
+    const u32x2 b = byte_word_to_bf16<FMT>(w[part >> 1][2 * (part & 1) + 1], sc);
+    st_lds16(&t.v[kb][knswz(nb * 32 + part * 8)], u32x4{a[0], a[1], b[0], b[1]});
   }
 };
 

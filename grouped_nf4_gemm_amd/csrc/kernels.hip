@@ -230,12 +230,6 @@ __device__ __forceinline__ void slab_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Vector-memory loads one K-major B fetch issues per thread (see LQuantKN::fetch): one code
-// load + one scale load (+ the second-level scale for NF4_DQ).
-template <int FMT>
-constexpr int kn_fetch_loads() {
-  return FMT == FMT_NF4_DQ ? 3 : 2;
-}
 
 // The same main loop over a bf16 copy of the stack (written by expand_kernel with the same
 // decode functions): A and B both go HBM -> LDS by direct loads, with no decode work, and
@@ -592,8 +586,10 @@ __device__ __forceinline__ void consumer_barrier() {
 template <int BKIND, int FMT>
 struct WSProducer {
   static constexpr bool KN = BKIND == B_QKN;
+  using RowL = typename std::conditional<fmt_8bit(FMT), LQuantRow8<FMT>, LQuantRow<FMT>>::type;
+  using KnL = typename std::conditional<fmt_8bit(FMT), LQuantKN8<FMT>, LQuantKN<FMT>>::type;
   // vector-memory loads of one B slab per producer thread (two K-major loaders, or one row)
-  static constexpr int LOADS = KN ? 2 * kn_fetch_loads<FMT>() : LQuantRow<FMT>::LOADS;
+  static constexpr int LOADS = KN ? 2 * KnL::LOADS : RowL::LOADS;
   using BTile = typename std::conditional<KN, LTileKN, LTile>::type;
   DecodeTables &tb;
   ATile &A0, &A1;
@@ -601,8 +597,8 @@ struct WSProducer {
   __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
   LDirectAN<4> la;
   int v, p;  // producer wave (0..3) and thread (0..255)
-  LQuantRow<FMT> nk[3];    // NK ring: slab t in nk[t % 3]
-  LQuantKN<FMT> kn[3][2];  // KN ring: two K-major loaders (virtual threads p, p + 256)
+  RowL nk[3];   // NK ring: slab t in nk[t % 3]
+  KnL kn[3][2];  // KN ring: two K-major loaders (virtual threads p, p + 256)
 
   __device__ __forceinline__ WSProducer(DecodeTables &tb_, ATile &a0, ATile &a1, BBuf &b0, BBuf &b1,
                                         const GroupedArgs &g)
@@ -750,7 +746,9 @@ static void launch_large(const GroupedArgs &a, dim3 grid, hipStream_t s) {
   switch (a.q.fmt) {
     case FMT_NF4: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_NF4><<<grid, WS_THREADS, 0, s>>>(a); break;
     case FMT_NF4_DQ: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_NF4_DQ><<<grid, WS_THREADS, 0, s>>>(a); break;
-    default: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_MXFP4><<<grid, WS_THREADS, 0, s>>>(a); break;
+    case FMT_MXFP4: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_MXFP4><<<grid, WS_THREADS, 0, s>>>(a); break;
+    case FMT_INT8: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_INT8><<<grid, WS_THREADS, 0, s>>>(a); break;
+    default: gemm_ws_kernel<BKIND, EPI, SWIGLU, FMT_FP8><<<grid, WS_THREADS, 0, s>>>(a); break;
   }
 }
 
@@ -1217,10 +1215,45 @@ __global__ void quant_mxfp4_kernel(const float *__restrict__ w, int64_t nblk, ui
   if (ok && (lane & 31) == 0) scales[b] = (uint8_t)X;
 }
 
+// 8-bit bases: one wave64 per block of 64 (element i on lane i).  INT8: s = absmax / 127,
+// q = rne(w / s) in [-127, 127].  FP8: s = absmax / 448, the hardware round-to-nearest-even
+// conversion of w / s clamped to the largest finite value 448 (it would give NaN beyond).
+template <int FMT>
+__global__ void quant8_kernel(const float *__restrict__ w, int64_t nblk, uint8_t *__restrict__ codes,
+                              float *__restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (b >= nblk) return;
+  const float v = w[b * 64 + lane];
+  float amax = fabsf(v);
+  for (int d = 32; d > 0; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  const float sc = amax / (FMT == FMT_INT8 ? 127.0f : 448.0f);
+  uint32_t q = 0;
+  if (sc != 0.0f) {
+    const float t = v / sc;
+    if constexpr (FMT == FMT_INT8) {
+      q = (uint32_t)(uint8_t)(int8_t)(int)fminf(127.0f, fmaxf(-127.0f, rintf(t)));
+    } else {
+      const float c = fminf(448.0f, fmaxf(-448.0f, t));
+      q = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xffu;
+      if (q == 0x80u) q = 0;  // -0 is stored as +0
+    }
+  }
+  codes[b * 64 + lane] = (uint8_t)q;
+  if (lane == 0) scales[b] = sc;
+}
+
 bool launch_quantize(int fmt, int64_t n, const float *w, uint8_t *codes, void *scale, float *scale2,
                      hipStream_t s) {
   if (n == 0) return true;
+  if (fmt < FMT_NF4 || fmt > FMT_FP8) return false;
   LaunchScope ls(FAM_QUANT, s);
+  if (fmt_8bit(fmt)) {
+    const int64_t nblk = n / 64;
+    if (fmt == FMT_INT8) quant8_kernel<FMT_INT8><<<cdiv(nblk, 4), 256, 0, s>>>(w, nblk, codes, (float *)scale);
+    else quant8_kernel<FMT_FP8><<<cdiv(nblk, 4), 256, 0, s>>>(w, nblk, codes, (float *)scale);
+    return last_launch_ok();
+  }
   if (fmt == FMT_MXFP4) {
     const int64_t nblk = n / 32;
     quant_mxfp4_kernel<<<cdiv(nblk, 8), 256, 0, s>>>(w, nblk, codes, (uint8_t *)scale);
@@ -1246,10 +1279,23 @@ __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *_
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nwords) return;
   const int64_t elem = elem0 + i * 8;
-  const uint32_t w = *(const uint32_t *)(q.codes + elem / 2);
   float vals[8];
   u32x4 bits;
-  if (q.fmt == FMT_MXFP4) {
+  if (fmt_8bit(q.fmt)) {  // 8 code bytes, one fp32 scale per 64 elements
+    const u32x2 c = *(const u32x2 *)(q.codes + elem);
+    const float sc = ((const float *)q.scale)[elem >> 6];
+    const bool i8 = q.fmt == FMT_INT8;
+    const u32x2 a = i8 ? byte_word_to_bf16<FMT_INT8>(c[0], sc) : byte_word_to_bf16<FMT_FP8>(c[0], sc);
+    const u32x2 b = i8 ? byte_word_to_bf16<FMT_INT8>(c[1], sc) : byte_word_to_bf16<FMT_FP8>(c[1], sc);
+    bits = u32x4{a[0], a[1], b[0], b[1]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t byte = (c[j >> 2] >> (8 * (j & 3))) & 0xffu;
+      const float v = i8 ? (float)(int)(int8_t)byte : __builtin_amdgcn_cvt_pk_f32_fp8((int)byte, false)[0];
+      vals[j] = v * sc;
+    }
+  } else if (q.fmt == FMT_MXFP4) {
+    const uint32_t w = *(const uint32_t *)(q.codes + elem / 2);
     const uint32_t X = ((const uint8_t *)q.scale)[elem >> 5];
     const float sc = e8m0_to_f32(X);
     bits = mxfp4_word_to_bf16(w, sc);
@@ -1260,6 +1306,7 @@ __global__ void dequant_kernel(QStack q, int64_t elem0, int64_t nwords, float *_
       vals[j] = m * sc;
     }
   } else {
+    const uint32_t w = *(const uint32_t *)(q.codes + elem / 2);
     const float am = nf4_block_absmax(q, elem >> 6, tb);
     bits = nf4_word_to_bf16(w, am, tb);
 #pragma unroll
@@ -1320,12 +1367,31 @@ __global__ __launch_bounds__(256) void expand_kernel(QStack q, int64_t nwords, u
   }
 }
 
+// The same for 8-bit stacks: thread t of a workgroup takes 8-byte piece 256 p + t (8
+// elements under one fp32 scale) and writes its 16 bytes of bf16.
+template <int FMT>
+__global__ __launch_bounds__(256) void expand8_kernel(QStack q, int64_t npieces, uint16_t *__restrict__ out) {
+  const int64_t w0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int64_t w = w0 + 256 * p;
+    if (w >= npieces) continue;
+    const u32x2 c = ((const u32x2 *)q.codes)[w];
+    const float sc = ((const float *)q.scale)[w >> 3];
+    const u32x2 a = byte_word_to_bf16<FMT>(c[0], sc), b = byte_word_to_bf16<FMT>(c[1], sc);
+    *(u32x4 *)(out + w * 8) = u32x4{a[0], a[1], b[0], b[1]};
+  }
+}
+
 bool launch_expand(const QStack &q, int E, uint16_t *out, hipStream_t s) {
   const int64_t nwords = (int64_t)E * q.N * q.K / 8;
   if (nwords == 0) return true;
+  if (q.fmt < FMT_NF4 || q.fmt > FMT_FP8) return false;
   LaunchScope ls(FAM_EXPAND, s);
   const unsigned grid = (unsigned)((nwords + 1023) / 1024);
   switch (q.fmt) {
+    case FMT_INT8: expand8_kernel<FMT_INT8><<<grid, 256, 0, s>>>(q, nwords, out); break;
+    case FMT_FP8: expand8_kernel<FMT_FP8><<<grid, 256, 0, s>>>(q, nwords, out); break;
     case FMT_NF4: expand_kernel<FMT_NF4><<<grid, 256, 0, s>>>(q, nwords, out); break;
     case FMT_NF4_DQ: expand_kernel<FMT_NF4_DQ><<<grid, 256, 0, s>>>(q, nwords, out); break;
     default: expand_kernel<FMT_MXFP4><<<grid, 256, 0, s>>>(q, nwords, out); break;
@@ -1336,6 +1402,7 @@ bool launch_expand(const QStack &q, int E, uint16_t *out, hipStream_t s) {
 bool launch_dequant(const QStack &q, int64_t elem0, int64_t n, float *out_f32, uint16_t *out_bf16,
                     hipStream_t s) {
   if (n == 0) return true;
+  if (q.fmt < FMT_NF4 || q.fmt > FMT_FP8) return false;
   LaunchScope ls(FAM_DEQUANT, s);
   const int64_t nwords = n / 8;
   dequant_kernel<<<cdiv(nwords, 256), 256, 0, s>>>(q, elem0, nwords, out_f32, out_bf16);

@@ -52,8 +52,8 @@ class QStack:
     E: int
     N: int
     K: int
-    codes: torch.Tensor          # uint8 [E*N*K/2]
-    scale: torch.Tensor          # fp32 / uint8
+    codes: torch.Tensor          # uint8 [E*N*K/2] (4-bit) or [E*N*K] (int8, fp8)
+    scale: torch.Tensor          # fp32 (nf4, int8, fp8) / uint8 (nf4_dq absmax codes, mxfp4 E8M0)
     scale2: torch.Tensor | None  # fp32 (NF4_DQ)
     dq_table: torch.Tensor | None = None  # fp32 [256] (NF4_DQ; None = built-in c / 255)
     codebook: torch.Tensor | None = None  # fp32 [16] (NF4 formats; None = built-in NF4 table)
@@ -68,8 +68,8 @@ class QStack:
     @staticmethod
     def empty(fmt: str, E: int, N: int, K: int, device="cuda") -> "QStack":
         n = E * N * K
-        codes = torch.empty(n // 2, dtype=torch.uint8, device=device)
-        if fmt == "nf4":
+        codes = torch.empty(n if fmt in ("int8", "fp8") else n // 2, dtype=torch.uint8, device=device)
+        if fmt in ("nf4", "int8", "fp8"):
             scale, scale2 = torch.empty(n // 64, dtype=torch.float32, device=device), None
         elif fmt == "nf4_dq":
             scale = torch.empty(n // 64, dtype=torch.uint8, device=device)
@@ -183,9 +183,11 @@ class MoELayer:
             if (q.E, q.N, q.K) != (E, N, K):
                 raise ValueError(f"{name}: stack [{E}, {N}, {K}] expected, got [{q.E}, {q.N}, {q.K}]")
             n = E * N * K
-            _arg(q.codes, f"{name}.codes", torch.uint8, (n // 2,), dev)
+            byte = q.fmt in ("int8", "fp8")
+            _arg(q.codes, f"{name}.codes", torch.uint8, (n if byte else n // 2,), dev)
             nscale = n // 32 if q.fmt == "mxfp4" else n // 64
-            _arg(q.scale, f"{name}.scale", torch.float32 if q.fmt == "nf4" else torch.uint8, (nscale,), dev)
+            _arg(q.scale, f"{name}.scale", torch.float32 if q.fmt in ("nf4", "int8", "fp8") else torch.uint8,
+                 (nscale,), dev)
             if q.fmt == "nf4_dq":
                 _arg(q.scale2, f"{name}.scale2", torch.float32, ((n // 64 + 255) // 256,), dev)
         for name, l, N, K in (("l_gu", l_gu, 2 * I, H), ("l_dn", l_dn, H, I)):

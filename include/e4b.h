@@ -46,29 +46,42 @@ typedef enum {
   E4B_ERR_HIP = 4
 } e4b_status;
 
-/* 4-bit storage formats of a frozen stack.
+/* Storage formats of a frozen stack.
  *  NF4:    16-value NormalFloat code (QLoRA table), blocks of 64 consecutive
  *          elements along K with one fp32 absmax; element 2j in the HIGH nibble of
  *          byte j.  w = fp32(nf4[q]) * absmax.
  *  NF4_DQ: NF4 whose absmax is itself 8-bit: absmax = fp32(c / 255) * scale2[b / 256]
  *          with b the flat block index over the whole stack.
  *  MXFP4:  FP4 E2M1 elements (element 2j in the LOW nibble) with one E8M0 scale byte
- *          per 32 consecutive elements along K: w = e2m1[q] * 2^(X - 127). */
-typedef enum { E4B_FMT_NF4 = 0, E4B_FMT_NF4_DQ = 1, E4B_FMT_MXFP4 = 2 } e4b_fmt;
+ *          per 32 consecutive elements along K: w = e2m1[q] * 2^(X - 127).
+ *  INT8:   one signed byte per element, blocks of 64 along K with an fp32 scale:
+ *          w = fp32(q) * scale (the library's quantiser: scale = absmax / 127).
+ *  FP8:    one OCP FP8 E4M3 byte per element (finite, largest 448), blocks of 64 along K
+ *          with an fp32 scale: w = fp32(e4m3(q)) * scale (quantiser: scale = absmax / 448).
+ * The 8-bit formats are the int8 / fp8 storage modes of the fused-stack base (README,
+ * opening section); their GEMMs run on the large tiles at every batch size. */
+typedef enum {
+  E4B_FMT_NF4 = 0,
+  E4B_FMT_NF4_DQ = 1,
+  E4B_FMT_MXFP4 = 2,
+  E4B_FMT_INT8 = 3,
+  E4B_FMT_FP8 = 4
+} e4b_fmt;
 
 /* A frozen stack [E, N, K] (K contiguous) in one of the formats above: the packed codes
  * plus per-block scales that the method page ("The abstraction that fails, and what
  * replaces it") names as the frozen packed base.  All pointers are device pointers owned
  * by the caller.
- *  codes   : uint8 [E, N, K/2]
- *  scale   : NF4: float [E, N, K/64]; NF4_DQ: uint8 [E, N, K/64]; MXFP4: uint8 [E, N, K/32]
+ *  codes   : uint8 [E, N, K/2] (4-bit formats) or [E, N, K] (INT8, FP8)
+ *  scale   : NF4, INT8, FP8: float [E, N, K/64]; NF4_DQ: uint8 [E, N, K/64];
+ *            MXFP4: uint8 [E, N, K/32]
  *  scale2  : NF4_DQ only: float [ceil(E*N*K/64 / 256)]; NULL otherwise.
  *  dq_table: NF4_DQ only: float [256], the value of each 8-bit absmax code:
  *            absmax = fp32(dq_table[c] * scale2[b / 256]).  NULL = the built-in linear
  *            code fp32(c / 255).  Must be NULL for the other formats.
  *  codebook: NF4 and NF4_DQ: float [16], the value of each 4-bit code,
  *            w = bf16(fp32(codebook[q] * absmax)).  NULL = the built-in NormalFloat
- *            table.  Must be NULL for MXFP4 (its E2M1 values are fixed by the format).
+ *            table.  Must be NULL for the other formats (their code values are fixed).
  * A non-NULL table for a format that has none is E4B_ERR_INVALID_ARG. */
 typedef struct {
   int32_t fmt;

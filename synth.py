@@ -25,8 +25,7 @@ import dataclasses
 
 import numpy as np
 
-FMT_NF4, FMT_NF4_DQ, FMT_MXFP4 = 0, 1, 2
-FMT_NAMES = {"nf4": FMT_NF4, "nf4_dq": FMT_NF4_DQ, "mxfp4": FMT_MXFP4}
+FMT_NAMES = {"nf4": 0, "nf4_dq": 1, "mxfp4": 2, "int8": 3, "fp8": 4}
 
 
 @dataclasses.dataclass(frozen=True)

@@ -142,6 +142,7 @@ def test_dgrad_needs_training_forward(L):
 def test_quantize_and_dequant_rejections(L):
     lib = L.lib()
     assert lib.e4b_quantize(7, 1, 8, 64, 0x1, 0x2, 0x3, None, None) == L.E4B_ERR_UNSUPPORTED
+    assert lib.e4b_quantize(5, 1, 8, 64, 0x1, 0x2, 0x3, None, None) == L.E4B_ERR_UNSUPPORTED
     assert lib.e4b_quantize(0, 1, 8, 96, 0x1, 0x2, 0x3, None, None) == L.E4B_ERR_INVALID_ARG
     assert lib.e4b_quantize(1, 1, 8, 64, 0x1, 0x2, 0x3, None, None) == L.E4B_ERR_INVALID_ARG
     q = L.QWeight(0, 2, 8, 64, 0x1, 0x2, None)
@@ -204,7 +205,9 @@ def test_code_table_rejections(L):
     L.reset_stats()
     cases = [L.QWeight(0, 1, 8, 64, 0x1, 0x2, None, 0x3, None),        # NF4 + dq_table
              L.QWeight(2, 1, 8, 64, 0x1, 0x2, None, 0x3, None),        # MXFP4 + dq_table
-             L.QWeight(2, 1, 8, 64, 0x1, 0x2, None, None, 0x4)]        # MXFP4 + codebook
+             L.QWeight(2, 1, 8, 64, 0x1, 0x2, None, None, 0x4),        # MXFP4 + codebook
+             L.QWeight(3, 1, 8, 64, 0x1, 0x2, None, None, 0x4),        # INT8 + codebook
+             L.QWeight(4, 1, 8, 64, 0x1, 0x2, None, 0x3, None)]        # FP8 + dq_table
     for q in cases:
         assert lib.e4b_dequant(ctypes.byref(q), 0, 0x10, None, None) == L.E4B_ERR_INVALID_ARG
     ok = L.QWeight(1, 1, 8, 64, 0x1, 0x2, 0x5, 0x3, 0x4)               # NF4_DQ + both tables

@@ -26,7 +26,7 @@ def _weights(E, N, K, seed, scale=0.02):
     return w
 
 
-@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4", "int8", "fp8"])
 @pytest.mark.parametrize("E,N,K", [(2, 96, 128), (3, 64, 2880), (1, 8, 64 * 300)])
 def test_dequant_bitexact(fmt, E, N, K):
     print(f"dequant {fmt} {E}x{N}x{K}", flush=True)
@@ -42,13 +42,18 @@ def test_dequant_bitexact(fmt, E, N, K):
     assert np.array_equal(f1.cpu().numpy(), f_ref[E - 1])
 
 
-@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4", "int8", "fp8"])
 def test_dequant_every_code(fmt):
-    """All 256 code bytes under a spread of block scales."""
+    """All 256 code bytes under a spread of block scales (FP8: every finite code)."""
     E, N, K = 1, 64, 512
     rng = np.random.default_rng(3)
-    codes = np.tile(np.arange(256, dtype=np.uint8), E * N * K // 2 // 256)
-    if fmt == "nf4":
+    byte = fmt in ("int8", "fp8")
+    codes = np.tile(np.arange(256, dtype=np.uint8), E * N * K // (1 if byte else 2) // 256)
+    if fmt == "fp8":
+        codes[(codes & 0x7F) == 0x7F] = 0  # the two NaN codes never occur in a stack
+    if byte:
+        q = oracle.QWeight(fmt, E, N, K, codes, rng.uniform(0, 0.1, E * N * K // 64).astype(np.float32))
+    elif fmt == "nf4":
         scale = rng.uniform(0, 3, E * N * K // 64).astype(np.float32)
         q = oracle.QWeight(fmt, E, N, K, codes, scale)
     elif fmt == "nf4_dq":
@@ -117,7 +122,7 @@ def test_layer_stack_tables(T):
     assert not torch.equal(plain["y"], out["y"])
 
 
-@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nf4", "nf4_dq", "mxfp4", "int8", "fp8"])
 def test_quantize_bitexact(fmt):
     E, N, K = 3, 80, 2880
     w = _weights(E, N, K, seed=11)

@@ -45,6 +45,10 @@ SHAPES = [
     ("mxfp4", 6, 192, 192, 100, 4, 8, 16.0, "mxfp4"),
     ("one-expert", 1, 128, 128, 200, 1, 8, 16.0, "nf4"),
     ("rank128", 2, 128, 256, 40, 2, 128, 256.0, "nf4"),
+    ("int8-few", 4, 192, 320, 20, 2, 16, 32.0, "int8"),
+    ("int8", 5, 192, 320, 150, 3, 16, 32.0, "int8"),
+    ("fp8-few", 4, 256, 192, 20, 2, 8, 16.0, "fp8"),
+    ("fp8", 3, 256, 448, 300, 2, 64, 128.0, "fp8"),
 ]
 
 
@@ -183,6 +187,8 @@ EXPAND_SHAPES = [
     ("x-dq", 4, 320, 192, 150, 2, 8, 16.0, "nf4_dq"),
     ("x-mxfp4", 6, 192, 192, 100, 4, 8, 16.0, "mxfp4"),
     ("x-multi-tile", 3, 256, 448, 300, 2, 64, 128.0, "nf4"),
+    ("x-int8", 4, 192, 320, 150, 3, 16, 32.0, "int8"),
+    ("x-fp8", 3, 256, 192, 150, 2, 8, 16.0, "fp8"),
 ]
 
 
