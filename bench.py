@@ -27,10 +27,12 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="large")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="large workload: skip the decode, many-small and mxfp4 lines")
     p.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = automatic")
     p.add_argument("--copy-calib", action="store_true",
                    help="run a plain 256 MiB device copy first (HBM counter calibration)")
@@ -56,31 +58,67 @@ def csrc_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_work(s, fam: str, M: int, touched: int) -> tuple[float, float]:
-    """Algorithmic (flops, bytes) of ONE launch of a kernel family on workload s.
-    flops = 2*rows*cols*reduction over the base and LoRA products the step performs
-    on routed rows only; bytes = packed weights + scales of the `touched` experts (those
-    with at least one routed row) read once + their adapter rows + the operand and output
-    rows the kernel must touch."""
-    E, H, I, r = touched, s.H, s.I, s.r
-    wbytes_per_elem = 0.5 + (4.0 / 64 if s.fmt == "nf4" else 1.0 / 64 if s.fmt == "nf4_dq" else 1.0 / 32)
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop/byte where the two roofs meet
+
+
+def step_work(s, fam: str, touched: int, train: bool, nsplit: int = 1) -> tuple[float, float]:
+    """Algorithmic (flops, bytes) of ONE STEP's launches of a kernel family on workload s.
+    flops = 2*rows*cols*reduction over the base and LoRA products on routed rows only (no tile
+    padding); bytes = every operand and output the family must touch once: packed weights and
+    scales of the `touched` experts (those with routed rows), their adapter rows, activation
+    rows in and out.  The same rules hold for every workload (training or forward only)."""
+    M, T, k, E, H, I, r = s.M, s.T, s.k, touched, s.H, s.I, s.r
+    wb = 0.5 + (4.0 / 64 if s.fmt == "nf4" else 1.0 / 64 if s.fmt == "nf4_dq" else 1.0 / 32)
+    if s.fmt in ("int8", "fp8"):
+        wb = 1.0 + 4.0 / 64
+    bf, f4 = 2, 4
     if fam == "gemm_gate_up":
         fl = 2.0 * M * 2 * I * H + 2.0 * M * 2 * I * r
-        by = E * 2 * I * H * wbytes_per_elem + E * 2 * I * r * 2 + M * H * 2 + M * I * 2 + M * r * 2
-        if s.name != "large" and not s.name.startswith("decode"):
-            by += M * 2 * I * 2  # saved pre-activations (training)
-    elif fam == "gemm_gate_up_dgrad":
-        fl = 2.0 * M * H * 2 * I + 2.0 * M * H * r
-        by = E * 2 * I * H * wbytes_per_elem + M * 2 * I * 2 + M * H * 4
+        by = E * 2 * I * H * wb + E * 2 * I * r * bf + M * H * bf + M * r * bf + M * I * bf
+        by += M * 2 * I * bf if train else 0  # saved pre-activation
     elif fam == "gemm_down":
         fl = 2.0 * M * H * I + 2.0 * M * H * r
-        by = E * H * I * wbytes_per_elem + E * H * r * 2 + M * I * 2 + M * r * 2 + M * H * 4
+        by = E * H * I * wb + E * H * r * bf + M * I * bf + M * r * bf + M * H * f4 * nsplit
     elif fam == "gemm_down_dgrad":
         fl = 2.0 * M * I * H + 2.0 * M * I * r
-        by = E * H * I * wbytes_per_elem + M * H * 2 + 2 * M * 2 * I * 2
+        by = E * H * I * wb + E * I * r * bf + M * H * bf + M * r * bf + 2 * M * 2 * I * bf
+    elif fam == "gemm_gate_up_dgrad":
+        fl = 2.0 * M * H * 2 * I + 2.0 * M * H * r
+        by = E * 2 * I * H * wb + E * H * r * bf + M * 2 * I * bf + M * r * bf + M * H * f4
+    elif fam == "lora_a":  # z1 = A1 x, z2 = A2 h (+ u2 = B2^T dO, u1 = B1^T dG when training)
+        fl = 2.0 * M * r * (H + I) + (2.0 * M * r * (H + 2 * I) if train else 0)
+        by = M * (H + I) * bf + E * r * (H + I) * bf + 2 * M * r * bf
+        if train:
+            by += M * (H + 2 * I) * bf + E * r * (H + 2 * I) * bf + 2 * M * r * bf
+    elif fam == "wgrad":  # dB1, dA1, dB2, dA2: reductions over each expert's rows
+        fl = 2.0 * M * r * (2 * I + H + H + I)
+        by = M * (2 * I + H + H + I) * bf + 4 * M * r * bf + s.E * r * (2 * I + H + H + I) * f4
+    elif fam == "combine":
+        fl, by = 0.0, M * H * f4 * nsplit + T * H * bf + T * k * 8
+    elif fam == "combine_bwd":
+        fl, by = 0.0, T * H * bf + M * H * f4 + M * H * bf + T * k * 12
+    elif fam == "unpermute":
+        fl, by = 0.0, M * H * f4 + T * H * bf + T * k * 4
+    elif fam == "route":
+        fl, by = 0.0, M * 4 + 2 * M * 4 + 2 * (s.E + 1) * 4
+    elif fam == "transpose":  # the four adapter matrices read and written once
+        fl, by = 0.0, 2 * s.E * r * (2 * I + H + H + I) * bf
+    elif fam == "expand":  # packed stacks in, bf16 copies out
+        fl, by = 0.0, s.E * 3 * I * H * (wb + bf)
     else:
-        fl, by = 0.0, 0.0
+        raise KeyError(f"no algorithmic work formula for kernel family {fam!r}")
     return fl, by
+
+
+def roof_of(fl: float, by: float, ms: float) -> dict:
+    """Roofline entry of `ms` milliseconds of work: bound by MFMA (bf16 peak) when the
+    arithmetic intensity is above the ridge, else by HBM."""
+    sec = ms / 1e3
+    if fl > 0 and fl / max(by, 1.0) >= RIDGE:
+        return {"bound": "mfma", "achieved": fl / sec / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": fl / sec / 1e12 / PEAK_BF16_TFLOPS}
+    return {"bound": "hbm", "achieved": by / sec / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": by / sec / 1e9 / PEAK_HBM_GBS}
 
 
 def step_flops(s, with_bwd: bool) -> float:
@@ -236,35 +274,18 @@ def router_timing(s, reps: int = 50) -> dict:
     return res
 
 
-def main():
-    a = parse()
-    if a.summarize_stats:
-        summarize_stats(*a.summarize_stats, a.command)
-        return
-    if a.summarize_pmc:
-        summarize_pmc(*a.summarize_pmc, a.command)
-        return
-    if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is described in "
-                                   "DESIGN.md and not implemented", "n_gpus": a.gpus}))
-        sys.exit(2)
+def measure(s, a, inp, steps: int, warmup: int, kernel_steps: int) -> dict:
+    """Time `steps` steps of workload s (inputs resident in HBM) and return the result fields:
+    ms/step from HIP events around the timed steps (graph replays for forward-only workloads),
+    then, in a separate pass outside that window, per-kernel-family times from the library's
+    own events on its launch stream, and the roofline of the dominant family."""
     import numpy as np
     import torch
 
-    import synth
     from grouped_nf4_gemm_amd import LoRA, MoELayer, QStack, timing_enable, timing_read
 
-    s = synth.WORKLOADS[a.workload]
     with_bwd = not s.name.startswith("decode")
     dev = "cuda"
-    if a.copy_calib:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    inp = synth.make_inputs(s)
     b16 = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
     w_gu = QStack.quantize(s.fmt, torch.from_numpy(inp.W1).to(dev))
     w_dn = QStack.quantize(s.fmt, torch.from_numpy(inp.W2).to(dev))
@@ -284,39 +305,31 @@ def main():
                               None if q.scale2 is None else q.scale2.clone())
         cl = lambda l: LoRA(l.A.clone(), l.B.clone(), l.scaling)
         layers.append(MoELayer(cq(w_gu), cq(w_dn), cl(l_gu), cl(l_dn), s.T, s.k, train=False))
-    layer = layers[0]
     y = torch.empty(s.T, s.H, dtype=torch.bfloat16, device=dev)
     dx = torch.empty_like(y)
     d_topw = torch.empty(s.T, s.k, dtype=torch.float32, device=dev)
-    grads = None
-    nstep = 0
+    state = {"grads": None, "n": 0}
 
     def step():
-        nonlocal grads, nstep
-        layer = layers[nstep % len(layers)]
-        nstep += 1
+        layer = layers[state["n"] % len(layers)]
+        state["n"] += 1
         layer.forward(x, ids, topw, y)
         if with_bwd:
             layer.dgrad(ids, topw, dy, dx, d_topw)
-            grads = layer.wgrad(x, grads)
+            state["grads"] = layer.wgrad(x, state["grads"])
 
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    timing_read()  # drop warmup events
-    timing_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(a.steps):
+    for _ in range(steps):
         step()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    timing_enable(False)
-    per_kernel = timing_read()
-    ms = ev0.elapsed_time(ev1) / a.steps
+    ms = ev0.elapsed_time(ev1) / steps
     ms_eager = ms
     use_graph = a.graph == "on" or (a.graph == "auto" and not with_bwd)
     graph_steps = 0
@@ -327,7 +340,7 @@ def main():
         if with_bwd:
             raise SystemExit("--graph applies to forward-only workloads")
         y_ref = y.clone()
-        reps = max(1, -(-a.steps // len(layers)))
+        reps = max(1, -(-steps // len(layers)))
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -353,46 +366,111 @@ def main():
         graph_steps = reps * len(layers)
         ms = g0.elapsed_time(g1) / graph_steps
         del graph
-    routed = s.M
-    value = routed / (ms / 1e3)
-
-    # dominant kernel and its roofline
-    dom = max(per_kernel.items(), key=lambda kv: kv[1][1])
-    dom_name, (dom_n, dom_ms) = dom
-    avg_ms = dom_ms / dom_n
+    # per-kernel pass, outside the timed window
+    timing_read()
+    timing_enable(True)
+    for _ in range(kernel_steps):
+        step()
+    torch.cuda.synchronize()
+    timing_enable(False)
+    per_kernel = timing_read()
     touched = int(np.unique(inp.ids[(inp.ids >= 0) & (inp.ids < s.E)]).size)
-    fl, by = kernel_work(s, dom_name, routed, touched)
-    if s.name.startswith("decode"):
-        roof = {"bound": "hbm", "achieved": by / (avg_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": fl / (avg_ms / 1e3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = dom_name
-    roof["avg_launch_ms"] = avg_ms
-    roof["traffic"] = read_traffic(dom_name, s.name)
+    kernels = {}
+    for fam, (n, tot) in sorted(per_kernel.items(), key=lambda kv: -kv[1][1]):
+        kms = tot / kernel_steps
+        fl, by = step_work(s, fam, touched, with_bwd)
+        r = roof_of(fl, by, kms)
+        kernels[fam] = {"ms_per_step": kms, "launches_per_step": n / kernel_steps, "bound": r["bound"],
+                        "frac": r["frac"]}
+    dom = max(kernels, key=lambda f: kernels[f]["ms_per_step"])
+    n_dom = kernels[dom]["launches_per_step"]
+    avg_ms = kernels[dom]["ms_per_step"] / n_dom
+    fl, by = step_work(s, dom, touched, with_bwd)
+    roof = roof_of(fl / n_dom, by / n_dom, avg_ms)
+    roof.update({"kernel": dom, "avg_launch_ms": avg_ms, "traffic": read_traffic(dom, s.name)})
+    del layers, w_gu, w_dn
+    torch.cuda.empty_cache()
+    return {
+        "value": s.M / (ms / 1e3), "ms_per_step": ms, "ms_per_step_eager": ms_eager,
+        "steps": graph_steps if use_graph else steps,
+        "timed": ("%d replays of a HIP graph of %d forwards" % (graph_steps // ncopy, ncopy))
+        if use_graph else "%d eager steps" % steps,
+        "touched": touched, "layer_copies": ncopy, "wall_s": wall,
+        "step_tflops": step_flops(s, with_bwd) / (ms / 1e3) / 1e12,
+        "roofline": roof, "kernels": kernels,
+    }
 
+
+SECONDARY = ("decode-t1", "decode-t8", "decode-t64", "many-small", "mxfp4")
+
+
+def main():
+    a = parse()
+    if a.summarize_stats:
+        summarize_stats(*a.summarize_stats, a.command)
+        return
+    if a.summarize_pmc:
+        summarize_pmc(*a.summarize_pmc, a.command)
+        return
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is described in "
+                                   "DESIGN.md and not implemented", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+
+    import synth
+
+    s = synth.WORKLOADS[a.workload]
+    with_bwd = not s.name.startswith("decode")
+    if a.copy_calib:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    inp = synth.make_inputs(s)
+    res = measure(s, a, inp, a.steps, a.warmup, min(a.steps, 5))
     out = {
         "metric": "routed tokens/s (NF4+LoRA grouped MoE layer, fwd+dgrad+wgrad step)" if with_bwd
         else "routed tokens/s (NF4+LoRA grouped MoE layer, forward)",
-        "value": value, "unit": "routed tokens/s", "n_gpus": 1, "steps": graph_steps if use_graph else a.steps, "warmup": a.warmup,
-        "ms_per_step": ms, "ms_per_step_eager": ms_eager,
-        "timed": ("%d replays of a HIP graph of %d forwards" % (graph_steps // len(layers), len(layers)))
-        if use_graph else "%d eager steps" % a.steps,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "value": res["value"], "unit": "routed tokens/s", "n_gpus": 1, "steps": res["steps"],
+        "warmup": a.warmup, "ms_per_step": res["ms_per_step"], "ms_per_step_eager": res["ms_per_step_eager"],
+        "timed": res["timed"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded; random-init weights quantised to " + s.fmt + ")",
         "config": {"workload": s.name, "E": s.E, "H": s.H, "I": s.I, "T": s.T, "topk": s.k, "r": s.r,
                    "alpha": s.alpha, "weights": s.fmt, "global_batch": s.T, "parallelism": "none (1 GPU)",
-                   "layer_copies": len(layers), "experts_touched": touched},
-        "step_tflops": step_flops(s, with_bwd) / (ms / 1e3) / 1e12,
-        "step_mfma_frac": step_flops(s, with_bwd) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-        "wall_s": wall,
-        "roofline": roof,
-        "kernels_ms_per_step": {k: v[1] / a.steps for k, v in sorted(per_kernel.items(), key=lambda kv: -kv[1][1])},
+                   "layer_copies": res["layer_copies"], "experts_touched": res["touched"]},
+        "step_tflops": res["step_tflops"], "step_mfma_frac": res["step_tflops"] / PEAK_BF16_TFLOPS,
+        "wall_s": res["wall_s"], "roofline": res["roofline"],
+        "kernels": {k: {kk: round(vv, 5) for kk, vv in v.items() if kk != "bound"} | {"bound": v["bound"]}
+                    for k, v in res["kernels"].items()},
     }
     out["router"] = router_timing(s)
-    del layer, layers, w_gu, w_dn
-    torch.cuda.empty_cache()
+    if a.workload == "large" and not a.no_secondary:
+        # the other configurations of the same layer, measured in the same run (their own
+        # inputs; the three decode batch sizes share one set of weights)
+        sec = {}
+        dec_w = None
+        for name in SECONDARY:
+            s2 = synth.WORKLOADS[name]
+            if name.startswith("decode"):
+                inp2 = synth.make_inputs(s2, weights=dec_w is None)
+                if dec_w is None:
+                    dec_w = (inp2.W1, inp2.W2)
+                inp2.W1, inp2.W2 = dec_w
+                r2 = measure(s2, a, inp2, 40, 5, 5)
+            else:
+                r2 = measure(s2, a, synth.make_inputs(s2), 20, 3, 5)
+            top = sorted(r2["kernels"].items(), key=lambda kv: -kv[1]["ms_per_step"])[:4]
+            sec[name] = {"value": r2["value"], "ms_per_step": r2["ms_per_step"], "timed": r2["timed"],
+                         "roofline": {k: r2["roofline"][k] for k in ("kernel", "bound", "frac", "achieved", "unit",
+                                                                    "avg_launch_ms")},
+                         "kernels": {k: {"ms_per_step": round(v["ms_per_step"], 5), "frac": round(v["frac"], 4)}
+                                     for k, v in top}}
+            print(f"# secondary {name}: {r2['ms_per_step']:.4f} ms/step, {r2['roofline']['kernel']} "
+                  f"{r2['roofline']['frac']:.3f} of {r2['roofline']['bound']}", file=sys.stderr, flush=True)
+        out["secondary"] = sec
     if not a.no_cpu_baseline:
         n_tok = a.cpu_sample_tokens or (320 if with_bwd else 16)
         out["cpu_baseline"] = cpu_baseline(s, inp, n_tok)
