@@ -15,6 +15,7 @@ E4B_OK, E4B_ERR_INVALID_ARG, E4B_ERR_UNSUPPORTED, E4B_ERR_WORKSPACE, E4B_ERR_HIP
 FMT = {"nf4": 0, "nf4_dq": 1, "mxfp4": 2, "int8": 3, "fp8": 4}
 E4B_TRAIN = 1
 E4B_EXPAND = 2
+E4B_SEPARATE = 4
 
 EXPORTS = [
     "e4b_version", "e4b_status_str", "e4b_moe_workspace_size", "e4b_moe_fwd", "e4b_moe_dgrad",

@@ -65,7 +65,7 @@ bool last_launch_ok() { return hipGetLastError() == hipSuccess; }
 // ------------------------------------------------------------------ workspace layout
 struct Layout {
   size_t cnt, off, perm, inv, z1, z2, G, h, O, dO, u2, dG, u1, dXp, A1T, B1T, A2T, B2T, part, W1x, W2x,
-      total;
+      zp, ctr, total;
 };
 static constexpr size_t NONE = ~(size_t)0;
 // Activations and stacks that the 4-bit GEMMs stream with buffer loads must each stay
@@ -102,7 +102,12 @@ static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
   L.G = train ? take(M * 2 * I * 2) : NONE;
   L.h = take(M * I * 2);
   // the decode-shaped forward keeps up to SMALL_MAX_SPLITS partial sums of O (inference only)
-  L.O = take((M <= (size_t)SMALL_M_MAX && !train ? SMALL_MAX_SPLITS : 1) * M * H * 4);
+  const bool decode = M <= (size_t)SMALL_M_MAX && !train;
+  L.O = take((decode ? SMALL_MAX_SPLITS : 1) * M * H * 4);
+  // two-launch decode forward: z2 partial sums of the gate_up workgroups (at most one per 8
+  // strips of 16 h columns) and one arrival counter per 256 output columns of down
+  L.zp = decode ? take((size_t)cdiv(cdiv(I, 16), 8) * M * r2 * 4) : NONE;
+  L.ctr = decode ? take((size_t)cdiv(H, 256) * 4) : NONE;
   if (train) {
     L.dO = take(M * H * 2);
     L.u2 = take(M * r2 * 2);
@@ -161,7 +166,7 @@ static e4b_status check_desc(const e4b_moe_desc *d) {
   const int64_t M = (int64_t)d->T * d->topk;
   if ((int64_t)d->T * d->H * 2 > BUF_LIMIT || M * d->H * 4 > BUF_LIMIT || M * 2 * d->I * 2 > BUF_LIMIT)
     return E4B_ERR_INVALID_ARG;
-  if (d->flags & ~(E4B_TRAIN | E4B_EXPAND)) return E4B_ERR_INVALID_ARG;
+  if (d->flags & ~(E4B_TRAIN | E4B_EXPAND | E4B_SEPARATE)) return E4B_ERR_INVALID_ARG;
   if (const e4b_act *a = d->act) {
     if (a->kind == E4B_ACT_SWIGLU) {
       if (a->b_gu || a->b_dn) return E4B_ERR_INVALID_ARG;  // the stock epilogue has no biases
@@ -274,6 +279,58 @@ static e4b_status validate_layer(const e4b_moe_desc *d, const e4b_qweight *w_gu,
   return E4B_OK;
 }
 
+// Decode-shaped inference forward as two launches (see E4B_SEPARATE): the gate_up launch
+// routes inside each workgroup, forms z1 for its rows and the z2 partial sums over its h
+// columns, and zeroes the down launch's arrival counters; the down launch adds the z2
+// partial sums (first split) and forms y in the last workgroup of each column range.
+static e4b_status moe_fwd_two_launch(const e4b_moe_desc &d, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
+                                     const e4b_lora *l_gu, const e4b_lora *l_dn, const uint16_t *x,
+                                     const int32_t *ids, const float *topw, uint16_t *y, void *ws, const Layout &L,
+                                     int r1, int r2, hipStream_t s) {
+  const int M = d.T * d.topk, E = d.E, H = d.H, I = d.I;
+  GroupedArgs gu{};
+  gu.off = nullptr; gu.E = E; gu.M = M; gu.N = I; gu.K = H;
+  gu.A = x; gu.lda = H; gu.a_gather = nullptr; gu.a_gdiv = d.topk;
+  gu.a_bytes = (uint32_t)((int64_t)d.T * H * 2);
+  gu.q = qstack(w_gu);
+  gu.xb = r1 ? l_gu->B : nullptr; gu.xb_estride = (int64_t)2 * I * r1; gu.ldxb = r1; gu.r = r1;
+  gu.C = at<uint16_t>(ws, L.h); gu.ldc = I; gu.alpha = 1.0f;
+  gu.Gout = nullptr; gu.ldg = 2 * I; gu.I = I;
+  set_act(d, gu, d.act ? d.act->b_gu : nullptr, (int64_t)2 * I);
+
+  GroupedArgs dn{};
+  dn.off = at<int32_t>(ws, L.off); dn.E = E; dn.M = M; dn.N = H; dn.K = I;
+  dn.A = at<uint16_t>(ws, L.h); dn.lda = I; dn.a_gdiv = 1;
+  dn.a_bytes = (uint32_t)((int64_t)M * I * 2);
+  dn.q = qstack(w_dn);
+  dn.xb = r2 ? l_dn->B : nullptr; dn.xb_estride = (int64_t)H * r2; dn.ldxb = r2; dn.r = r2;
+  dn.C = at<float>(ws, L.O); dn.ldc = H; dn.alpha = 1.0f; dn.I = I;
+  set_act(d, dn, d.act ? d.act->b_dn : nullptr, H);
+  const int nsplit = small_down_splits(M, E, H, I);
+
+  DecodeFuse f{};
+  f.on = 1;
+  f.ids = ids; f.topk = d.topk;
+  f.cnt = at<int32_t>(ws, L.cnt); f.off = at<int32_t>(ws, L.off);
+  f.perm = at<int32_t>(ws, L.perm); f.inv = at<int32_t>(ws, L.inv);
+  f.ctr = at<int32_t>(ws, L.ctr);
+  f.a1 = r1 ? l_gu->A : nullptr; f.a1_estride = (int64_t)r1 * H; f.s1 = r1 ? l_gu->scaling : 0.0f;
+  f.a2 = r2 ? l_dn->A : nullptr; f.a2_estride = (int64_t)r2 * I; f.r2 = r2; f.s2 = r2 ? l_dn->scaling : 0.0f;
+  f.zp = at<float>(ws, L.zp);
+  f.topw = topw; f.T = d.T; f.y = y;
+  f.split_stride = (int64_t)M * H; f.nsplit = nsplit;
+  gu.fz = f;
+  dn.fz = f;
+  f.nparts = small_gate_up_parts(gu);
+  f.nctr = small_down_ranges(dn, nsplit);
+  if (f.nparts > cdiv(cdiv(I, 16), 8) || f.nctr > cdiv(H, 256)) return E4B_ERR_UNSUPPORTED;  // the layout's bounds
+  gu.fz = f;
+  dn.fz = f;
+  E4B_LAUNCH(launch_small_gate_up(gu, s));
+  E4B_LAUNCH(launch_small_down(dn, nsplit, s));
+  return E4B_OK;
+}
+
 // The forward as a stream-ordered kernel sequence over a workspace of ws_bytes bytes.
 static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, const e4b_qweight *w_dn,
                           const e4b_lora *l_gu, const e4b_lora *l_dn, const uint16_t *x, const int32_t *ids,
@@ -295,6 +352,9 @@ static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, con
   uint16_t *W1x = L.W1x == NONE ? nullptr : at<uint16_t>(ws, L.W1x);
   uint16_t *W2x = L.W2x == NONE ? nullptr : at<uint16_t>(ws, L.W2x);
 
+  if (M <= SMALL_M_MAX && !fmt_8bit(w_gu->fmt) && !(d.flags & (E4B_TRAIN | E4B_SEPARATE)) && E <= FUSE_E_MAX &&
+      r1 <= FUSE_R_MAX && r2 <= FUSE_R_MAX)
+    return M == 0 ? E4B_OK : moe_fwd_two_launch(d, w_gu, w_dn, l_gu, l_dn, x, ids, topw, y, ws, L, r1, r2, s);
   E4B_LAUNCH(launch_route(ids, M, E, cnt, off, perm, inv, s));
   if (M == 0) return E4B_OK;
   if (W1x) {
@@ -404,7 +464,7 @@ e4b_status e4b_moe_fwd_noalloc(const e4b_moe_desc *desc, const e4b_qweight *w_gu
                                const int32_t *ids, const float *topw, uint16_t *y, void *stream) {
   int r1, r2;
   E4B_TRY(validate_layer(desc, w_gu, w_dn, l_gu, l_dn, &r1, &r2));
-  if (desc->flags != 0) return E4B_ERR_INVALID_ARG;  // inference only, no bf16 stack copies
+  if (desc->flags & ~E4B_SEPARATE) return E4B_ERR_INVALID_ARG;  // inference only, no bf16 stack copies
   if (layout(*desc, r1, r2).total > (size_t)E4B_NOALLOC_SCRATCH_BYTES) return E4B_ERR_WORKSPACE;
   if (desc->T > 0 && (!x || !ids || !topw || !y)) return E4B_ERR_INVALID_ARG;
   void *ws = nullptr;

@@ -40,6 +40,36 @@ struct LaunchScope {
 };
 bool last_launch_ok();
 
+// Two-launch decode forward (few routed rows, inference).  The gate_up launch also routes
+// the raw ids inside every workgroup, forms z1 = s1 A1[e] x for the workgroup's own rows and
+// writes the workgroup's partial sums of z2 = s2 A2[e] h over its h columns; the down launch
+// adds those partial sums (split 0) and the last of its workgroups to finish a column range
+// forms y over that range.  on = 0: every operand comes from the grouped-GEMM fields.
+struct DecodeFuse {
+  int on;
+  const int32_t *ids;               // [M] expert of routed row f = t * topk + j
+  int topk;
+  int32_t *cnt, *off, *perm, *inv;  // routing, written by one gate_up workgroup
+  int32_t *ctr;                     // down launch: one arrival counter per column range
+  int nctr;                         // zeroed by the gate_up launch
+  const uint16_t *a1;               // gate_up LoRA A [E][r1][H] (r1 = the launch's r)
+  int64_t a1_estride;
+  float s1;
+  const uint16_t *a2;               // down LoRA A [E][r2][I]
+  int64_t a2_estride;
+  int r2;
+  float s2;
+  float *zp;                        // z2 partial sums [nparts][M][r2]
+  int nparts;
+  const float *topw;                // combine: [T][topk]
+  int T;
+  uint16_t *y;                      // [T][ldc of the down launch]
+  int64_t split_stride;             // floats between the down launch's split partial sums
+  int nsplit;
+};
+// Fused decode limits: workgroup routing scratch in LDS and one 32-wide MFMA tile of rank.
+constexpr int FUSE_E_MAX = 256, FUSE_R_MAX = 32;
+
 // Operands of one grouped GEMM over expert segments (see gemm.hpp).
 struct GroupedArgs {
   const int32_t *off;
@@ -91,6 +121,7 @@ struct GroupedArgs {
   // order, down [E][H]
   const uint16_t *bias;
   int64_t bias_estride;
+  DecodeFuse fz;
 };
 
 enum BKind : int { B_QNK = 0, B_QKN = 1, B_DENSE = 2 };
@@ -148,6 +179,10 @@ bool launch_small_lora_a(const GroupedArgs &a, hipStream_t s);
 bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s);
 int small_down_splits(int M, int E, int N, int K);
 bool launch_small_down(const GroupedArgs &a, int splits, hipStream_t s);
+// Workgroups along the strip dimension of the decode-shaped gate_up and down launches (the
+// z2 partial-sum count and the arrival-counter count of the two-launch forward).
+int small_gate_up_parts(const GroupedArgs &a);
+int small_down_ranges(const GroupedArgs &a, int splits);
 // Router: top-k ids (larger logit first, ties to the lower id) and the fp32 softmax over
 // them, E <= 1024, k <= 64; its gradient to the logits with the ids held fixed.
 bool launch_router_topk(const float *logits, int T, int E, int k, int32_t *ids, float *w, hipStream_t s);

@@ -22,6 +22,8 @@
 //  * gate_up rows come as 16 gate rows and the 16 up rows of the same h columns, so the
 //    SwiGLU epilogue pairs lanes n and n + 16.  down splits K over workgroups and writes
 //    fp32 partial sums that the combine adds in split order.
+#include <type_traits>
+
 #include "gemm.hpp"
 #include "kernels.hpp"
 
@@ -139,7 +141,168 @@ __device__ __forceinline__ int stage_swz(int rho, int p) {
 }
 constexpr int stage_bytes(int ch) { return SM_WAVES * 32 * ch * 32; }
 
-template <int FMT, int SPW, int EPI, int DC>
+// ------------------------------------------------------------ two-launch decode forward
+// Routing of M <= 256 routed rows inside one workgroup, with the result of the route kernel:
+// per-wave counts, their scan over the waves and over the experts, then stable ranks by
+// ballot.  LDS: [4][E+1] counts, [E+1] cnt, [E+1] off, [M] perm, [M] inv.
+struct LdsRoute {
+  int32_t *cnt, *off, *perm, *inv;
+};
+__host__ __device__ constexpr size_t route_lds_bytes(int E, int M) { return (size_t)(6 * (E + 1) + 2 * M) * 4; }
+
+__device__ __forceinline__ LdsRoute route_in_lds(const int32_t *__restrict__ ids, int M, int E, int32_t *sm) {
+  const int KE = E + 1, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int32_t *wc = sm, *cnt = sm + 4 * KE, *off = cnt + KE, *perm = off + KE, *inv = perm + M;
+  for (int i = tid; i < 4 * KE; i += SM_THREADS) wc[i] = 0;
+  const int f = 64 * w + lane;
+  const bool act = w < 4 && f < M;
+  const int e = act ? ids[f] : 0;
+  const bool valid = act && e >= 0 && e < E;
+  const int key = valid ? e : E;
+  __syncthreads();
+  if (act) atomicAdd(&wc[w * KE + key], 1);
+  __syncthreads();
+  for (int k = tid; k < KE; k += SM_THREADS) {
+    int run = 0;
+    for (int ww = 0; ww < 4; ++ww) {
+      const int c = wc[ww * KE + k];
+      wc[ww * KE + k] = run;
+      run += c;
+    }
+    cnt[k] = run;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int base = 0;
+    for (int c = 0; c < E; c += 64) {
+      const int ee = c + lane;
+      const int v = ee < E ? cnt[ee] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (lane >= d) incl += u;
+      }
+      if (ee < E) off[ee] = base + incl - v;
+      base += __shfl(incl, 63);
+    }
+    if (lane == 0) off[E] = base;
+  }
+  __syncthreads();
+  if (w < 4) {
+    const int nbits = 32 - __clz(E);
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    uint64_t eq = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      eq &= bit ? m : ~m;
+    }
+    const int rank = __popcll(eq & lt);
+    if (valid) {
+      const int pos = off[e] + wc[w * KE + e] + rank;
+      perm[pos] = f;
+      inv[f] = pos;
+    } else if (act) {
+      inv[f] = -1;
+    }
+  }
+  __syncthreads();
+  return LdsRoute{cnt, off, perm, inv};
+}
+
+// One gate_up workgroup hands the routing to the down launch (and to the caller's
+// workspace), and zeroes the down launch's arrival counters.
+__device__ __forceinline__ void route_export(const LdsRoute &r, const GroupedArgs &g) {
+  const int KE = g.E + 1, nvalid = r.off[g.E];
+  for (int i = threadIdx.x; i < KE; i += SM_THREADS) {
+    g.fz.cnt[i] = r.cnt[i];
+    g.fz.off[i] = r.off[i];
+  }
+  for (int p = threadIdx.x; p < g.M; p += SM_THREADS) {
+    g.fz.perm[p] = p < nvalid ? r.perm[p] : -1;
+    g.fz.inv[p] = r.inv[p];
+  }
+  for (int i = threadIdx.x; i < g.fz.nctr; i += SM_THREADS) g.fz.ctr[i] = 0;
+}
+
+// z2 of the rows row0 .. row0 + rows - 1 (rows <= 32) from the gate_up launch's partial
+// sums, added in part order: zs[t][j] = bf16(s2 * sum_q zp[q][row0 + t][j]) for j < r (the
+// down launch's rank), zero for r <= j < 32.  Every thread takes one output and every G-th
+// part, G = 512 / outputs (at least 1); the G sums of an output are then added in order.
+// red: rows * 32 floats of LDS; zs: [32][32] bf16 of LDS.  Ends with a barrier.
+__device__ __forceinline__ void z2_reduce(const GroupedArgs &g, int row0, int rows, float *red, uint16_t *zs) {
+  const int r = g.r, nout = rows * r, P = g.fz.nparts;
+  const int G = max(1, SM_THREADS / max(1, nout)), stride = SM_THREADS / G;
+  const int64_t pstride = (int64_t)g.M * r;
+  for (int o = threadIdx.x / G; o < nout; o += stride) {
+    const int gi = threadIdx.x % G, t = o / r, j = o - t * r;
+    const float *src = g.fz.zp + (int64_t)(row0 + t) * r + j;
+    float acc = 0.0f;
+    int q = gi;
+    for (; q + 3 * G < P; q += 4 * G) {
+      const float v0 = src[q * pstride], v1 = src[(q + G) * pstride];
+      const float v2 = src[(q + 2 * G) * pstride], v3 = src[(q + 3 * G) * pstride];
+      acc += v0;
+      acc += v1;
+      acc += v2;
+      acc += v3;
+    }
+    for (; q < P; q += G) acc += src[q * pstride];
+    red[o * G + gi] = acc;
+  }
+  lds_barrier();
+  for (int o = threadIdx.x; o < 32 * 32; o += SM_THREADS) {
+    const int t = o >> 5, j = o & 31;
+    float v = 0.0f;
+    if (t < rows && j < r) {
+      const int oo = t * r + j;
+      for (int gi = 0; gi < G; ++gi) v += red[oo * G + gi];
+      v *= g.fz.s2;
+    }
+    zs[o] = f2bf(v);
+  }
+  lds_barrier();
+}
+
+// Down launch of the two-launch forward: once this workgroup's partial sums are stored it
+// counts its arrival on its column range [c0, c1); the last of the range's gridDim.y *
+// gridDim.z workgroups forms y there, as the combine kernel does: y[t][c] =
+// bf16(sum_j w[t,j] * (sum over splits of O[s][inv[t,j]][c])), splits then choices in order.
+// flag: one int of LDS.  Every wave of the workgroup calls it once.
+__device__ __forceinline__ void arrive_combine(const GroupedArgs &g, int c0, int c1, int *flag) {
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int total = (int)(gridDim.y * gridDim.z);
+    *flag = atomicAdd(&g.fz.ctr[blockIdx.x], 1) == total - 1;
+  }
+  __syncthreads();
+  if (!*flag) return;
+  __threadfence();
+  c1 = min(c1, g.N);
+  if (c0 >= c1) return;
+  const int ncol4 = (c1 - c0) / 4, k = g.fz.topk;
+  const float *O = (const float *)g.C;
+  for (int idx = threadIdx.x; idx < g.fz.T * ncol4; idx += SM_THREADS) {
+    const int t = idx / ncol4, c = c0 + 4 * (idx - t * ncol4);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int p = g.fz.inv[(int64_t)t * k + j];
+      if (p < 0) continue;
+      const float w = g.fz.topw[(int64_t)t * k + j];
+      f32x4 o = *(const f32x4 *)(O + (int64_t)p * g.ldc + c);
+      for (int s2 = 1; s2 < g.fz.nsplit; ++s2) o += *(const f32x4 *)(O + s2 * g.fz.split_stride + (int64_t)p * g.ldc + c);
+      a0 += w * o[0];
+      a1 += w * o[1];
+      a2 += w * o[2];
+      a3 += w * o[3];
+    }
+    *(u32x2 *)(g.fz.y + (int64_t)t * g.ldc + c) = u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+  }
+}
+
+template <int FMT, int SPW, int EPI, int DC, bool FUSE>
 __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, int kb_per_split,
                                                                  int64_t split_stride) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
@@ -155,8 +318,20 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   SmallTables &tb = table_of(sm);
   SmallX &xs = sm.rest.xs;
   if constexpr (NF4ISH) init_small_tables(tb, g.q.codebook);
+  constexpr bool FUP = FUSE && EPI == EPI_SWIGLU_FWD, FDN = FUSE && EPI == EPI_F32;
+  // two-launch forward: the gate_up launch routes in LDS (the activation ring's space)
+  const int32_t *offp = g.off, *gath = g.a_gather;
+  if constexpr (FUP) {
+    const LdsRoute rt = route_in_lds(g.fz.ids, g.M, g.E, (int32_t *)&xs);
+    if (blockIdx.x == 0 && blockIdx.y == 0) route_export(rt, g);
+    offp = rt.off;
+    gath = rt.perm;
+  }
   TileM tm;
-  if (!find_tile_wave(g.off, g.E, SM_BMT, blockIdx.y, tm)) return;  // the same for every wave
+  if (!find_tile_wave(offp, g.E, SM_BMT, blockIdx.y, tm)) {  // the same for every wave
+    if constexpr (FDN) arrive_combine(g, blockIdx.x * SM_WAVES * 32, (blockIdx.x + 1) * SM_WAVES * 32, (int *)&xs);
+    return;
+  }
   const int e = tm.e;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -164,6 +339,14 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   const int N = g.q.N, K = g.q.K, KB = K / 64;
   const int kb0 = blockIdx.z * kb_per_split, kb1 = min(KB, kb0 + kb_per_split);
   const int nchunks = max(0, (kb1 - kb0 + SM_CB - 1) / SM_CB);
+  // gate_up launch of the two-launch forward: z1 = s1 A1[e] x accumulates beside the main
+  // product from the same activation fragments.  Wave w takes the two MFMA steps
+  // 2 (w & 1), 2 (w & 1) + 1 of block w >> 1 of every chunk (32 tokens x 32 adapter rows);
+  // its A1 fragments ride the register ring with the weights.
+  const bool zon = FUP && g.r > 0;
+  const __amdgpu_buffer_rsrc_t ra1 =
+      make_rsrc(FUP ? g.fz.a1 + (int64_t)e * g.fz.a1_estride : nullptr, FUP ? (uint32_t)(g.r * K * 2) : 0u);
+  const uint32_t a1v = (zon && n < g.r) ? (uint32_t)(n * K * 2 + 64 * hh) : OOB;
 
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.q.codes, g.q.codes_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.q.scale, g.q.scale_bytes);
@@ -223,13 +406,15 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   uint32_t xoff = OOB;
   if (xrow < tm.rows) {
     const int64_t p = tm.row0 + xrow;
-    const int64_t src = g.a_gather ? (int64_t)(g.a_gather[p] / g.a_gdiv) : p;
+    const int64_t src = gath ? (int64_t)(gath[p] / g.a_gdiv) : p;
     xoff = (uint32_t)((src * g.lda + (int64_t)kb0 * 64 + 16 * xpiece) * 2);
   }
 
   u32x4 cw[R][SPW][SM_CB];
   ChunkScale cs[R][SPW];
   u32x4 xr[R][2];  // activation pieces ride the same ring as the weights
+  u32x4 a1r[FUP ? R : 1][2];
+  f32x16 zacc = {};
   f32x16 acc[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s)
@@ -247,6 +432,12 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     *(u32x4 *)(row + 8 * xpiece_swz(xrow, 2 * xpiece + 1)) = xr[slot][1];
   };
   auto load_w = [&](int slot, int c) {
+    if constexpr (FUP) {  // this wave's A1 fragments of chunk c (block w >> 1, steps 2 (w & 1) + q)
+      const int kb = kb0 + c * SM_CB + (w >> 1);
+      const uint32_t zdead = (c < nchunks && kb < kb1) ? 0u : OOB;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) a1r[slot][q] = bload128(ra1, a1v, ((uint32_t)kb * 128 + 16u * (2 * (w & 1) + q)) | zdead);
+    }
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       // the chunk's codes, 32 rows x 128 bytes (a chunk past the split reads zero; blocks of a
@@ -294,6 +485,19 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     load_w(d, d);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // this lane's operand pieces of the LoRA K-extension in the two-launch forward (token n,
+  // adapter columns 16 q + 8 h .. +7): z1 (gate_up) or z2 (down, first split)
+  u32x4 zf[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+  if constexpr (FUP) lds_barrier();  // the routing in the activation ring's space has been read
+  if constexpr (FDN) {
+    if (g.r > 0 && blockIdx.z == 0) {
+      uint16_t *zs = (uint16_t *)((char *)&xs + 4096);
+      z2_reduce(g, tm.row0, tm.rows, (float *)&xs, zs);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) zf[q] = *(const u32x4 *)(zs + n * 32 + 16 * q + 8 * hh);
+      lds_barrier();
+    }
+  }
   store_x(0, 0);
   store_x(1, 1);
   lds_barrier();
@@ -322,6 +526,14 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
         bf16x8 af[4];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) af[s4] = *(const bf16x8 *)(xb + 8 * xpiece_swz(n, 8 * b + 4 * hh + s4));
+        if constexpr (FUP) {
+          if (zon && b == (w >> 1)) {
+            zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16((w & 1) ? af[2] : af[0],
+                                                           __builtin_bit_cast(bf16x8, a1r[d][0]), zacc, 0, 0, 0);
+            zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16((w & 1) ? af[3] : af[1],
+                                                           __builtin_bit_cast(bf16x8, a1r[d][1]), zacc, 0, 0, 0);
+          }
+        }
         // a block past kb1 reads zero codes, which are nf4 code 0 (-1), against staged
         // activations that are not zero: its scale is set to zero instead
         const bool live = kb0 + c * SM_CB + b < kb1;
@@ -359,13 +571,40 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     }
   }
 
+  // z1 of the two-launch forward: the eight waves' partial products added in wave order
+  if constexpr (FUP) {
+    if (zon) {
+      float *red = (float *)&xs;  // [8 waves][32 tokens][32]; the ring is no longer read
+      uint16_t *zs = (uint16_t *)((char *)&xs + 32768);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[(w * 32 + 8 * (v >> 2) + 4 * hh + (v & 3)) * 32 + n] = zacc[v];
+      lds_barrier();
+      for (int o = threadIdx.x; o < 32 * 32; o += SM_THREADS) {
+        float v = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < SM_WAVES; ++ww) v += red[(ww * 32 + (o >> 5)) * 32 + (o & 31)];
+        zs[o] = f2bf((o & 31) < g.r ? g.fz.s1 * v : 0.0f);
+      }
+      lds_barrier();
+#pragma unroll
+      for (int q = 0; q < 2; ++q) zf[q] = *(const u32x4 *)(zs + n * 32 + 16 * q + 8 * hh);
+    }
+  }
+  // the down LoRA-A fragment of this wave's h columns (z2 partial sums, two-launch forward)
+  u32x4 a2f = {0, 0, 0, 0};
+  if constexpr (FUP) {
+    const int i0 = (blockIdx.x * SM_WAVES + w) * 16;
+    if (n < g.fz.r2 && i0 < g.I) a2f = *(const u32x4 *)(g.fz.a2 + (int64_t)e * g.fz.a2_estride + (int64_t)n * g.I + i0 + 8 * hh);
+  }
+
   // LoRA K-extension (first split only): acc += z . B[e]^T over the adapter rank
   const int tok = n;
   if (g.r > 0 && blockIdx.z == 0) {
     for (int kk = 0; kk < g.r; kk += 16) {
       const int kc = kk + 8 * hh;
       u32x4 za = {0, 0, 0, 0};
-      if (tok < tm.rows && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
+      if constexpr (FUSE) za = kk == 0 ? zf[0] : zf[1];
+      else if (tok < tm.rows && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
 #pragma unroll
       for (int s = 0; s < SPW; ++s) {
         u32x4 zb = {0, 0, 0, 0};
@@ -386,19 +625,48 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
         bg = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, false, g.act == 1, g.I)]);
         bu = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, true, g.act == 1, g.I)]);
       }
+      uint16_t *hT = (uint16_t *)stage;  // two-launch forward: h of the tile, [32 tokens][16]
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float mine = acc[s][v];
         const float other = __shfl_xor(mine, 16);
         const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
+        uint16_t hb = 0;
         if (n < 16 && i < g.I && t < tm.rows) {
           const int64_t p = tm.row0 + t;
           const float gt = mine + bg, up = other + bu;
           const float h = g.act == 1 ? glu_clamped(gt, up, g.glu_alpha, g.glu_limit) : gt * sigmoid_fast(gt) * up;
-          ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(h);
+          hb = f2bf(h);
+          ((uint16_t *)g.C)[p * g.ldc + i] = hb;
           if (g.Gout) {
             g.Gout[p * g.ldg + gate_up_row(i, false, g.act == 1, g.I)] = f2bf(gt);
             g.Gout[p * g.ldg + gate_up_row(i, true, g.act == 1, g.I)] = f2bf(up);
+          }
+        }
+        if constexpr (FUP) {
+          if (n < 16) hT[t * 16 + n] = hb;
+        }
+      }
+      if constexpr (FUP) {
+        // z2 partial sums over this workgroup's h columns: the tile's h (tokens x 16) times
+        // this wave's A2 fragment, then the eight waves added in wave order
+        if (g.fz.r2 > 0) {
+          asm volatile("" ::: "memory");
+          const bf16x8 hf = *(const bf16x8 *)(hT + n * 16 + 8 * hh);
+          const f32x16 zp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, __builtin_bit_cast(bf16x8, a2f), f32x16{}, 0, 0, 0);
+          float *red = (float *)&xs;  // [8 waves][32 tokens][32]
+#pragma unroll
+          for (int v = 0; v < 16; ++v) red[(w * 32 + 8 * (v >> 2) + 4 * hh + (v & 3)) * 32 + n] = zp[v];
+          lds_barrier();
+          const int r2 = g.fz.r2;
+          for (int o = threadIdx.x; o < 32 * 32; o += SM_THREADS) {
+            const int t = o >> 5, j = o & 31;
+            if (t < tm.rows && j < r2) {
+              float v = 0.0f;
+#pragma unroll
+              for (int ww = 0; ww < SM_WAVES; ++ww) v += red[(ww * 32 + t) * 32 + j];
+              g.fz.zp[((int64_t)blockIdx.x * g.M + tm.row0 + t) * r2 + j] = v;
+            }
           }
         }
       }
@@ -414,6 +682,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
       }
     }
   }
+  if constexpr (FDN) arrive_combine(g, blockIdx.x * SM_WAVES * 32, (blockIdx.x + 1) * SM_WAVES * 32, (int *)&xs);
 }
 
 // Variant for few tokens per expert: workgroup slots of at most XMAX tokens, whose
@@ -428,7 +697,7 @@ constexpr int XMAX = 8;
 static_assert(XMAX == 8, "token rows of a direct slot");
 constexpr int XPT = 8;  // staged 16-byte activation pieces per thread: rows x blocks <= 512
 
-template <int FMT, int EPI, int CH, bool SEQ>
+template <int FMT, int EPI, int CH, bool SEQ, bool FUSE>
 __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g, int kb_per_split,
                                                                    int64_t split_stride, int nseq) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
@@ -442,8 +711,20 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
   extern __shared__ __attribute__((aligned(16))) uint32_t small_lds[];
   SmallTables &tb = direct_tb;  // read by the NF4 formats only
   uint16_t *xs = (uint16_t *)small_lds;
+  constexpr bool FUP = FUSE && EPI == EPI_SWIGLU_FWD, FDN = FUSE && EPI == EPI_F32;
+  // two-launch forward: the gate_up launch routes in LDS (the staged activations' space)
+  const int32_t *offp = g.off, *gath = g.a_gather;
+  if constexpr (FUP) {
+    const LdsRoute rt = route_in_lds(g.fz.ids, g.M, g.E, (int32_t *)small_lds);
+    if (blockIdx.x == 0 && blockIdx.y == 0) route_export(rt, g);
+    offp = rt.off;
+    gath = rt.perm;
+  }
   TileM tm;
-  if (!find_tile_wave(g.off, g.E, XMAX, blockIdx.y, tm)) return;  // the same for every wave
+  if (!find_tile_wave(offp, g.E, XMAX, blockIdx.y, tm)) {  // the same for every wave
+    if constexpr (FDN) arrive_combine(g, blockIdx.x * nseq * SM_WAVES * 32, (blockIdx.x + 1) * nseq * SM_WAVES * 32, (int *)small_lds);
+    return;
+  }
   const int e = tm.e;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, hh = lane >> 5;
@@ -519,7 +800,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       if (i < npieces) {
         const int xr = i / (nblk * 8), piece = i - xr * (nblk * 8);
         const int64_t p = tm.row0 + xr;
-        const int64_t src = g.a_gather ? (int64_t)(g.a_gather[p] / g.a_gdiv) : p;
+        const int64_t src = gath ? (int64_t)(gath[p] / g.a_gdiv) : p;
         xp[u] = *(const u32x4 *)(g.A + src * g.lda + (int64_t)kb0 * 64 + piece * 8);
       }
     }
@@ -543,10 +824,23 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       zb0 = u32x4{0, 0, 0, 0};
       if (lora && row >= 0 && 8 * hh < g.r) zb0 = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row * g.ldxb + 8 * hh);
     };
-    if (lora && xlane && 8 * hh < g.r) za0 = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + 8 * hh);
+    if (!FUSE && lora && xlane && 8 * hh < g.r) za0 = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + 8 * hh);
     load_zb0();
-    // this wave's code stage: [32 strip rows][2 CH pieces of 16 bytes], pieces swizzled
-    char *stage = (char *)small_lds + ((xrows * xrow_len * 2 + 15) & ~15) + w * (32 * CH * 32);
+    // two-launch forward, gate_up: this wave's down LoRA-A fragment of its strip's h columns
+    u32x4 a2f = {0, 0, 0, 0};
+    float zsum[4] = {0.f, 0.f, 0.f, 0.f};  // z2 partial sums, tokens 4 h + v (v < 4)
+    auto load_a2f = [&](int st) {
+      if constexpr (FUP) {
+        a2f = u32x4{0, 0, 0, 0};
+        if (n < g.fz.r2 && st * 16 < g.I)
+          a2f = *(const u32x4 *)(g.fz.a2 + (int64_t)e * g.fz.a2_estride + (int64_t)n * g.I + st * 16 + 8 * hh);
+      }
+    };
+    load_a2f(strip_of(0));
+    u32x4 zf1 = {0, 0, 0, 0};  // the second 16 adapter columns (two-launch forward)
+    // the code stages: [waves][32 strip rows][2 CH pieces of 16 bytes], pieces swizzled
+    char *stage0 = (char *)small_lds + ((xrows * xrow_len * 2 + 15) & ~15);
+    char *stage = stage0 + w * (32 * CH * 32);
 
     u32x4 craw[CS][NI];
     // scale windows, and the four block scales of the window in use, taken out of it as
@@ -653,6 +947,15 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     }
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NF4ISH) init_small_tables(tb, g.q.codebook);
+    if constexpr (FUP) lds_barrier();  // the routing in the staged activations' space has been read
+    if constexpr (FDN) {
+      if (lora) {  // z2 of the slot's rows from the gate_up launch's partial sums
+        uint16_t *zs = (uint16_t *)(stage0 + 4096);
+        z2_reduce(g, tm.row0, xrows, (float *)stage0, zs);
+        za0 = *(const u32x4 *)(zs + xrow * 32 + 8 * hh);
+        zf1 = *(const u32x4 *)(zs + xrow * 32 + 16 + 8 * hh);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
       const int i = threadIdx.x + u * SM_THREADS;
@@ -662,6 +965,49 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       }
     }
     lds_barrier();
+    if constexpr (FUP) {
+      // z1 = s1 A1[e] x of the slot's rows from the staged activations: wave w takes the
+      // 16-wide k steps w, w + 8, ... (32 tokens x 32 adapter rows per MFMA), 16 A1
+      // fragments in flight per round; then the waves' products are added in wave order
+      if (lora) {
+        const __amdgpu_buffer_rsrc_t ra1 = make_rsrc(g.fz.a1 + (int64_t)e * g.fz.a1_estride, (uint32_t)(g.r * K * 2));
+        const uint32_t a1v = n < g.r ? (uint32_t)(n * K * 2 + 16 * hh) : OOB;
+        const int KS = K / 16;
+        f32x16 zacc = {};
+        for (int s0 = w; s0 < KS; s0 += SM_WAVES * 16) {
+          u32x4 bfr[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int st = s0 + SM_WAVES * i;
+            bfr[i] = bload128(ra1, a1v, st < KS ? (uint32_t)st * 32 : OOB);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int st = s0 + SM_WAVES * i;
+            if (st < KS) {
+              const int c = 2 * (st & 3) + hh;  // 8-element piece of block st / 4
+              const bf16x8 af = *(const bf16x8 *)(xsrc + (st >> 2) * 64 + ((c ^ (xrow & 7)) * 8));
+              zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bfr[i]), zacc, 0, 0, 0);
+            }
+          }
+        }
+        float *red = (float *)stage0;  // [8 waves][8 tokens][32]
+        uint16_t *zs = (uint16_t *)(stage0 + SM_WAVES * XMAX * 32 * 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(w * XMAX + 4 * hh + v) * 32 + n] = zacc[v];
+        lds_barrier();
+        if (threadIdx.x < XMAX * 32) {
+          float v = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < SM_WAVES; ++ww) v += red[(ww * XMAX + (threadIdx.x >> 5)) * 32 + (threadIdx.x & 31)];
+          zs[threadIdx.x] = f2bf((threadIdx.x & 31) < g.r ? g.fz.s1 * v : 0.0f);
+        }
+        lds_barrier();
+        za0 = *(const u32x4 *)(zs + xrow * 32 + 8 * hh);
+        zf1 = *(const u32x4 *)(zs + xrow * 32 + 16 + 8 * hh);
+        lds_barrier();  // the main loop writes the code stages
+      }
+    }
 
     for (int k = 0;;) {
     Ops ops[2];
@@ -696,7 +1042,8 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         u32x4 za = za0, zb = zb_done;
         if (kk > 0) {
           za = zb = u32x4{0, 0, 0, 0};
-          if (xlane && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
+          if constexpr (FUSE) za = zf1;
+          else if (xlane && kc < g.r) za = *(const u32x4 *)(g.xa + (tm.row0 + tok) * g.ldxa + kc);
           if (row_done >= 0 && kc < g.r) zb = *(const u32x4 *)(g.xb + e * g.xb_estride + (int64_t)row_done * g.ldxb + kc);
         }
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, za), __builtin_bit_cast(bf16x8, zb),
@@ -711,20 +1058,36 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
         bg = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, false, g.act == 1, g.I)]);
         bu = bf2f(g.bias[e * g.bias_estride + gate_up_row(i, true, g.act == 1, g.I)]);
       }
+      uint16_t *hT = (uint16_t *)stage;  // two-launch forward: h of the strip, [32 tokens][16]
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float mine = acc[v];
         const float other = __shfl_xor(mine, 16);
         const int t = 8 * (v >> 2) + 4 * hh + (v & 3);
+        uint16_t hb = 0;
         if (n < 16 && i < g.I && t >= t0 && t < t0 + xrows) {
           const int64_t p = tm.row0 + t;
           const float gt = mine + bg, up = other + bu;
           const float h = g.act == 1 ? glu_clamped(gt, up, g.glu_alpha, g.glu_limit) : gt * sigmoid_fast(gt) * up;
-          ((uint16_t *)g.C)[p * g.ldc + i] = f2bf(h);
+          hb = f2bf(h);
+          ((uint16_t *)g.C)[p * g.ldc + i] = hb;
           if (g.Gout) {
             g.Gout[p * g.ldg + gate_up_row(i, false, g.act == 1, g.I)] = f2bf(gt);
             g.Gout[p * g.ldg + gate_up_row(i, true, g.act == 1, g.I)] = f2bf(up);
           }
+        }
+        if constexpr (FUP) {
+          if (n < 16) hT[t * 16 + n] = hb;
+        }
+      }
+      if constexpr (FUP) {
+        // z2 partial sums over the strip's 16 h columns (tokens < XMAX: accumulator v < 4)
+        if (g.fz.r2 > 0 && row_done >= 0) {
+          asm volatile("" ::: "memory");
+          const bf16x8 hf = *(const bf16x8 *)(hT + n * 16 + 8 * hh);
+          const f32x16 zp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hf, __builtin_bit_cast(bf16x8, a2f), f32x16{}, 0, 0, 0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) zsum[v] += zp[v];
         }
       }
     } else if (row_done >= 0) {
@@ -742,6 +1105,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     if (!SEQ || k >= nseq || !strip_valid(strip_of(k))) break;
     setup_strip(strip_of(k));
     load_zb0();
+    load_a2f(strip_of(k));
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       __builtin_amdgcn_sched_barrier(0);
@@ -749,7 +1113,25 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     }
     __builtin_amdgcn_sched_barrier(0);
     }  // strips
+    if constexpr (FUP) {
+      // the workgroup's z2 partial sums: the waves' sums added in wave order
+      if (g.fz.r2 > 0) {
+        float *red = (float *)stage0;  // [8 waves][8 tokens][32]
+        lds_barrier();  // every wave is past its last strip's tile
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(w * XMAX + 4 * hh + v) * 32 + n] = zsum[v];
+        lds_barrier();
+        const int t = threadIdx.x >> 5, j = threadIdx.x & 31, r2 = g.fz.r2;
+        if (t < xrows && j < r2) {
+          float v = 0.0f;
+#pragma unroll
+          for (int ww = 0; ww < SM_WAVES; ++ww) v += red[(ww * XMAX + t) * 32 + j];
+          g.fz.zp[((int64_t)blockIdx.x * g.M + tm.row0 + t) * r2 + j] = v;
+        }
+      }
+    }
   }
+  if constexpr (FDN) arrive_combine(g, blockIdx.x * nseq * SM_WAVES * 32, (blockIdx.x + 1) * nseq * SM_WAVES * 32, (int *)small_lds);
 }
 
 // Compute units of the current device (cached per device).
@@ -779,55 +1161,81 @@ static bool use_direct(const GroupedArgs &a, int kbs) {
   return a.M <= 2 * min(a.E, a.M) && direct_rows(a) * kbs * 8 <= XPT * SM_THREADS;
 }
 
-template <int FMT, int EPI>
-static void launch_small_fmt(const GroupedArgs &a, int spw, int strips_per_expert, int slots, int splits,
-                             int kbs, int64_t split_stride, hipStream_t s) {
-  (void)spw;
-  (void)slots;
-  if (use_direct(a, kbs)) {
+// Launch shape of one decode-shaped GEMM: the direct variant (staged activation rows, nseq
+// strips per wave) or the 32-token slots.
+struct SmallPlan {
+  bool direct, four;
+  int nseq;
+  dim3 grid;
+  size_t lds;
+};
+template <int FMT>
+static SmallPlan small_plan(const GroupedArgs &a, int strips_per_expert, int splits, int kbs) {
+  SmallPlan p{};
+  p.direct = use_direct(a, kbs);
+  if (p.direct) {
     // strips per wave: the fewest with which the workgroups of the touched experts (at most
     // min(E, M)) fit on the compute units at once
     const int cus = device_cus();
-    int nseq = 1;
-    while (nseq < 16 && (int64_t)cdiv(strips_per_expert, SM_WAVES * nseq) * min(a.E, a.M) * splits > cus) ++nseq;
-    const dim3 grid(cdiv(strips_per_expert, SM_WAVES * nseq), small_slots(a.M, a.E, XMAX), splits);
+    p.nseq = 1;
+    while (p.nseq < 16 && (int64_t)cdiv(strips_per_expert, SM_WAVES * p.nseq) * min(a.E, a.M) * splits > cus) ++p.nseq;
+    p.grid = dim3(cdiv(strips_per_expert, SM_WAVES * p.nseq), small_slots(a.M, a.E, XMAX), splits);
     const size_t xlds = ((size_t)direct_rows(a) * kbs * 64 * 2 + 15) & ~(size_t)15;
     // four-block stages when they fit beside the table and the staged activations
     constexpr size_t STATIC_LDS = FMT != FMT_MXFP4 ? sizeof(SmallTables) : 0;
-    const bool four = STATIC_LDS + xlds + stage_bytes(4) <= 160 * 1024;
-    const size_t lds = xlds + stage_bytes(four ? 4 : 2);
-    if (nseq > 1) {
-      if (four) small_direct_kernel<FMT, EPI, 4, true><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, nseq);
-      else small_direct_kernel<FMT, EPI, 2, true><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, nseq);
+    p.four = STATIC_LDS + xlds + stage_bytes(4) <= 160 * 1024;
+    p.lds = xlds + stage_bytes(p.four ? 4 : 2);
+  } else {
+    p.nseq = 1;
+    p.grid = dim3(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, SM_BMT), splits);
+    p.lds = 0;
+  }
+  return p;
+}
+
+template <int FMT, int EPI, bool FUSE>
+static void launch_small_plan(const GroupedArgs &a, const SmallPlan &p, int kbs, int64_t split_stride, hipStream_t s) {
+  if (p.direct) {
+    if (p.nseq > 1) {
+      if (p.four) small_direct_kernel<FMT, EPI, 4, true, FUSE><<<p.grid, SM_THREADS, p.lds, s>>>(a, kbs, split_stride, p.nseq);
+      else small_direct_kernel<FMT, EPI, 2, true, FUSE><<<p.grid, SM_THREADS, p.lds, s>>>(a, kbs, split_stride, p.nseq);
     } else {
-      if (four) small_direct_kernel<FMT, EPI, 4, false><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, 1);
-      else small_direct_kernel<FMT, EPI, 2, false><<<grid, SM_THREADS, lds, s>>>(a, kbs, split_stride, 1);
+      if (p.four) small_direct_kernel<FMT, EPI, 4, false, FUSE><<<p.grid, SM_THREADS, p.lds, s>>>(a, kbs, split_stride, 1);
+      else small_direct_kernel<FMT, EPI, 2, false, FUSE><<<p.grid, SM_THREADS, p.lds, s>>>(a, kbs, split_stride, 1);
     }
   } else {
-    const dim3 grid(cdiv(strips_per_expert, SM_WAVES), small_slots(a.M, a.E, SM_BMT), splits);
-    small_gemm_kernel<FMT, 1, EPI, 3><<<grid, SM_THREADS, 0, s>>>(a, kbs, split_stride);
+    small_gemm_kernel<FMT, 1, EPI, 3, FUSE><<<p.grid, SM_THREADS, 0, s>>>(a, kbs, split_stride);
   }
 }
 
 template <int EPI>
-static void launch_small(const GroupedArgs &a, int spw, int strips_per_expert, int slots, int splits, int kbs,
-                         int64_t split_stride, hipStream_t s) {
+static SmallPlan launch_small(const GroupedArgs &a, int strips_per_expert, int splits, int kbs, int64_t split_stride,
+                              hipStream_t s, bool launch = true) {
+  auto go = [&](auto fmt_tag) {
+    constexpr int FMT = decltype(fmt_tag)::value;
+    const SmallPlan p = small_plan<FMT>(a, strips_per_expert, splits, kbs);
+    if (launch) {
+      if (a.fz.on) launch_small_plan<FMT, EPI, true>(a, p, kbs, split_stride, s);
+      else launch_small_plan<FMT, EPI, false>(a, p, kbs, split_stride, s);
+    }
+    return p;
+  };
   switch (a.q.fmt) {
-    case FMT_NF4: launch_small_fmt<FMT_NF4, EPI>(a, spw, strips_per_expert, slots, splits, kbs, split_stride, s); break;
-    case FMT_NF4_DQ: launch_small_fmt<FMT_NF4_DQ, EPI>(a, spw, strips_per_expert, slots, splits, kbs, split_stride, s); break;
-    default: launch_small_fmt<FMT_MXFP4, EPI>(a, spw, strips_per_expert, slots, splits, kbs, split_stride, s); break;
+    case FMT_NF4: return go(std::integral_constant<int, FMT_NF4>{});
+    case FMT_NF4_DQ: return go(std::integral_constant<int, FMT_NF4_DQ>{});
+    default: return go(std::integral_constant<int, FMT_MXFP4>{});
   }
 }
-
 
 bool launch_small_gate_up(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_GATE_UP, s);
-  const int strips_per_expert = cdiv(a.I, 16);
-  const int64_t strips = (int64_t)strips_per_expert * min(a.E, a.M);
-  const int KB = a.K / 64;
-  launch_small<EPI_SWIGLU_FWD>(a, pick_spw(strips), strips_per_expert, 0, 1, KB, 0, s);
+  launch_small<EPI_SWIGLU_FWD>(a, cdiv(a.I, 16), 1, a.K / 64, 0, s);
   return last_launch_ok();
+}
+
+int small_gate_up_parts(const GroupedArgs &a) {
+  return (int)launch_small<EPI_SWIGLU_FWD>(a, cdiv(a.I, 16), 1, a.K / 64, 0, nullptr, false).grid.x;
 }
 
 // K splits of down: enough waves for the device, each split a whole number of chunks.  With
@@ -846,15 +1254,20 @@ int small_down_splits(int M, int E, int N, int K) {
   return splits;
 }
 
+static int small_down_kbs(const GroupedArgs &a, int splits) {
+  return cdiv(cdiv(a.K / 64, splits), SM_CB) * SM_CB;
+}
+
 bool launch_small_down(const GroupedArgs &a, int splits, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_DOWN, s);
-  const int strips_per_expert = cdiv(a.N, 32);
-  const int64_t strips = (int64_t)strips_per_expert * min(a.E, a.M);
-  const int KB = a.K / 64;
-  const int kbs = cdiv(cdiv(KB, splits), SM_CB) * SM_CB;
-  launch_small<EPI_F32>(a, pick_spw(strips), strips_per_expert, 0, splits, kbs, (int64_t)a.M * a.ldc, s);
+  launch_small<EPI_F32>(a, cdiv(a.N, 32), splits, small_down_kbs(a, splits), (int64_t)a.M * a.ldc, s);
   return last_launch_ok();
+}
+
+int small_down_ranges(const GroupedArgs &a, int splits) {
+  return (int)launch_small<EPI_F32>(a, cdiv(a.N, 32), splits, small_down_kbs(a, splits), (int64_t)a.M * a.ldc,
+                                    nullptr, false).grid.x;
 }
 
 // z[p][j] = alpha * <B[e_p][j], A[src(p)]> for the routed rows p of the valid experts: one

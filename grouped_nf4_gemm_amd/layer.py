@@ -12,7 +12,7 @@ import dataclasses
 import torch
 
 from . import _lib
-from ._lib import FMT, E4B_EXPAND, E4B_TRAIN, check
+from ._lib import FMT, E4B_EXPAND, E4B_SEPARATE, E4B_TRAIN, check
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -168,10 +168,13 @@ class MoELayer:
     """One routed-expert layer: frozen stacks w_gu [E, 2I, H], w_dn [E, H, I] plus
     optional adapters on each.  Owns its workspace (caller-side allocation).
     expand=True asks the forward of a large batch to stream bf16 copies of the stacks
-    (written into the workspace) instead of decoding them inside the GEMM tiles."""
+    (written into the workspace) instead of decoding them inside the GEMM tiles.
+    separate=True runs a decode-shaped inference forward (at most 256 routed rows) as six
+    launches instead of the default two."""
 
     def __init__(self, w_gu: QStack, w_dn: QStack, l_gu: LoRA | None, l_dn: LoRA | None,
-                 T: int, topk: int, train: bool = True, expand: bool | None = None, act: dict | None = None):
+                 T: int, topk: int, train: bool = True, expand: bool | None = None, act: dict | None = None,
+                 separate: bool = False):
         """act: None for the stock act(gate) * up, or {"kind": "clamped_glu", "alpha": a,
         "limit": L, "b_gu": bf16 [E, 2I] or None, "b_dn": bf16 [E, H] or None} for the clamped
         GLU over interleaved gate/up rows (gpt-oss experts)."""
@@ -195,7 +198,7 @@ class MoELayer:
                 _arg(l.A, f"{name}.A", torch.bfloat16, (E, l.r, K), dev)
                 _arg(l.B, f"{name}.B", torch.bfloat16, (E, N, l.r), dev)
         self.T, self.topk = T, topk
-        self.flags = (E4B_TRAIN if train else 0) | (E4B_EXPAND if expand else 0)
+        self.flags = (E4B_TRAIN if train else 0) | (E4B_EXPAND if expand else 0) | (E4B_SEPARATE if separate else 0)
         self._act = None
         if act is not None:
             b_gu, b_dn = act.get("b_gu"), act.get("b_dn")

@@ -111,6 +111,14 @@ typedef struct {
  * (2 bytes per weight; workspace_size grows accordingly) and stream those instead; the
  * results are bit-identical, and the dgrad still decodes the packed stacks. */
 #define E4B_EXPAND 2u
+/* An inference forward of at most 256 routed rows (decode) runs as two launches (project
+ * record, "entry_points": the captured decode step): the gate_up launch routes the ids in
+ * each workgroup, forms z1 = s1 A1 x for its own rows and the partial sums of z2 over its h
+ * columns; the down launch adds those partial sums and its last workgroup over each column
+ * range forms y there.  This applies with E <= 256 and adapter ranks <= 32 and for the 4-bit
+ * formats; E4B_SEPARATE runs the same forward as six launches instead (route, LoRA-A,
+ * gate_up, LoRA-A, down, combine).  Both agree to rounding (z1 is summed in another order). */
+#define E4B_SEPARATE 4u
 
 /* Expert activation between the two projections.
  *  E4B_ACT_SWIGLU: the stock epilogue act(gate) * up with SiLU (method page, "Limitations":

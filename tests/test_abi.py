@@ -76,8 +76,17 @@ def test_expanded_stacks_workspace(L):
     _, small_default = _ws(L, _desc(L, E=E, H=H, I=I, T=128, k=2, flags=TRAIN))     # 256 rows
     _, small_forced = _ws(L, _desc(L, E=E, H=H, I=I, T=128, k=2, flags=TRAIN | EXPAND))
     assert small_forced == small_default
-    st, _ = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN | 4))  # unknown flag bit
+    st, _ = _ws(L, _desc(L, E=E, H=H, I=I, T=2048, k=2, flags=TRAIN | 8))  # unknown flag bit
     assert st == L.E4B_ERR_INVALID_ARG
+
+
+def test_separate_flag_accepted(L):
+    """E4B_SEPARATE (the decode-shaped forward as six launches) is a known flag; it does not
+    change the workspace size."""
+    SEPARATE = 4
+    _, n0 = _ws(L, _desc(L, T=16, k=2, flags=0))
+    st, n1 = _ws(L, _desc(L, T=16, k=2, flags=SEPARATE))
+    assert st == 0 and n1 == n0
 
 
 @pytest.mark.parametrize("kw", [dict(H=100), dict(I=96), dict(E=0), dict(k=9), dict(k=0),
