@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--command", default="", help="command line recorded in a summary")
     p.add_argument("--expand", action="store_true",
                    help="large calls: the forward streams bf16 copies of the stacks instead of decoding them in the tile")
+    p.add_argument("--separate", action="store_true",
+                   help="decode-shaped forward as six launches instead of two")
     p.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
                    help="time forward-only steps as replays of one captured HIP graph "
                         "(auto: on for the decode-shaped workloads)")
@@ -299,12 +301,12 @@ def measure(s, a, inp, steps: int, warmup: int, kernel_steps: int) -> dict:
     # (> 2 GB in all), so the 256 MB last-level cache cannot serve the weights of a step
     # from the previous ones; every copy holds the same bytes.
     ncopy = 1 if with_bwd else max(1, -(-2_500_000_000 // (w_gu.codes.numel() + w_dn.codes.numel())))
-    layers = [MoELayer(w_gu, w_dn, l_gu, l_dn, s.T, s.k, train=with_bwd, expand=a.expand)]
+    layers = [MoELayer(w_gu, w_dn, l_gu, l_dn, s.T, s.k, train=with_bwd, expand=a.expand, separate=a.separate)]
     for _ in range(ncopy - 1):
         cq = lambda q: QStack(q.fmt, q.E, q.N, q.K, q.codes.clone(), q.scale.clone(),
                               None if q.scale2 is None else q.scale2.clone())
         cl = lambda l: LoRA(l.A.clone(), l.B.clone(), l.scaling)
-        layers.append(MoELayer(cq(w_gu), cq(w_dn), cl(l_gu), cl(l_dn), s.T, s.k, train=False))
+        layers.append(MoELayer(cq(w_gu), cq(w_dn), cl(l_gu), cl(l_dn), s.T, s.k, train=False, separate=a.separate))
     y = torch.empty(s.T, s.H, dtype=torch.bfloat16, device=dev)
     dx = torch.empty_like(y)
     d_topw = torch.empty(s.T, s.k, dtype=torch.float32, device=dev)

@@ -228,28 +228,36 @@ __device__ __forceinline__ void route_export(const LdsRoute &r, const GroupedArg
 
 // z2 of the rows row0 .. row0 + rows - 1 (rows <= 32) from the gate_up launch's partial
 // sums, added in part order: zs[t][j] = bf16(s2 * sum_q zp[q][row0 + t][j]) for j < r (the
-// down launch's rank), zero for r <= j < 32.  Every thread takes one output and every G-th
-// part, G = 512 / outputs (at least 1); the G sums of an output are then added in order.
-// red: rows * 32 floats of LDS; zs: [32][32] bf16 of LDS.  Ends with a barrier.
+// down launch's rank), zero for r <= j < 32.  Every thread takes one group of 4 adjacent
+// outputs (one output when r is not a multiple of 4) and every G-th part, G = 512 / groups
+// (at least 1), loading 8 parts at a time; the G sums of a group are then added in order.
+// red: 2048 floats of LDS; zs: [32][32] bf16 of LDS.  Ends with a barrier.
 __device__ __forceinline__ void z2_reduce(const GroupedArgs &g, int row0, int rows, float *red, uint16_t *zs) {
-  const int r = g.r, nout = rows * r, P = g.fz.nparts;
-  const int G = max(1, SM_THREADS / max(1, nout)), stride = SM_THREADS / G;
+  const int r = g.r, P = g.fz.nparts;
+  const int W = (r & 3) == 0 ? 4 : 1;  // outputs per group
+  const int ng = rows * r / W;
+  const int G = max(1, SM_THREADS / max(1, ng)), stride = SM_THREADS / G;
   const int64_t pstride = (int64_t)g.M * r;
-  for (int o = threadIdx.x / G; o < nout; o += stride) {
-    const int gi = threadIdx.x % G, t = o / r, j = o - t * r;
-    const float *src = g.fz.zp + (int64_t)(row0 + t) * r + j;
-    float acc = 0.0f;
-    int q = gi;
-    for (; q + 3 * G < P; q += 4 * G) {
-      const float v0 = src[q * pstride], v1 = src[(q + G) * pstride];
-      const float v2 = src[(q + 2 * G) * pstride], v3 = src[(q + 3 * G) * pstride];
-      acc += v0;
-      acc += v1;
-      acc += v2;
-      acc += v3;
+  for (int o = threadIdx.x / G; o < ng; o += stride) {
+    const int gi = threadIdx.x % G;
+    const float *src = g.fz.zp + (int64_t)row0 * r + (int64_t)o * W;  // rows are r apart: group o at o * W
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = gi; q0 < P; q0 += 8 * G) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u * G;
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (q < P) {
+          if (W == 4) v[u] = *(const f32x4 *)(src + q * pstride);
+          else v[u][0] = src[q * pstride];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (q0 + u * G < P) acc += v[u];
     }
-    for (; q < P; q += G) acc += src[q * pstride];
-    red[o * G + gi] = acc;
+    for (int i = 0; i < W; ++i) red[(o * W + i) * G + gi] = acc[i];
   }
   lds_barrier();
   for (int o = threadIdx.x; o < 32 * 32; o += SM_THREADS) {
@@ -270,39 +278,72 @@ __device__ __forceinline__ void z2_reduce(const GroupedArgs &g, int row0, int ro
 // gridDim.z workgroups forms y there, as the combine kernel does: y[t][c] =
 // bf16(sum_j w[t,j] * (sum over splits of O[s][inv[t,j]][c])), splits then choices in order.
 // flag: one int of LDS.  Every wave of the workgroup calls it once.
+// The workgroup barrier orders every thread's stores before thread 0's device-scope release
+// fence, and thread 0's acquire fence before every thread's loads: one fence per workgroup
+// (each one writes back or invalidates caches of the whole cache level).
 __device__ __forceinline__ void arrive_combine(const GroupedArgs &g, int c0, int c1, int *flag) {
-  __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
     const int total = (int)(gridDim.y * gridDim.z);
-    *flag = atomicAdd(&g.fz.ctr[blockIdx.x], 1) == total - 1;
+    __threadfence();
+    const bool last = atomicAdd(&g.fz.ctr[blockIdx.x], 1) == total - 1;
+    if (last) __threadfence();
+    *flag = last;
   }
   __syncthreads();
   if (!*flag) return;
-  __threadfence();
   c1 = min(c1, g.N);
   if (c0 >= c1) return;
-  const int ncol4 = (c1 - c0) / 4, k = g.fz.topk;
+  const int ncol4 = (c1 - c0) / 4, k = g.fz.topk, ns = g.fz.nsplit, nq = g.fz.T * ncol4;
   const float *O = (const float *)g.C;
-  for (int idx = threadIdx.x; idx < g.fz.T * ncol4; idx += SM_THREADS) {
-    const int t = idx / ncol4, c = c0 + 4 * (idx - t * ncol4);
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int p = g.fz.inv[(int64_t)t * k + j];
-      if (p < 0) continue;
-      const float w = g.fz.topw[(int64_t)t * k + j];
-      f32x4 o = *(const f32x4 *)(O + (int64_t)p * g.ldc + c);
-      for (int s2 = 1; s2 < g.fz.nsplit; ++s2) o += *(const f32x4 *)(O + s2 * g.fz.split_stride + (int64_t)p * g.ldc + c);
-      a0 += w * o[0];
-      a1 += w * o[1];
-      a2 += w * o[2];
-      a3 += w * o[3];
+  // four column quads per thread and step; for each choice the partial sums of every split
+  // of the four quads are loaded together (their latencies overlap)
+  for (int q0 = threadIdx.x; q0 < nq; q0 += 4 * SM_THREADS) {
+    f32x4 a[4];
+    int tq[4], cq[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = min(q0 + u * SM_THREADS, nq - 1);
+      tq[u] = q / ncol4;
+      cq[u] = c0 + 4 * (q - tq[u] * ncol4);
+      a[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    *(u32x2 *)(g.fz.y + (int64_t)t * g.ldc + c) = u32x2{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+    for (int j = 0; j < k; ++j) {
+      int pj[4];
+      float wj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pj[u] = g.fz.inv[(int64_t)tq[u] * k + j];
+        wj[u] = g.fz.topw[(int64_t)tq[u] * k + j];
+      }
+      f32x4 ov[4][SMALL_MAX_SPLITS];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int sp = 0; sp < SMALL_MAX_SPLITS; ++sp)
+          if (sp < ns && pj[u] >= 0) ov[u][sp] = *(const f32x4 *)(O + sp * g.fz.split_stride + (int64_t)pj[u] * g.ldc + cq[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (pj[u] < 0) continue;
+        f32x4 o = ov[u][0];
+#pragma unroll
+        for (int sp = 1; sp < SMALL_MAX_SPLITS; ++sp)
+          if (sp < ns) o += ov[u][sp];
+        a[u][0] += wj[u] * o[0];
+        a[u][1] += wj[u] * o[1];
+        a[u][2] += wj[u] * o[2];
+        a[u][3] += wj[u] * o[3];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q0 + u * SM_THREADS < nq)
+        *(u32x2 *)(g.fz.y + (int64_t)tq[u] * g.ldc + cq[u]) = u32x2{pack_bf16x2(a[u][0], a[u][1]), pack_bf16x2(a[u][2], a[u][3])};
   }
 }
 
-template <int FMT, int SPW, int EPI, int DC, bool FUSE>
+// FUSE (two-launch forward): 0 off; 1 or 2: on, with ranks up to 16 FUSE.
+template <int FMT, int SPW, int EPI, int DC, int FUSE>
 __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, int kb_per_split,
                                                                  int64_t split_stride) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
@@ -340,13 +381,18 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   const int kb0 = blockIdx.z * kb_per_split, kb1 = min(KB, kb0 + kb_per_split);
   const int nchunks = max(0, (kb1 - kb0 + SM_CB - 1) / SM_CB);
   // gate_up launch of the two-launch forward: z1 = s1 A1[e] x accumulates beside the main
-  // product from the same activation fragments.  Wave w takes the two MFMA steps
-  // 2 (w & 1), 2 (w & 1) + 1 of block w >> 1 of every chunk (32 tokens x 32 adapter rows);
-  // its A1 fragments ride the register ring with the weights.
+  // product from the staged activations.  Wave w takes the 32-wide k step w of every chunk
+  // (block w / 2) with 16 x 16 x 32 MFMAs: tokens 16 hf + lane % 16, adapter rows 16 jt +
+  // lane % 16, k = 8 (lane / 16) .. +7 of the step; its A1 fragments ride the register ring
+  // with the weights.
+  constexpr int ZT = FUSE == 2 ? 2 : 1;  // adapter tiles of 16
   const bool zon = FUP && g.r > 0;
   const __amdgpu_buffer_rsrc_t ra1 =
       make_rsrc(FUP ? g.fz.a1 + (int64_t)e * g.fz.a1_estride : nullptr, FUP ? (uint32_t)(g.r * K * 2) : 0u);
-  const uint32_t a1v = (zon && n < g.r) ? (uint32_t)(n * K * 2 + 64 * hh) : OOB;
+  uint32_t a1v[ZT];
+#pragma unroll
+  for (int jt = 0; jt < ZT; ++jt)
+    a1v[jt] = (zon && 16 * jt + (lane & 15) < g.r) ? (uint32_t)((16 * jt + (lane & 15)) * K * 2 + 16 * (lane >> 4)) : OOB;
 
   const __amdgpu_buffer_rsrc_t rc = make_rsrc(g.q.codes, g.q.codes_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(g.q.scale, g.q.scale_bytes);
@@ -413,8 +459,12 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   u32x4 cw[R][SPW][SM_CB];
   ChunkScale cs[R][SPW];
   u32x4 xr[R][2];  // activation pieces ride the same ring as the weights
-  u32x4 a1r[FUP ? R : 1][2];
-  f32x16 zacc = {};
+  u32x4 a1r[FUP ? R : 1][ZT];
+  f32x4 zacc[2][ZT];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int jt = 0; jt < ZT; ++jt) zacc[hf][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x16 acc[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s)
@@ -432,11 +482,12 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     *(u32x4 *)(row + 8 * xpiece_swz(xrow, 2 * xpiece + 1)) = xr[slot][1];
   };
   auto load_w = [&](int slot, int c) {
-    if constexpr (FUP) {  // this wave's A1 fragments of chunk c (block w >> 1, steps 2 (w & 1) + q)
+    if constexpr (FUP) {  // this wave's A1 fragments of chunk c (k step w: block w / 2)
       const int kb = kb0 + c * SM_CB + (w >> 1);
       const uint32_t zdead = (c < nchunks && kb < kb1) ? 0u : OOB;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) a1r[slot][q] = bload128(ra1, a1v, ((uint32_t)kb * 128 + 16u * (2 * (w & 1) + q)) | zdead);
+      for (int jt = 0; jt < ZT; ++jt)
+        a1r[slot][jt] = bload128(ra1, a1v[jt], ((uint32_t)(kb0 + c * SM_CB) * 128 + 64u * w) | zdead);
     }
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
@@ -491,7 +542,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   if constexpr (FUP) lds_barrier();  // the routing in the activation ring's space has been read
   if constexpr (FDN) {
     if (g.r > 0 && blockIdx.z == 0) {
-      uint16_t *zs = (uint16_t *)((char *)&xs + 4096);
+      uint16_t *zs = (uint16_t *)((char *)&xs + 8192);
       z2_reduce(g, tm.row0, tm.rows, (float *)&xs, zs);
 #pragma unroll
       for (int q = 0; q < 2; ++q) zf[q] = *(const u32x4 *)(zs + n * 32 + 16 * q + 8 * hh);
@@ -528,10 +579,15 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
         for (int s4 = 0; s4 < 4; ++s4) af[s4] = *(const bf16x8 *)(xb + 8 * xpiece_swz(n, 8 * b + 4 * hh + s4));
         if constexpr (FUP) {
           if (zon && b == (w >> 1)) {
-            zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16((w & 1) ? af[2] : af[0],
-                                                           __builtin_bit_cast(bf16x8, a1r[d][0]), zacc, 0, 0, 0);
-            zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16((w & 1) ? af[3] : af[1],
-                                                           __builtin_bit_cast(bf16x8, a1r[d][1]), zacc, 0, 0, 0);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const int m = 16 * hf + (lane & 15);
+              const bf16x8 xa = *(const bf16x8 *)(&xs.v[c & 3][m][0] + 8 * xpiece_swz(m, 4 * w + (lane >> 4)));
+#pragma unroll
+              for (int jt = 0; jt < ZT; ++jt)
+                zacc[hf][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, a1r[d][jt]),
+                                                                       zacc[hf][jt], 0, 0, 0);
+            }
           }
         }
         // a block past kb1 reads zero codes, which are nf4 code 0 (-1), against staged
@@ -577,7 +633,18 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
       float *red = (float *)&xs;  // [8 waves][32 tokens][32]; the ring is no longer read
       uint16_t *zs = (uint16_t *)((char *)&xs + 32768);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) red[(w * 32 + 8 * (v >> 2) + 4 * hh + (v & 3)) * 32 + n] = zacc[v];
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int jt = 0; jt < ZT; ++jt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            red[(w * 32 + 16 * hf + 4 * (lane >> 4) + v) * 32 + 16 * jt + (lane & 15)] = zacc[hf][jt][v];
+      if (ZT == 1) {  // adapter rows 16 .. 31 are zero
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[(w * 32 + 16 * hf + 4 * (lane >> 4) + v) * 32 + 16 + (lane & 15)] = 0.0f;
+      }
       lds_barrier();
       for (int o = threadIdx.x; o < 32 * 32; o += SM_THREADS) {
         float v = 0.0f;
@@ -697,7 +764,7 @@ constexpr int XMAX = 8;
 static_assert(XMAX == 8, "token rows of a direct slot");
 constexpr int XPT = 8;  // staged 16-byte activation pieces per thread: rows x blocks <= 512
 
-template <int FMT, int EPI, int CH, bool SEQ, bool FUSE>
+template <int FMT, int EPI, int CH, bool SEQ, int FUSE>
 __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g, int kb_per_split,
                                                                    int64_t split_stride, int nseq) {
   constexpr bool NF4ISH = FMT != FMT_MXFP4;
@@ -838,6 +905,27 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     };
     load_a2f(strip_of(0));
     u32x4 zf1 = {0, 0, 0, 0};  // the second 16 adapter columns (two-launch forward)
+    // z1 of the two-launch forward (gate_up): wave w takes the 32-wide k steps w, w + 8, ...
+    // with 16 x 16 x 32 MFMAs (tokens lane % 16, adapter rows 16 jt + lane % 16, k = 8 (lane
+    // / 16) .. +7 of the step), ZI = 16 (step, tile) items per round; the first round's A1
+    // fragments are loaded before the codes, so that waiting for them does not wait for the codes
+    constexpr int ZT = FUSE == 2 ? 2 : 1, ZI = 16;
+    const int KS32 = K / 32, zitems = FUP && lora ? ZT * ((KS32 - w + SM_WAVES - 1) / SM_WAVES) : 0;
+    const __amdgpu_buffer_rsrc_t ra1 =
+        make_rsrc(FUP ? g.fz.a1 + (int64_t)e * g.fz.a1_estride : nullptr, FUP ? (uint32_t)(g.r * K * 2) : 0u);
+    u32x4 a1f[FUP ? ZI : 1];
+    auto load_a1_round = [&](int i0) {
+#pragma unroll
+      for (int i = 0; i < ZI; ++i) {
+        const int it = i0 + i, jt = it % ZT, st = w + SM_WAVES * (it / ZT);
+        const int j = 16 * jt + (lane & 15);
+        const uint32_t voff = j < g.r ? (uint32_t)(j * K * 2 + 16 * (lane >> 4)) : OOB;
+        a1f[i] = bload128(ra1, voff, it < zitems ? (uint32_t)st * 64 : OOB);
+      }
+    };
+    if constexpr (FUP) {
+      if (zitems > 0) load_a1_round(0);
+    }
     // the code stages: [waves][32 strip rows][2 CH pieces of 16 bytes], pieces swizzled
     char *stage0 = (char *)small_lds + ((xrows * xrow_len * 2 + 15) & ~15);
     char *stage = stage0 + w * (32 * CH * 32);
@@ -950,7 +1038,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     if constexpr (FUP) lds_barrier();  // the routing in the staged activations' space has been read
     if constexpr (FDN) {
       if (lora) {  // z2 of the slot's rows from the gate_up launch's partial sums
-        uint16_t *zs = (uint16_t *)(stage0 + 4096);
+        uint16_t *zs = (uint16_t *)(stage0 + 8192);
         z2_reduce(g, tm.row0, xrows, (float *)stage0, zs);
         za0 = *(const u32x4 *)(zs + xrow * 32 + 8 * hh);
         zf1 = *(const u32x4 *)(zs + xrow * 32 + 16 + 8 * hh);
@@ -970,31 +1058,32 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
       // 16-wide k steps w, w + 8, ... (32 tokens x 32 adapter rows per MFMA), 16 A1
       // fragments in flight per round; then the waves' products are added in wave order
       if (lora) {
-        const __amdgpu_buffer_rsrc_t ra1 = make_rsrc(g.fz.a1 + (int64_t)e * g.fz.a1_estride, (uint32_t)(g.r * K * 2));
-        const uint32_t a1v = n < g.r ? (uint32_t)(n * K * 2 + 16 * hh) : OOB;
-        const int KS = K / 16;
-        f32x16 zacc = {};
-        for (int s0 = w; s0 < KS; s0 += SM_WAVES * 16) {
-          u32x4 bfr[16];
+        const int m = lane & 15, xr16 = m < xrows ? m : 0;  // token row of this lane's A fragment
+        const uint16_t *xs16 = xs + xr16 * xrow_len;
+        f32x4 zacc[ZT];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int st = s0 + SM_WAVES * i;
-            bfr[i] = bload128(ra1, a1v, st < KS ? (uint32_t)st * 32 : OOB);
-          }
+        for (int jt = 0; jt < ZT; ++jt) zacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i0 = 0; i0 < zitems; i0 += ZI) {
+          if (i0 > 0) load_a1_round(i0);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int st = s0 + SM_WAVES * i;
-            if (st < KS) {
-              const int c = 2 * (st & 3) + hh;  // 8-element piece of block st / 4
-              const bf16x8 af = *(const bf16x8 *)(xsrc + (st >> 2) * 64 + ((c ^ (xrow & 7)) * 8));
-              zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bfr[i]), zacc, 0, 0, 0);
+          for (int i = 0; i < ZI; ++i) {
+            const int it = i0 + i, jt = it % ZT, st = w + SM_WAVES * (it / ZT);
+            if (it < zitems) {
+              const int c = 4 * (st & 1) + (lane >> 4);  // 8-element piece of block st / 2
+              const bf16x8 xa = *(const bf16x8 *)(xs16 + (st >> 1) * 64 + ((c ^ (xr16 & 7)) * 8));
+              zacc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8, a1f[i]), zacc[jt], 0, 0, 0);
             }
           }
         }
         float *red = (float *)stage0;  // [8 waves][8 tokens][32]
         uint16_t *zs = (uint16_t *)(stage0 + SM_WAVES * XMAX * 32 * 4);
+        if ((lane >> 4) < 2) {  // tokens 4 (lane / 16) + v < 8
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[(w * XMAX + 4 * hh + v) * 32 + n] = zacc[v];
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              red[(w * XMAX + 4 * (lane >> 4) + v) * 32 + 16 * jt + (lane & 15)] = jt < ZT ? zacc[jt % ZT][v] : 0.0f;
+        }
         lds_barrier();
         if (threadIdx.x < XMAX * 32) {
           float v = 0.0f;
@@ -1193,7 +1282,7 @@ static SmallPlan small_plan(const GroupedArgs &a, int strips_per_expert, int spl
   return p;
 }
 
-template <int FMT, int EPI, bool FUSE>
+template <int FMT, int EPI, int FUSE>
 static void launch_small_plan(const GroupedArgs &a, const SmallPlan &p, int kbs, int64_t split_stride, hipStream_t s) {
   if (p.direct) {
     if (p.nseq > 1) {
@@ -1215,8 +1304,9 @@ static SmallPlan launch_small(const GroupedArgs &a, int strips_per_expert, int s
     constexpr int FMT = decltype(fmt_tag)::value;
     const SmallPlan p = small_plan<FMT>(a, strips_per_expert, splits, kbs);
     if (launch) {
-      if (a.fz.on) launch_small_plan<FMT, EPI, true>(a, p, kbs, split_stride, s);
-      else launch_small_plan<FMT, EPI, false>(a, p, kbs, split_stride, s);
+      if (!a.fz.on) launch_small_plan<FMT, EPI, 0>(a, p, kbs, split_stride, s);
+      else if (a.r <= 16) launch_small_plan<FMT, EPI, 1>(a, p, kbs, split_stride, s);
+      else launch_small_plan<FMT, EPI, 2>(a, p, kbs, split_stride, s);
     }
     return p;
   };
