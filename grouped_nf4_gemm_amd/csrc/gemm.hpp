@@ -445,6 +445,31 @@ struct LDirectAN {
           r, (__attribute__((address_space(3))) void *)&t.v[(v * NI + i) * 8 * BK], 16, voff[i], soff, 0, 0);
   }
 };
+// Direct-to-LDS loads of a [256][64] bf16 tile in the A (or NK B) layout from a dense
+// row-major matrix: tile row r <- matrix row src(r) (negative: zero), columns [k0, k0 + 64)
+// of which those at or past kbound read as zero.  NW loading waves (v: this wave).
+template <int NW>
+struct LDirectRows {
+  static constexpr int NI = 32 / NW;
+  uint32_t voff[NI];
+  template <class Src>
+  __device__ __forceinline__ void init(int v, Src src, int64_t ld, int k0, int kbound) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = (v * NI + i) * 8 + (l >> 3);
+      const int lc = swz_chunk(r, l & 7);  // the swizzle is its own inverse
+      const int64_t row = src(r);
+      voff[i] = (row >= 0 && k0 + lc * 8 < kbound) ? (uint32_t)((row * ld + k0 + lc * 8) * 2) : OOB;
+    }
+  }
+  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t r, uint16_t *tile, int v) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void *)&tile[(v * NI + i) * 8 * BK], 16, voff[i], 0, 0, 0);
+  }
+};
 // All eight waves of a 512-thread workgroup load.
 struct LDirectA : LDirectAN<8> {
   __device__ __forceinline__ void init(int rows, int64_t row0, const int32_t *__restrict__ gather, int gdiv,

@@ -647,10 +647,46 @@ struct WSProducer {
   __device__ __forceinline__ void issue_a(ATile &t, int slab, int nmain) {
     la.issue(ra, t, (uint32_t)(slab * BK * 2) | dead(slab, nmain), v);
   }
+  // The LoRA K-extension as nl = ceil(r / 64) more slabs nmain, nmain + 1: tile rows of
+  // the adapter input (xa, sorted rows) and of the adapter's B rows (xb, mapped like the
+  // weight rows) go straight into the next buffers; columns at or past r read as zero.
+  struct LoraCtx {
+    int nl;
+    int r, rows, Nrows;
+    int64_t row0, ldxa, ldxb;
+    RowMap map;
+    __amdgpu_buffer_rsrc_t rxa, rxb;
+  };
+  struct RowsA {
+    int rows;
+    int64_t row0;
+    __device__ __forceinline__ int64_t operator()(int r) const { return r < rows ? row0 + r : -1; }
+  };
+  struct RowsB {
+    RowMap map;
+    int Nrows;
+    __device__ __forceinline__ int64_t operator()(int r) const {
+      const int n = map(r);
+      return n < Nrows ? n : -1;
+    }
+  };
+  __device__ __forceinline__ void lora_slab(const LoraCtx &lc, int x, ATile &at, LTile &bt) {
+    LDirectRows<4> da, db;
+    da.init(v, RowsA{lc.rows, lc.row0}, lc.ldxa, x * BK, lc.r);
+    db.init(v, RowsB{lc.map, lc.Nrows}, lc.ldxb, x * BK, lc.r);
+    da.issue(lc.rxa, at.v, v);
+    db.issue(lc.rxb, &bt.v[0][0], v);
+    slab_barrier<0>();
+  }
   // iteration s: the A rows of slab s+1, the B codes of slab s+3, and the decode of slab s+1
-  // (codes loaded at iteration s-2) into buffers P = (s+1) % 2; Q = s % 3
+  // (codes loaded at iteration s-2) into buffers P = (s+1) % 2; Q = s % 3; past the main
+  // slabs, LoRA slab s+1 - nmain instead.
   template <int P, int Q>
-  __device__ __forceinline__ void body(int s, int nmain) {
+  __device__ __forceinline__ void body(int s, int nmain, const LoraCtx &lc) {
+    if (s + 1 >= nmain && lc.nl > 0) {
+      lora_slab(lc, s + 1 - nmain, atile<P>(), (P == 0 ? B0 : B1).nk);
+      return;
+    }
     issue_a(atile<P>(), s + 1, nmain);
     __builtin_amdgcn_sched_barrier(0);
     fetch_b<Q>(s + 3, nmain);
@@ -659,7 +695,10 @@ struct WSProducer {
     slab_barrier<LOADS>();  // A rows of slab s+1 landed; only the B codes of slab s+3 in flight
   }
   __device__ __forceinline__ void run(const GroupedArgs &g, int e, int n0, const RowMap &map, int Nrows,
-                                      const TileM &tm, int nmain) {
+                                      const TileM &tm, int nmain, int nl) {
+    const LoraCtx ls{nl, g.r, tm.rows, Nrows, tm.row0, g.ldxa, g.ldxb, map,
+                     make_rsrc(g.xa, (uint32_t)((int64_t)g.M * g.ldxa * 2)),
+                     make_rsrc(g.xb + (int64_t)e * g.xb_estride, (uint32_t)((int64_t)Nrows * g.ldxb * 2))};
     la.init(v, tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
     if constexpr (KN) {
       kn[0][0].init(g.q, e, n0, g.N, p);
@@ -679,19 +718,21 @@ struct WSProducer {
     wait_vmcnt<2 * LOADS>();  // A rows and B codes of slab 0
     decode<0, 0>();
     slab_barrier<2 * LOADS>();
+    // bodies 0 .. nb-1: the last prepares the last LoRA slab (slab nmain when there is none)
+    const int nb = nmain + max(nl, 1) - 1;
     for (int s = 0;; s += 6) {
-      body<1, 0>(s, nmain);
-      if (s + 1 >= nmain) break;
-      body<0, 1>(s + 1, nmain);
-      if (s + 2 >= nmain) break;
-      body<1, 2>(s + 2, nmain);
-      if (s + 3 >= nmain) break;
-      body<0, 0>(s + 3, nmain);
-      if (s + 4 >= nmain) break;
-      body<1, 1>(s + 4, nmain);
-      if (s + 5 >= nmain) break;
-      body<0, 2>(s + 5, nmain);
-      if (s + 6 >= nmain) break;
+      body<1, 0>(s, nmain, ls);
+      if (s + 1 >= nb) break;
+      body<0, 1>(s + 1, nmain, ls);
+      if (s + 2 >= nb) break;
+      body<1, 2>(s + 2, nmain, ls);
+      if (s + 3 >= nb) break;
+      body<0, 0>(s + 3, nmain, ls);
+      if (s + 4 >= nb) break;
+      body<1, 1>(s + 4, nmain, ls);
+      if (s + 5 >= nb) break;
+      body<0, 2>(s + 5, nmain, ls);
+      if (s + 6 >= nb) break;
     }
     wait_vmcnt<0>();  // nothing in flight past the main loop
   }
@@ -712,10 +753,11 @@ __global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
   const RowMap map{n0, g.I, SWIGLU, SWIGLU && g.act == 1};
   const int Nrows = SWIGLU ? 2 * g.I : g.N;
   const int nmain = g.K / BK;
+  // the LoRA K-extension: ceil(r / 64) more slabs of the producers' pipeline
+  const int nl = (g.r + BK - 1) / BK;
   if (threadIdx.x >= WS_CONSUMERS) {
     WSProducer<BKIND, FMT> pr(tb, A0, A1, B0, B1, g);
-    pr.run(g, e, n0, map, Nrows, tm, nmain);
-    lora_barriers(g);
+    pr.run(g, e, n0, map, Nrows, tm, nmain, nl);
     return;
   }
   LMma mma;
@@ -733,7 +775,11 @@ __global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
     consumer_barrier();
     if (s + 2 >= nmain) break;
   }
-  lora_extension(mma, g, tm, e, map, Nrows, A0, B0.nk);
+  for (int x = 0; x < nl; ++x) {  // LoRA slab x in buffers (nmain + x) % 2, NK layout, k < r
+    const bool odd = (nmain + x) & 1;
+    mma.step<false>(odd ? A1 : A0, (odd ? B1 : B0).nk, min(4, (g.r - x * BK + 15) / 16));
+    if (x + 1 < nl) consumer_barrier();
+  }
   large_epilogue<EPI>(mma, g, tm, n0);
 }
 
