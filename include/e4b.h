@@ -151,11 +151,19 @@ int32_t e4b_version(void);
 const char *e4b_status_str(int32_t status);
 
 /* Bytes of caller-owned device workspace that e4b_moe_fwd / e4b_moe_dgrad /
- * e4b_lora_wgrad need for this layer (adapters may be NULL).  Host call. */
+ * e4b_lora_wgrad need for this layer (adapters may be NULL).  Host call, no device work;
+ * bad shapes or adapters give E4B_ERR_INVALID_ARG and leave *bytes untouched.  (The
+ * workspace is this library's own contract: the pages leave memory management to the
+ * caller's framework.) */
 e4b_status e4b_moe_workspace_size(const e4b_moe_desc *desc, const e4b_lora *l_gu,
                                   const e4b_lora *l_dn, size_t *bytes);
 
-/* Forward.  w_gu: gate_up stack [E, 2I, H]; w_dn: down stack [E, H, I] (same fmt).
+/* Forward (method page, "The abstraction that fails, and what replaces it": each routed
+ * expert's frozen packed projection plus its own low-rank delta, added before the
+ * activation, act(W_e x + B[e] A[e] x); "Why it happens": the trainable term is
+ * scaling * (x A[e]^T) B[e]^T; README, "The package family": one grouped launch over the
+ * 4-bit-packed stacks with in-register decode and fp32 accumulation).
+ *  w_gu: gate_up stack [E, 2I, H]; w_dn: down stack [E, H, I] (same fmt).
  *  x bf16 [T, H]; ids int32 [T, topk]; topw fp32 [T, topk]; y bf16 [T, H] (written).
  *  ws: workspace of e4b_moe_workspace_size bytes.  With E4B_TRAIN the workspace
  *  then holds the routing and activations that dgrad and wgrad read: keep it and
@@ -182,7 +190,11 @@ e4b_status e4b_moe_fwd_noalloc(const e4b_moe_desc *desc, const e4b_qweight *w_gu
                                const uint16_t *x, const int32_t *ids, const float *topw, uint16_t *y,
                                void *stream);
 
-/* Input gradient after a training forward with the same arguments.
+/* Input gradient after a training forward with the same arguments (method page, "The
+ * abstraction that fails, and what replaces it": the grouped forward with optional dgrad;
+ * "Why it happens": the base projection is dequantised again in the backward, so nothing
+ * dequantised is held between the calls).  Needs E4B_TRAIN in desc->flags and the
+ * forward's workspace (else E4B_ERR_INVALID_ARG / E4B_ERR_WORKSPACE, nothing enqueued).
  *  dy bf16 [T, H] -> dx bf16 [T, H] (overwritten); d_topw fp32 [T, topk]
  *  (nullable; d(sum dy*y)/d topw).  Writes the dgrad activations that
  *  e4b_lora_wgrad reads into ws. */
@@ -191,14 +203,19 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu,
                          const int32_t *ids, const float *topw, const uint16_t *dy,
                          uint16_t *dx, float *d_topw, void *ws, size_t ws_bytes, void *stream);
 
-/* LoRA weight gradients after e4b_moe_dgrad, overwritten, fp32:
+/* Gradients of the trainable per-expert adapters (method page, "The abstraction that
+ * fails, and what replaces it": A[e] / B[e] trainable, the packed base frozen), after
+ * e4b_moe_dgrad on the same workspace; overwritten, fp32, device:
  *  dA_gu [E, r1, H], dB_gu [E, 2I, r1], dA_dn [E, r2, I], dB_dn [E, H, r2].
  *  Experts that received no rows get zeros.  x is the forward's input. */
 e4b_status e4b_lora_wgrad(const e4b_moe_desc *desc, const e4b_lora *l_gu, const e4b_lora *l_dn,
                           const uint16_t *x, void *ws, size_t ws_bytes, float *dA_gu,
                           float *dB_gu, float *dA_dn, float *dB_dn, void *stream);
 
-/* Routing metadata (stable grouping of the T*topk routed rows by expert):
+/* Routing metadata, the grouping that lets one launch serve every expert's rows (README,
+ * "The package family": one launch over the expert stacks; method page, "Why it
+ * happens": the delta is applied per routed expert).  Stable grouping of the T*topk routed
+ * rows by expert, device outputs, overwritten:
  *  cnt int32 [E+1] (cnt[E] = rows with an id outside [0, E)); off int32 [E+1]
  *  (exclusive scan, off[E] = valid rows); perm int32 [T*topk] (sorted position ->
  *  flat index t*topk+j, ascending flat index within an expert, -1 past off[E]);
@@ -226,22 +243,32 @@ e4b_status e4b_router_topk(const float *logits, int32_t T, int32_t E, int32_t to
 e4b_status e4b_router_bwd(const float *topw, const float *d_topw, const int32_t *ids, int32_t T, int32_t E,
                           int32_t topk, float *d_logits, void *stream);
 
-/* Decode expert `expert` of a stack (or the whole stack if expert < 0) to fp32
- * and/or bf16 [N, K] row-major (either output nullable). */
+/* Dequantise (method page, "The abstraction that fails, and what replaces it": the packed
+ * expert base, NF4 by default; README, opening section: the storage modes of the base):
+ * expert `expert` of a stack (or the whole stack if expert < 0) to fp32 and/or bf16
+ * [N, K] row-major, device, overwritten (either output nullable).  The values are those
+ * the GEMM tiles use.  An expert index >= E, no output or a malformed stack:
+ * E4B_ERR_INVALID_ARG (an unknown format: E4B_ERR_UNSUPPORTED), nothing enqueued. */
 e4b_status e4b_dequant(const e4b_qweight *w, int32_t expert, float *out_f32,
                        uint16_t *out_bf16, void *stream);
 
-/* Quantise an fp32 stack w [E, N, K] into codes/scale/scale2 laid out as in
- * e4b_qweight (nearest code, ties to the lower NF4 index / the even E2M1 code). */
+/* Quantise (README, opening section: NF4 / FP4 / int8 / fp8 storage of the frozen base;
+ * method page, "The abstraction that fails, and what replaces it": quant_type chooses it
+ * at load) an fp32 stack w [E, N, K] (device) into codes / scale / scale2 laid out as in
+ * e4b_qweight (device, caller-allocated, overwritten): nearest code, ties to the lower NF4
+ * index / the even E2M1 code; INT8 and FP8 round to nearest even.  An unknown format is
+ * E4B_ERR_UNSUPPORTED. */
 e4b_status e4b_quantize(int32_t fmt, int32_t E, int32_t N, int32_t K, const float *w,
                         uint8_t *codes, void *scale, float *scale2, void *stream);
 
 /* Synchronises `stream` and returns the number of routed rows that the last
- * forward on this workspace dropped for an out-of-range expert id. */
+ * forward on this workspace dropped for an out-of-range expert id.  (A diagnostic of this
+ * library, no passage of the pages; the routed rows themselves are defined above.) */
 e4b_status e4b_moe_check(const e4b_moe_desc *desc, const void *ws, void *stream,
                          int32_t *dropped_rows);
 
-/* Observability: kernel launches since the last reset, per kernel family. */
+/* Observability: kernel launches since the last reset, per kernel family (this library's
+ * own; README, "What is measured", is what its figures are compared with). */
 typedef struct {
   int64_t launches_total;
   int64_t route, lora_a, gemm_gate_up, gemm_down, combine;
