@@ -864,6 +864,28 @@ struct LMma {
       for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
   }
+  // A k-step range over only the first ni (< 4) 32-row sub-tiles of this wave's 128 rows:
+  // the tile's other rows are padding past the expert's rows (its last row tile), so their
+  // A fragments and MFMAs are skipped (ni is the same for the whole wave).
+  template <bool KN, class BT>
+  __device__ __forceinline__ void step_rows(const ATile &A, const BT &B, int ksteps, int ni) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 31;
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const int kc = ks * 2 + (lane >> 5);
+      bf16x8 b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = bfrag(B, j, ks);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < ni) {
+          const bf16x8 a = *(const bf16x8 *)&A.v[aswz(wm() * 128 + i * 32 + r, kc)];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
   template <bool KN, class BT>
   __device__ __forceinline__ void kstep(const ATile &A, const BT &B, int ks) {
     Frag f;

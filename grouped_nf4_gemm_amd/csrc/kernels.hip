@@ -766,18 +766,33 @@ __global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
     if constexpr (KN) return b.kn;
     else return b.nk;
   };
+  // 32-row sub-tiles of this wave's 128 rows that hold rows of the expert: fewer than 4 only in
+  // an expert's last row tile, whose padding rows then cost no MFMAs
+  const int half_rows = tm.rows - LMma::wm() * 128;
+  const int ni = half_rows <= 0 ? 0 : min(4, (half_rows + 31) / 32);
   consumer_barrier();  // slab 0
-  for (int s = 0;; s += 2) {
-    mma.step<KN>(A0, bt(B0), 4);
-    consumer_barrier();
-    if (s + 1 >= nmain) break;
-    mma.step<KN>(A1, bt(B1), 4);
-    consumer_barrier();
-    if (s + 2 >= nmain) break;
+  if (ni == 4) {
+    for (int s = 0;; s += 2) {
+      mma.step<KN>(A0, bt(B0), 4);
+      consumer_barrier();
+      if (s + 1 >= nmain) break;
+      mma.step<KN>(A1, bt(B1), 4);
+      consumer_barrier();
+      if (s + 2 >= nmain) break;
+    }
+  } else {
+    for (int s = 0;; s += 2) {
+      mma.step_rows<KN>(A0, bt(B0), 4, ni);
+      consumer_barrier();
+      if (s + 1 >= nmain) break;
+      mma.step_rows<KN>(A1, bt(B1), 4, ni);
+      consumer_barrier();
+      if (s + 2 >= nmain) break;
+    }
   }
   for (int x = 0; x < nl; ++x) {  // LoRA slab x in buffers (nmain + x) % 2, NK layout, k < r
     const bool odd = (nmain + x) & 1;
-    mma.step<false>(odd ? A1 : A0, (odd ? B1 : B0).nk, min(4, (g.r - x * BK + 15) / 16));
+    mma.step_rows<false>(odd ? A1 : A0, (odd ? B1 : B0).nk, min(4, (g.r - x * BK + 15) / 16), ni);
     if (x + 1 < nl) consumer_barrier();
   }
   large_epilogue<EPI>(mma, g, tm, n0);
