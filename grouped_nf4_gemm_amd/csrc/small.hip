@@ -374,7 +374,8 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
     return;
   }
   const int e = tm.e;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index, in a scalar register: offsets derived from it are wave-uniform
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const uint32_t l4 = (uint32_t)lane * 4;
   const int N = g.q.N, K = g.q.K, KB = K / 64;
@@ -793,7 +794,8 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
     return;
   }
   const int e = tm.e;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index, in a scalar register: offsets derived from it are wave-uniform
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const uint32_t l4 = (uint32_t)lane * 4;
   const int N = g.q.N, K = g.q.K, KB = K / 64;
