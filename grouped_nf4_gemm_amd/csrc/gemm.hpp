@@ -105,33 +105,33 @@ __device__ __forceinline__ void st_lds16(uint16_t *p, u32x4 v) { *(u32x4 *)p = v
 
 // ---------------------------------------------------------------- A loader
 // Rows of a row-major bf16 matrix (k contiguous).  Tile row i <-> sorted row
-// row0 + i; with a gather, the source row is gather[row0 + i] / gdiv.
+// row0 + i; with a gather, the source row is gather[row0 + i] / gdiv.  Eight consecutive
+// lanes read the 128 bytes of one row's slab (one cache line per eight lanes); pass v takes
+// tile rows 32 v .. 32 v + 31.  The source rows are resolved once per tile (init).
 template <int BR>
 struct RowLoader {
-  static constexpr int VECS = BR / 32;                 // 16-byte vectors per thread
-  static constexpr int TPR = NTHREADS / BR;            // threads per row
+  static constexpr int VECS = BR / 32;  // passes (16-byte vectors per thread)
   u32x4 buf[VECS];
-  __device__ __forceinline__ void fetch(const uint16_t *__restrict__ base, int64_t ld, int rows,
-                                        int64_t src_row_of_first, const int32_t *__restrict__ gather,
-                                        int gdiv, int k0, int kbound) {
-    const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
-    const int kk = k0 + part * VECS * 8;
-    bool ok = i < rows;
-    int64_t src = 0;
-    if (ok) src = gather ? (int64_t)(gather[src_row_of_first + i] / gdiv) : src_row_of_first + i;
-    const uint16_t *p = base + src * ld + kk;
+  int64_t src[VECS];  // element offset of the pass's source row, or -1
+  __device__ __forceinline__ void init(int64_t ld, int rows, int64_t row0, const int32_t *__restrict__ gather,
+                                       int gdiv) {
+    const int r = threadIdx.x >> 3;
 #pragma unroll
     for (int v = 0; v < VECS; ++v) {
-      if (ok && kk + v * 8 < kbound)
-        buf[v] = *(const u32x4 *)(p + v * 8);
-      else
-        buf[v] = u32x4{0, 0, 0, 0};
+      const int i = v * 32 + r;
+      src[v] = i < rows ? (gather ? (int64_t)(gather[row0 + i] / gdiv) : row0 + i) * ld : -1;
     }
   }
-  __device__ __forceinline__ void store(LdsTile<BR> &t) {
-    const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
+  __device__ __forceinline__ void fetch(const uint16_t *__restrict__ base, int k0, int kbound) {
+    const int kk = k0 + (threadIdx.x & 7) * 8;
 #pragma unroll
-    for (int v = 0; v < VECS; ++v) st_lds16(&t.v[i][part * VECS * 8 + v * 8], buf[v]);
+    for (int v = 0; v < VECS; ++v)
+      buf[v] = (src[v] >= 0 && kk < kbound) ? *(const u32x4 *)(base + src[v] + kk) : u32x4{0, 0, 0, 0};
+  }
+  __device__ __forceinline__ void store(LdsTile<BR> &t) {
+    const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
+#pragma unroll
+    for (int v = 0; v < VECS; ++v) st_lds16(&t.v[v * 32 + r][c * 8], buf[v]);
   }
 };
 
@@ -153,30 +153,25 @@ struct RowMap {
 };
 
 // ---------------------------------------------------------------- dense B, NK
-// B tile rows n (mapped) of a per-expert bf16 matrix [N, ld] (k contiguous).
+// B tile rows n (mapped) of a per-expert bf16 matrix [N, ld] (k contiguous), read like
+// RowLoader: eight lanes per row, pass v takes tile rows 32 v .. 32 v + 31.
 template <int BR>
 struct DenseNKLoader {
   static constexpr int VECS = BR / 32;
-  static constexpr int TPR = NTHREADS / BR;
   u32x4 buf[VECS];
   __device__ __forceinline__ void fetch(const uint16_t *__restrict__ base, int64_t ld,
                                         const RowMap &map, int N, int k0, int kbound) {
-    const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
-    const int n = map(i);
-    const int kk = k0 + part * VECS * 8;
-    const uint16_t *p = base + (int64_t)n * ld + kk;
+    const int r = threadIdx.x >> 3, kk = k0 + (threadIdx.x & 7) * 8;
 #pragma unroll
     for (int v = 0; v < VECS; ++v) {
-      if (n < N && kk + v * 8 < kbound)
-        buf[v] = *(const u32x4 *)(p + v * 8);
-      else
-        buf[v] = u32x4{0, 0, 0, 0};
+      const int n = map(v * 32 + r);
+      buf[v] = (n < N && kk < kbound) ? *(const u32x4 *)(base + (int64_t)n * ld + kk) : u32x4{0, 0, 0, 0};
     }
   }
   __device__ __forceinline__ void store(LdsTile<BR> &t) {
-    const int i = threadIdx.x / TPR, part = threadIdx.x % TPR;
+    const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
 #pragma unroll
-    for (int v = 0; v < VECS; ++v) st_lds16(&t.v[i][part * VECS * 8 + v * 8], buf[v]);
+    for (int v = 0; v < VECS; ++v) st_lds16(&t.v[v * 32 + r][c * 8], buf[v]);
   }
 };
 
