@@ -902,4 +902,78 @@ struct LMma {
   }
 };
 
+// ---------------------------------------------------------------- k-major tiles
+// Tiles of the weight-gradient products, whose reduction index (the routed rows) is the
+// row index of both operands in memory: [64 k][W] bf16 rows copied as they are, with a
+// row pitch of W + 32 elements (320 or 192 bytes), so that the four rows one 16-lane
+// group of a transposing fragment read touches fall in distinct banks.
+template <int W>
+struct KTile {
+  static constexpr int PITCH = W + 32;
+  uint16_t v[BK][PITCH];
+};
+// MFMA fragment (32 columns at col0, k-step ks) from a KTile with the transposing LDS
+// read: within each 16-lane group, lane i receives element i % 4 of the 8-byte pieces
+// addressed by lanes 4 j + i / 4; lane 4 kr + c addresses row kr, columns 4 c .. 4 c + 3
+// of the group's 16 columns, so lane i ends up with column i at four consecutive k.  The
+// fragment layout is the same for the A and the B operand.
+template <int W>
+__device__ __forceinline__ bf16x8 ktile_frag(const KTile<W> &t, int ks, int col0) {
+  typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
+  const int lane = threadIdx.x & 63;
+  const int G = lane >> 4, i = lane & 15;
+  const int row = ks * 16 + (G >> 1) * 8 + (i >> 2);
+  const int col = col0 + (G & 1) * 16 + (i & 3) * 4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&t.v[row][col]));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&t.v[row + 4][col]));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+// Rows k0 .. k0 + 63 (of krows) of a row-major [rows][ld] bf16 matrix, columns col0 ..
+// col0 + W - 1 (of ncols) into a KTile: W / 8 lanes read one row's 2 W bytes, each pass
+// takes 256 / (W / 8) rows.  Row k is source row row0 + k, or gather[row0 + k] / gdiv.
+template <int W>
+struct KRowLoader {
+  static constexpr int LPR = W / 8, RPP = NTHREADS / LPR, PASSES = BK / RPP;
+  u32x4 buf[PASSES];
+  __device__ __forceinline__ void fetch(const uint16_t *__restrict__ base, int64_t ld, int col0, int ncols,
+                                        int row0, int krows, const int32_t *__restrict__ gather, int gdiv, int k0) {
+    const int c = threadIdx.x % LPR, r = threadIdx.x / LPR;
+    const int col = col0 + c * 8;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int kk = k0 + p * RPP + r;
+      const bool ok = kk < krows && col < ncols;
+      int64_t src = 0;
+      if (ok) src = gather ? (int64_t)(gather[row0 + kk] / gdiv) : (int64_t)(row0 + kk);
+      buf[p] = ok ? *(const u32x4 *)(base + src * ld + col) : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(KTile<W> &t) {
+    const int c = threadIdx.x % LPR, r = threadIdx.x / LPR;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) st_lds16(&t.v[p * RPP + r][c * 8], buf[p]);
+  }
+};
+// Products over KTiles: acc[i][j] += A-tile columns (wm TM + i) 32 .. x B-tile columns
+// (wn TN + j) 32 .., over `ksteps` 16-row k steps.  The accumulators are those of Mma.
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void mma_ktiles(Mma<BM, BN, WM, WN> &m, const KTile<BM> &A, const KTile<BN> &B,
+                                           int ksteps) {
+  constexpr int TM = Mma<BM, BN, WM, WN>::TM, TN = Mma<BM, BN, WM, WN>::TN;
+  const int wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+  for (int ks = 0; ks < ksteps; ++ks) {
+    bf16x8 a[TM], b[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) a[i] = ktile_frag(A, ks, (wm * TM + i) * 32);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = ktile_frag(B, ks, (wn * TN + j) * 32);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        m.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], m.acc[i][j], 0, 0, 0);
+  }
+}
+
 }  // namespace e4b

@@ -871,32 +871,32 @@ bool launch_lora_a(const GroupedArgs &a, hipStream_t s) {
 // C[e][a][b] = sum over the routed rows m of expert e of P[m][a] * Q[m][b].
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
-  __shared__ LdsTile<BM> As;
-  __shared__ LdsTile<BN> Bs;
+  // both operands stay in their memory order, [routed row][column], in LDS; the MFMA
+  // fragments come out of the transposing LDS read
+  __shared__ KTile<BM> As;
+  __shared__ KTile<BN> Bs;
   const int e = blockIdx.z / g.nsplit, sp = blockIdx.z % g.nsplit;
   const int a0 = blockIdx.y * BM, b0 = blockIdx.x * BN;
   const int row0 = g.off[e], krows = g.off[e + 1] - g.off[e];
   Mma<BM, BN, WM, WN> mma;
   mma.zero();
-  KMajorLoader<BM> la;
-  KMajorLoader<BN> lb;
+  KRowLoader<BM> la;
+  KRowLoader<BN> lb;
   // this split's slabs of the expert's rows
   const int nall = (krows + BK - 1) / BK, chunk = (nall + g.nsplit - 1) / g.nsplit;
   const int s0 = min(nall, sp * chunk), s1 = min(nall, s0 + chunk);
-  if (s0 < s1) {
-    la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, s0 * BK);
-    lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, s0 * BK);
-  }
+  auto fetch = [&](int s) {
+    la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, s * BK);
+    lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, s * BK);
+  };
+  if (s0 < s1) fetch(s0);
   for (int s = s0; s < s1; ++s) {
     __syncthreads();
     la.store(As);
     lb.store(Bs);
     __syncthreads();
-    if (s + 1 < s1) {
-      la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, (s + 1) * BK);
-      lb.fetch(g.Q, g.ldq, b0, g.Nb, row0, krows, g.q_gather, g.q_gdiv, (s + 1) * BK);
-    }
-    mma.step(As, Bs, 4);
+    if (s + 1 < s1) fetch(s + 1);
+    mma_ktiles(mma, As, Bs, 4);
   }
   // every split writes its (possibly zero) partial sums
   float *C = g.nsplit > 1 ? g.part + ((int64_t)sp * g.E + e) * g.Na * g.Nb : g.C + (int64_t)e * g.Na * g.Nb;
