@@ -928,7 +928,43 @@ bool launch_wgrad(const WgradArgs &a, hipStream_t s) {
 }
 
 // =============================================================== combine and friends
-// y[t] = bf16(sum_j w[t,j] * O[inv[t*k+j]]), fp32 sum in j order.
+// y[t] = bf16(sum_j w[t,j] * O[inv[t*k+j]]), fp32 sum in j order.  One partial sum (the
+// training forward): every choice's row piece is loaded before any is added, so the k
+// loads of a thread are in flight together.
+template <int U>  // 1024-column chunks per workgroup
+__global__ void combine1_kernel(const float *__restrict__ O, const int32_t *__restrict__ inv,
+                                const float *__restrict__ topw, int k, int H, uint16_t *__restrict__ y) {
+  constexpr int KP = 8;  // choices held in registers (k <= KP)
+  const int t = blockIdx.x;
+  int pj[KP];
+  float wj[KP];
+#pragma unroll
+  for (int j = 0; j < KP; ++j) {
+    pj[j] = j < k ? inv[(int64_t)t * k + j] : -1;
+    wj[j] = j < k ? topw[(int64_t)t * k + j] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int h = (blockIdx.y * U + u) * 1024 + threadIdx.x * 4;
+    if (h >= H) break;
+    f32x4 o[KP];
+#pragma unroll
+    for (int j = 0; j < KP; ++j) o[j] = pj[j] >= 0 ? *(const f32x4 *)(O + (int64_t)pj[j] * H + h) : f32x4{0.f, 0.f, 0.f, 0.f};
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      if (pj[j] < 0) continue;
+      a0 += wj[j] * o[j][0];
+      a1 += wj[j] * o[j][1];
+      a2 += wj[j] * o[j][2];
+      a3 += wj[j] * o[j][3];
+    }
+    u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+    *(u32x2 *)(y + (int64_t)t * H + h) = out;
+  }
+}
+
+// Any number of partial sums (up to COMBINE_MAX_SPLITS), added in split order first.
 template <int U>  // 1024-column chunks per workgroup
 __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t split_stride,
                                const int32_t *__restrict__ inv, const float *__restrict__ topw, int k,
@@ -950,10 +986,7 @@ __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t 
     const int h = (blockIdx.y * U + u) * 1024 + threadIdx.x * 4;
     if (h >= H) break;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int p = j < KP ? pj[j] : inv[(int64_t)t * k + j];
-      if (p < 0) continue;
-      const float w = j < KP ? wj[j] : topw[(int64_t)t * k + j];
+    auto add = [&](int p, float w) {
       f32x4 ov[COMBINE_MAX_SPLITS];
 #pragma unroll
       for (int c = 0; c < COMBINE_MAX_SPLITS; ++c)
@@ -966,6 +999,14 @@ __global__ void combine_kernel(const float *__restrict__ O, int nsplit, int64_t 
       a1 += w * o[1];
       a2 += w * o[2];
       a3 += w * o[3];
+    };
+    // the first KP choices from registers (a compile-time index each), the rest from memory
+#pragma unroll
+    for (int j = 0; j < KP; ++j)
+      if (pj[j] >= 0) add(pj[j], wj[j]);
+    for (int j = KP; j < k; ++j) {
+      const int p = inv[(int64_t)t * k + j];
+      if (p >= 0) add(p, topw[(int64_t)t * k + j]);
     }
     u32x2 out{pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
     *(u32x2 *)(y + (int64_t)t * H + h) = out;
@@ -1081,6 +1122,11 @@ bool launch_combine(const float *O, int nsplit, int64_t split_stride, const int3
   if (nsplit < 1 || nsplit > COMBINE_MAX_SPLITS) return false;
   LaunchScope ls(FAM_COMBINE, s);
   // many tokens: a workgroup per token covers up to 4 chunks (fewer, longer workgroups)
+  if (nsplit == 1 && k <= 8) {
+    if (T >= 1024) combine1_kernel<4><<<dim3(T, cdiv(H, 4096)), 256, 0, s>>>(O, inv, topw, k, H, y);
+    else combine1_kernel<1><<<dim3(T, cdiv(H, 1024)), 256, 0, s>>>(O, inv, topw, k, H, y);
+    return last_launch_ok();
+  }
   if (T >= 1024) combine_kernel<4><<<dim3(T, cdiv(H, 4096)), 256, 0, s>>>(O, nsplit, split_stride, inv, topw, k, H, y);
   else combine_kernel<1><<<dim3(T, cdiv(H, 1024)), 256, 0, s>>>(O, nsplit, split_stride, inv, topw, k, H, y);
   return last_launch_ok();
