@@ -21,7 +21,7 @@ __constant__ float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 // walks each range in order, ranking equal expert ids inside a wave64 by the
 // lanes below them (bitwise key match from ballots), which keeps the grouping
 // stable in the flat index t*k + j.
-constexpr int RT_WAVES = 8;
+constexpr int RT_WAVES = 16;
 
 __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(const int32_t *__restrict__ ids, int M,
                                                               int E, int32_t *__restrict__ cnt,
