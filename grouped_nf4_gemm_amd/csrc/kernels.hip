@@ -1223,11 +1223,43 @@ __global__ void transpose_kernel(const uint16_t *__restrict__ in, int R, int C, 
   }
 }
 
+// Narrow matrices (adapter factors: one side is the rank, at most 128): a thread takes 8
+// consecutive elements of one row of the narrow side (one 16-byte access), blockIdx.y the
+// 8-element group, so that a wave's 2-byte accesses on the other side cover 128
+// consecutive bytes.
+template <bool NARROW_IN>
+__global__ void transpose_narrow_kernel(const uint16_t *__restrict__ in, int R, int C, uint16_t *__restrict__ out) {
+  const int e = blockIdx.z, g8 = blockIdx.y * 8;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint16_t *src = in + (int64_t)e * R * C;
+  uint16_t *dst = out + (int64_t)e * R * C;
+  if constexpr (NARROW_IN) {  // C <= 128: input row i, columns g8 .. g8 + 7
+    if (i >= R) return;
+    const u32x4 v = *(const u32x4 *)(src + (int64_t)i * C + g8);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dst[(int64_t)(g8 + q) * R + i] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+  } else {  // R <= 128: output row i, elements g8 .. g8 + 7
+    if (i >= C) return;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)src[(int64_t)(g8 + 2 * q) * C + i] | ((uint32_t)src[(int64_t)(g8 + 2 * q + 1) * C + i] << 16);
+    *(u32x4 *)(dst + (int64_t)i * R + g8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 bool launch_transpose(const uint16_t *in, int E, int R, int C, uint16_t *out, hipStream_t s) {
   if (E == 0 || R == 0 || C == 0) return true;
   LaunchScope ls(FAM_TRANSPOSE, s);
-  dim3 grid(cdiv(C, 32), cdiv(R, 32), E);
-  transpose_kernel<<<grid, 256, 0, s>>>(in, R, C, out);
+  // narrow forms need the narrow side a multiple of 8 (16-byte row pieces)
+  if (C <= 128 && C % 8 == 0) {
+    transpose_narrow_kernel<true><<<dim3(cdiv(R, 256), C / 8, E), 256, 0, s>>>(in, R, C, out);
+  } else if (R <= 128 && R % 8 == 0) {
+    transpose_narrow_kernel<false><<<dim3(cdiv(C, 256), R / 8, E), 256, 0, s>>>(in, R, C, out);
+  } else {
+    dim3 grid(cdiv(C, 32), cdiv(R, 32), E);
+    transpose_kernel<<<grid, 256, 0, s>>>(in, R, C, out);
+  }
   return last_launch_ok();
 }
 
