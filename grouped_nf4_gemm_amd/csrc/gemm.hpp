@@ -107,7 +107,8 @@ __device__ __forceinline__ void st_lds16(uint16_t *p, u32x4 v) { *(u32x4 *)p = v
 // Rows of a row-major bf16 matrix (k contiguous).  Tile row i <-> sorted row
 // row0 + i; with a gather, the source row is gather[row0 + i] / gdiv.  Eight consecutive
 // lanes read the 128 bytes of one row's slab (one cache line per eight lanes); pass v takes
-// tile rows 32 v .. 32 v + 31.  The source rows are resolved once per tile (init).
+// tile rows 32 v .. 32 v + 31.  The source rows are resolved once per tile (init).  Each row
+// is read once per launch: non-temporal loads.
 template <int BR>
 struct RowLoader {
   static constexpr int VECS = BR / 32;  // passes (16-byte vectors per thread)
@@ -126,7 +127,7 @@ struct RowLoader {
     const int kk = k0 + (threadIdx.x & 7) * 8;
 #pragma unroll
     for (int v = 0; v < VECS; ++v)
-      buf[v] = (src[v] >= 0 && kk < kbound) ? *(const u32x4 *)(base + src[v] + kk) : u32x4{0, 0, 0, 0};
+      buf[v] = (src[v] >= 0 && kk < kbound) ? __builtin_nontemporal_load((const u32x4 *)(base + src[v] + kk)) : u32x4{0, 0, 0, 0};
   }
   __device__ __forceinline__ void store(LdsTile<BR> &t) {
     const int r = threadIdx.x >> 3, c = threadIdx.x & 7;
@@ -931,7 +932,8 @@ __device__ __forceinline__ bf16x8 ktile_frag(const KTile<W> &t, int ks, int col0
 }
 // Rows k0 .. k0 + 63 (of krows) of a row-major [rows][ld] bf16 matrix, columns col0 ..
 // col0 + W - 1 (of ncols) into a KTile: W / 8 lanes read one row's 2 W bytes, each pass
-// takes 256 / (W / 8) rows.  Row k is source row row0 + k, or gather[row0 + k] / gdiv.
+// takes 256 / (W / 8) rows.  Row k is source row row0 + k, or gather[row0 + k] / gdiv.  The
+// 128-wide operand of a weight-gradient tile is the large one, read once: non-temporal loads.
 template <int W>
 struct KRowLoader {
   static constexpr int LPR = W / 8, RPP = NTHREADS / LPR, PASSES = BK / RPP;
@@ -946,7 +948,7 @@ struct KRowLoader {
       const bool ok = kk < krows && col < ncols;
       int64_t src = 0;
       if (ok) src = gather ? (int64_t)(gather[row0 + kk] / gdiv) : (int64_t)(row0 + kk);
-      buf[p] = ok ? *(const u32x4 *)(base + src * ld + col) : u32x4{0, 0, 0, 0};
+      buf[p] = ok ? (W == 128 ? __builtin_nontemporal_load((const u32x4 *)(base + src * ld + col)) : *(const u32x4 *)(base + src * ld + col)) : u32x4{0, 0, 0, 0};
     }
   }
   __device__ __forceinline__ void store(KTile<W> &t) {

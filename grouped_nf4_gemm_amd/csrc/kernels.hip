@@ -949,7 +949,7 @@ __global__ void combine1_kernel(const float *__restrict__ O, const int32_t *__re
     if (h >= H) break;
     f32x4 o[KP];
 #pragma unroll
-    for (int j = 0; j < KP; ++j) o[j] = pj[j] >= 0 ? *(const f32x4 *)(O + (int64_t)pj[j] * H + h) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < KP; ++j) o[j] = pj[j] >= 0 ? __builtin_nontemporal_load((const f32x4 *)(O + (int64_t)pj[j] * H + h)) : f32x4{0.f, 0.f, 0.f, 0.f};
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
     for (int j = 0; j < KP; ++j) {
@@ -1151,7 +1151,7 @@ __global__ void combine_bwd_kernel(const uint16_t *__restrict__ dy, const float 
     const u32x2 d = *(const u32x2 *)(dy + (int64_t)t * H + h);
     const float d0 = __uint_as_float(d[0] << 16), d1 = __uint_as_float(d[0] & 0xffff0000u);
     const float d2 = __uint_as_float(d[1] << 16), d3 = __uint_as_float(d[1] & 0xffff0000u);
-    const f32x4 o = *(const f32x4 *)(O + (int64_t)p * H + h);
+    const f32x4 o = __builtin_nontemporal_load((const f32x4 *)(O + (int64_t)p * H + h));
     dot += d0 * o[0] + d1 * o[1] + d2 * o[2] + d3 * o[3];
     u32x2 out{pack_bf16x2(w * d0, w * d1), pack_bf16x2(w * d2, w * d3)};
     *(u32x2 *)(dO + (int64_t)p * H + h) = out;
@@ -1185,7 +1185,7 @@ __global__ void unpermute_kernel(const float *__restrict__ dXp, const int32_t *_
     for (int j = 0; j < k; ++j) {
       const int p = inv[(int64_t)t * k + j];
       if (p < 0) continue;
-      const f32x4 o = *(const f32x4 *)(dXp + (int64_t)p * H + h);
+      const f32x4 o = __builtin_nontemporal_load((const f32x4 *)(dXp + (int64_t)p * H + h));
       a0 += o[0];
       a1 += o[1];
       a2 += o[2];
