@@ -293,7 +293,6 @@ namespace e4b {
 // Wave w (< 8) of the accumulating waves owns rows (w >> 2) * 128 .. +127 and columns
 // (w & 3) * 64 .. +63 of the tile.
 constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
-constexpr int KN_STRIDE = L_BN + 16;  // [k][n] B tile row: 272 bf16 (544 bytes = 32 mod 128)
 constexpr uint32_t OOB = 0x80000000u;  // per-lane offset that reads as zero
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
@@ -381,17 +380,24 @@ struct LTile {  // [256 n][64 k] bf16, k contiguous, chunks swizzled as the A ti
   uint16_t v[L_BN][BK];
 };
 __device__ __forceinline__ int bswz(int row, int chunk) { return swz_chunk(row, chunk) << 3; }
-// [64 k][256 (+16) n] bf16, n contiguous, whose 16-byte chunks c (8 columns) sit at
-// c ^ ((c >> 3) & 3) within the row.  With the row stride of 32 mod 128 bytes this keeps
-// both access patterns free of bank conflicts: the decode stores (8 lanes write chunks
-// 4m + p, m = 0..7, of one row) and the transposing fragment reads (16 lanes read two
-// adjacent chunks in each of 4 consecutive rows).
+// [64 k][256 n] bf16, n contiguous, no padding.  Row k keeps its 16-byte chunk c (8 columns)
+// at c ^ f(k & 3) ^ ((c >> 3) & 3), f = {0, 7, 12, 11}.  Both access patterns then touch
+// distinct banks, whether a pass serves 128 or 256 bytes:
+//  - transposing fragment reads: a pass covers rows 4m .. 4m+3 and an aligned pair (16
+//    lanes) or quad (32 lanes) of chunks; bits 1-2 and bits 2-3 of f differ between the four
+//    rows, so the rows land in different pairs and quads, and the (c >> 3) & 3 term is the
+//    same for the whole pass;
+//  - decode stores: 8 lanes write chunks 4p + part (p = 0..7) of one row, where the
+//    (c >> 3) & 3 term spreads the eight chunks over bits 0-1; the next 8 lanes write the
+//    next row, which bit 0 of f moves to the other chunks of each quad.
+// f is linear in the bits of k, so rows 4 apart share it (fixed offsets between k-steps).
 struct LTileKN {
-  uint16_t v[BK][KN_STRIDE];
+  uint16_t v[BK][L_BN];
 };
-__device__ __forceinline__ int knswz(int col) {
+__device__ __forceinline__ int knswz(int k, int col) {
   const int c = col >> 3;
-  return ((c ^ ((c >> 3) & 3)) << 3) | (col & 7);
+  const int f = ((k & 1) ? 7 : 0) ^ ((k & 2) ? 12 : 0);
+  return ((c ^ f ^ ((c >> 3) & 3)) << 3) | (col & 7);
 }
 // [64 k][256 n] bf16 without padding, for B tiles that direct-to-LDS loads fill from a
 // bf16 copy of a stack stored [K rows][N]: row k keeps its 16-byte chunk c at c ^ ((k & 3)
@@ -621,7 +627,7 @@ struct LQuantKN {
   __device__ __forceinline__ void prepare(const DecodeTables &tb) { dec.prepare(sraw, s2, tb); }
   __device__ __forceinline__ void store(LTileKN &t, int part, int vt) const {
     const int kb = vt >> 3, nb = vt & 7;
-    st_lds16(&t.v[kb][knswz(nb * 32 + part * 8)], dec(w[part]));
+    st_lds16(&t.v[kb][knswz(kb, nb * 32 + part * 8)], dec(w[part]));
   }
 };
 
@@ -756,7 +762,7 @@ struct LQuantKN8 {
     const int kb = vt >> 3, nb = vt & 7;
     const u32x2 a = byte_word_to_bf16<FMT>(w[part >> 1][2 * (part & 1)], sc);
     const u32x2 b = byte_word_to_bf16<FMT>(w[part >> 1][2 * (part & 1) + 1], sc);
-    st_lds16(&t.v[kb][knswz(nb * 32 + part * 8)], u32x4{a[0], a[1], b[0], b[1]});
+    st_lds16(&t.v[kb][knswz(kb, nb * 32 + part * 8)], u32x4{a[0], a[1], b[0], b[1]});
   }
 };
 
@@ -819,9 +825,8 @@ struct LMma {
     const int row = ks * 16 + (G >> 1) * 8 + (i >> 2);
     const int col = wn() * 64 + j * 32 + (G & 1) * 16 + (i & 3) * 4;
     typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
-    const int pc = knswz(col);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row][pc]));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row + 4][pc]));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row][knswz(row, col)]));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(&B.v[row + 4][knswz(row + 4, col)]));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
     return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
   }
