@@ -197,10 +197,20 @@ int lora_a_splits(int M, int E, int N, int K) {
   if (M == 0) return 1;
   return splits_for((int64_t)cdiv(N, 64) * (cdiv(M, 128) + E), K / BK);
 }
+// Upper bound on the splits of one expert's weight-gradient reduction; each expert takes
+// as many as its own rows fill (wgrad_expert_splits).  With many experts the routed rows are
+// skewed (a few experts hold many times the mean), and one split count for all experts
+// would leave the largest as one long chain: then up to SPLIT_MAX, within a partial-sum
+// buffer of at most 256 MB.
 int wgrad_splits(int M, int E, int Na, int Nb) {
   if (M == 0 || E == 0) return 1;
   const int64_t tiles = Nb <= 64 ? (int64_t)cdiv(Nb, 64) * cdiv(Na, 128) : (int64_t)cdiv(Nb, 128) * cdiv(Na, 64);
-  return splits_for(tiles * E, (int64_t)M / E / BK);
+  int sp = splits_for(tiles * E, (int64_t)M / E / BK);
+  if (E >= 32) {
+    const int64_t per = (int64_t)E * Na * Nb * 4;
+    sp = std::max(sp, (int)std::min<int64_t>(SPLIT_MAX, std::max<int64_t>(1, ((int64_t)256 << 20) / per)));
+  }
+  return sp;
 }
 
 // Waits of the large-tile pipelines.  Direct-to-LDS loads count in vmcnt and are not
@@ -868,6 +878,12 @@ bool launch_lora_a(const GroupedArgs &a, hipStream_t s) {
 }
 
 // =============================================================== LoRA weight gradients
+// Splits of one expert's reduction over its `rows` routed rows: one per four 64-row slabs,
+// at least one, at most nsplit.
+__device__ __forceinline__ int wgrad_expert_splits(int rows, int nsplit) {
+  return max(1, min(nsplit, (rows + BK - 1) / BK / 4));
+}
+
 // C[e][a][b] = sum over the routed rows m of expert e of P[m][a] * Q[m][b].
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
@@ -878,12 +894,15 @@ __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
   const int e = blockIdx.z / g.nsplit, sp = blockIdx.z % g.nsplit;
   const int a0 = blockIdx.y * BM, b0 = blockIdx.x * BN;
   const int row0 = g.off[e], krows = g.off[e + 1] - g.off[e];
+  // this expert's own split count: the splits past it have no rows and write nothing
+  const int nsplit_e = g.nsplit > 1 ? wgrad_expert_splits(krows, g.nsplit) : 1;
+  if (sp >= nsplit_e) return;
   Mma<BM, BN, WM, WN> mma;
   mma.zero();
   KRowLoader<BM> la;
   KRowLoader<BN> lb;
   // this split's slabs of the expert's rows
-  const int nall = (krows + BK - 1) / BK, chunk = (nall + g.nsplit - 1) / g.nsplit;
+  const int nall = (krows + BK - 1) / BK, chunk = (nall + nsplit_e - 1) / nsplit_e;
   const int s0 = min(nall, sp * chunk), s1 = min(nall, s0 + chunk);
   auto fetch = [&](int s) {
     la.fetch(g.P, g.ldp, a0, g.Na, row0, krows, g.p_gather, g.p_gdiv, s * BK);
@@ -898,12 +917,26 @@ __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
     if (s + 1 < s1) fetch(s + 1);
     mma_ktiles(mma, As, Bs, 4);
   }
-  // every split writes its (possibly zero) partial sums
+  // every split of the expert writes its (possibly zero) partial sums
   float *C = g.nsplit > 1 ? g.part + ((int64_t)sp * g.E + e) * g.Na * g.Nb : g.C + (int64_t)e * g.Na * g.Nb;
   mma.for_each([&](int row, int col, float v) {
     const int a = a0 + row, b = b0 + col;
     if (a < g.Na && b < g.Nb) C[(int64_t)a * g.Nb + b] = v;
   });
+}
+
+// C[e] = the sum of expert e's own splits of the partial sums [nsplit][E][Na * Nb], in split
+// order.
+__global__ void wgrad_reduce_kernel(const float *__restrict__ part, const int32_t *__restrict__ off, int nsplit,
+                                    int64_t per_expert, int E, float *__restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)E * per_expert;
+  if (i >= n) return;
+  const int e = (int)(i / per_expert);
+  const int ns = wgrad_expert_splits(off[e + 1] - off[e], nsplit);
+  float acc = part[i];
+  for (int s2 = 1; s2 < ns; ++s2) acc += part[s2 * n + i];
+  C[i] = acc;
 }
 
 bool launch_wgrad(const WgradArgs &a, hipStream_t s) {
@@ -922,7 +955,9 @@ bool launch_wgrad(const WgradArgs &a, hipStream_t s) {
   if (!last_launch_ok()) return false;
   if (b.nsplit > 1) {
     const int64_t n = (int64_t)b.E * b.Na * b.Nb;
-    return launch_reduce_splits(b.part, b.nsplit, n, n, b.Nb, b.Nb, 1.0f, false, b.C, s);
+    wgrad_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(b.part, b.off, b.nsplit, (int64_t)b.Na * b.Nb,
+                                                                    b.E, b.C);
+    return last_launch_ok();
   }
   return true;
 }
