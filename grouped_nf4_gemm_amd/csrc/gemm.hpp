@@ -381,22 +381,21 @@ struct LTile {  // [256 n][64 k] bf16, k contiguous, chunks swizzled as the A ti
 };
 __device__ __forceinline__ int bswz(int row, int chunk) { return swz_chunk(row, chunk) << 3; }
 // [64 k][256 n] bf16, n contiguous, no padding.  Row k keeps its 16-byte chunk c (8 columns)
-// at c ^ f(k & 3) ^ ((c >> 3) & 3), f = {0, 7, 12, 11}.  Both access patterns then touch
-// distinct banks, whether a pass serves 128 or 256 bytes:
+// at c ^ f(k & 3) ^ ((c >> 3) & 3), f = {0, 5, 10, 15}.  All three access patterns then touch
+// distinct banks, whether a pass serves 128 or 256 bytes (checked by enumeration):
 //  - transposing fragment reads: a pass covers rows 4m .. 4m+3 and an aligned pair (16
 //    lanes) or quad (32 lanes) of chunks; bits 1-2 and bits 2-3 of f differ between the four
-//    rows, so the rows land in different pairs and quads, and the (c >> 3) & 3 term is the
-//    same for the whole pass;
-//  - decode stores: 8 lanes write chunks 4p + part (p = 0..7) of one row, where the
-//    (c >> 3) & 3 term spreads the eight chunks over bits 0-1; the next 8 lanes write the
-//    next row, which bit 0 of f moves to the other chunks of each quad.
+//    rows, and the (c >> 3) & 3 term is the same for the whole pass;
+//  - 4-bit decode stores (LQuantKN): lane l of a wave writes chunk 8 (l & 3) + part of row
+//    l >> 2, so a pass covers 2 or 4 rows x the four 64-column blocks;
+//  - 8-bit decode stores (LQuantKN8): 8 lanes write chunks 4p + part (p = 0..7) of one row.
 // f is linear in the bits of k, so rows 4 apart share it (fixed offsets between k-steps).
 struct LTileKN {
   uint16_t v[BK][L_BN];
 };
 __device__ __forceinline__ int knswz(int k, int col) {
   const int c = col >> 3;
-  const int f = ((k & 1) ? 7 : 0) ^ ((k & 2) ? 12 : 0);
+  const int f = ((k & 1) ? 5 : 0) ^ ((k & 2) ? 10 : 0);
   return ((c ^ f ^ ((c >> 3) & 3)) << 3) | (col & 7);
 }
 // [64 k][256 n] bf16 without padding, for B tiles that direct-to-LDS loads fill from a
@@ -589,23 +588,25 @@ __device__ __forceinline__ void fetch_scale(__amdgpu_buffer_rsrc_t rs, __amdgpu_
 }
 
 // B from a 4-bit stack reduced over its STORED row axis: LDS tile [64 k][256 n], k =
-// stored rows k0..k0+63, n = stored columns n0..n0+255.  Thread -> stored row tid / 8 and
-// 32 stored columns (tid % 8): one 16-byte code load and one block scale (32 aligned
-// columns lie in one NF4 block of 64 and in exactly one MXFP4 block of 32), decoded and
-// written as four 16-byte row pieces; the MFMA fragments are read with the transposing
-// LDS load.
+// stored rows k0..k0+63, n = stored columns n0..n0+255.  Thread p -> stored row p / 4 and the
+// 64 stored columns n0 + 64 (p % 4) ..: two 16-byte code loads (32 contiguous bytes), one
+// block scale for the NF4 formats (the 64 columns are one block) or two for MXFP4 (blocks
+// of 32), decoded and written as eight 16-byte row pieces; the MFMA fragments are read with
+// the transposing LDS load.  VTS: tile pieces per producer thread.
 template <int FMT>
 struct LQuantKN {
-  static constexpr int LOADS = FMT == FMT_NF4_DQ ? 3 : 2;  // one code load, the scale (+ second level)
-  u32x4 w;
+  static constexpr int VTS = 1, PARTS = 8;
+  static constexpr int LOADS = FMT == FMT_NF4_DQ ? 4 : 3;  // two code loads, the scale (+ second level)
+  u32x4 w0, w1;
   uint32_t sraw;
   float s2;
   GroupDecoder<FMT> dec;
+  float sa, sb;                       // MXFP4: the scales of the two blocks of 32
   uint32_t cvoff, svoff, crow, srow;  // offsets at k0 = 0 of this thread's stored row; per-row steps
   int64_t blk0, blkrow;
   __device__ __forceinline__ void init(const QStack &q, int e, int n0, int Nout, int vt) {
-    const int kb = vt >> 3, nb = vt & 7;
-    const int n = n0 + nb * 32;
+    const int kb = vt >> 2, nb = vt & 3;
+    const int n = n0 + nb * 64;
     crow = (uint32_t)(q.K / 2);
     blkrow = q.K / 64;
     srow = FMT == FMT_NF4 ? (uint32_t)(blkrow * 4) : FMT == FMT_NF4_DQ ? (uint32_t)blkrow : (uint32_t)(q.K / 32);
@@ -621,13 +622,30 @@ struct LQuantKN {
   }
   __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
                                         __amdgpu_buffer_rsrc_t rs2, int k0, uint32_t dead) {
-    w = bload128(rc, cvoff, ((uint32_t)k0 * crow) | dead);
-    fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)k0 * srow, blk0 + (int64_t)k0 * blkrow, dead, sraw, s2);
+    w0 = bload128(rc, cvoff, ((uint32_t)k0 * crow) | dead);
+    w1 = bload128(rc, cvoff + 16, ((uint32_t)k0 * crow) | dead);
+    if constexpr (FMT == FMT_MXFP4) {  // the two E8M0 bytes of the 64 columns (2-byte aligned)
+      sraw = bload16(rs, svoff, ((uint32_t)k0 * srow) | dead);
+    } else {
+      fetch_scale<FMT>(rs, rs2, svoff, (uint32_t)k0 * srow, blk0 + (int64_t)k0 * blkrow, dead, sraw, s2);
+    }
   }
-  __device__ __forceinline__ void prepare(const DecodeTables &tb) { dec.prepare(sraw, s2, tb); }
+  template <class TB>
+  __device__ __forceinline__ void prepare(const TB &tb) {
+    if constexpr (FMT == FMT_MXFP4) {
+      sa = e8m0_to_f32(sraw & 0xffu);
+      sb = e8m0_to_f32((sraw >> 8) & 0xffu);
+    } else {
+      dec.prepare(sraw, s2, tb);
+    }
+  }
   __device__ __forceinline__ void store(LTileKN &t, int part, int vt) const {
-    const int kb = vt >> 3, nb = vt & 7;
-    st_lds16(&t.v[kb][knswz(kb, nb * 32 + part * 8)], dec(w[part]));
+    const int kb = vt >> 2, nb = vt & 3;
+    const uint32_t w = part < 4 ? w0[part] : w1[part - 4];
+    u32x4 v;
+    if constexpr (FMT == FMT_MXFP4) v = mxfp4_word_to_bf16(w, part < 4 ? sa : sb);
+    else v = dec(w);
+    st_lds16(&t.v[kb][knswz(kb, nb * 64 + part * 8)], v);
   }
 };
 
@@ -733,6 +751,7 @@ struct LQuantRow8 {
 // the scale of the 64-column block they lie in, written as four 16-byte row pieces.
 template <int FMT>
 struct LQuantKN8 {
+  static constexpr int VTS = 2, PARTS = 4;
   static constexpr int LOADS = 3;
   u32x4 w[2];
   uint32_t sraw;

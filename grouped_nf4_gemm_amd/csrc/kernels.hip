@@ -599,8 +599,8 @@ struct WSProducer {
   static constexpr bool KN = BKIND == B_QKN;
   using RowL = typename std::conditional<fmt_8bit(FMT), LQuantRow8<FMT>, LQuantRow<FMT>>::type;
   using KnL = typename std::conditional<fmt_8bit(FMT), LQuantKN8<FMT>, LQuantKN<FMT>>::type;
-  // vector-memory loads of one B slab per producer thread (two K-major loaders, or one row)
-  static constexpr int LOADS = KN ? 2 * KnL::LOADS : RowL::LOADS;
+  // vector-memory loads of one B slab per producer thread (KnL::VTS K-major loaders, or one row)
+  static constexpr int LOADS = KN ? KnL::VTS * KnL::LOADS : RowL::LOADS;
   using BTile = typename std::conditional<KN, LTileKN, LTile>::type;
   DecodeTables &tb;
   ATile &A0, &A1;
@@ -608,8 +608,8 @@ struct WSProducer {
   __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
   LDirectAN<4> la;
   int v, p;  // producer wave (0..3) and thread (0..255)
-  RowL nk[3];   // NK ring: slab t in nk[t % 3]
-  KnL kn[3][2];  // KN ring: two K-major loaders (virtual threads p, p + 256)
+  RowL nk[3];          // NK ring: slab t in nk[t % 3]
+  KnL kn[3][KnL::VTS];  // KN ring: K-major loaders of virtual threads p, p + 256
 
   __device__ __forceinline__ WSProducer(DecodeTables &tb_, ATile &a0, ATile &a1, BBuf &b0, BBuf &b1,
                                         const GroupedArgs &g)
@@ -636,8 +636,8 @@ struct WSProducer {
   template <int Q>
   __device__ __forceinline__ void fetch_b(int slab, int nmain) {
     if constexpr (KN) {
-      kn[Q][0].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
-      kn[Q][1].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
+#pragma unroll
+      for (int h = 0; h < KnL::VTS; ++h) kn[Q][h].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
     } else {
       nk[Q].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
     }
@@ -646,10 +646,10 @@ struct WSProducer {
   __device__ __forceinline__ void decode() {
     if constexpr (KN) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < KnL::VTS; ++h) {
         kn[Q][h].prepare(tb);
 #pragma unroll
-        for (int part = 0; part < 4; ++part) kn[Q][h].store(btile<P>(), part, p + 256 * h);
+        for (int part = 0; part < KnL::PARTS; ++part) kn[Q][h].store(btile<P>(), part, p + 256 * h);
       }
     } else {
       nk[Q].decode_store(btile<P>(), tb, p);
@@ -712,10 +712,11 @@ struct WSProducer {
                      make_rsrc(g.xb + (int64_t)e * g.xb_estride, (uint32_t)((int64_t)Nrows * g.ldxb * 2))};
     la.init(v, tm.rows, tm.row0, g.a_gather, g.a_gdiv, g.lda);
     if constexpr (KN) {
-      kn[0][0].init(g.q, e, n0, g.N, p);
-      kn[0][1].init(g.q, e, n0, g.N, p + 256);
-      kn[1][0] = kn[2][0] = kn[0][0];
-      kn[1][1] = kn[2][1] = kn[0][1];
+#pragma unroll
+      for (int h = 0; h < KnL::VTS; ++h) {
+        kn[0][h].init(g.q, e, n0, g.N, p + 256 * h);
+        kn[1][h] = kn[2][h] = kn[0][h];
+      }
     } else {
       nk[0].init(g.q, e, map, Nrows, p);
       nk[1] = nk[2] = nk[0];
