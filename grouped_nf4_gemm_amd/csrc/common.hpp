@@ -125,13 +125,17 @@ __device__ __forceinline__ u32x4 nf4_word_to_bf16(uint32_t w, float absmax, cons
 }
 
 // Register-resident decode table of one NF4 block: the sixteen values e[q] = bf16(v[q] *
-// absmax) (the same rounding as nf4_scale_pack) split into byte planes, pl[i] = low bytes of
-// e[4i .. 4i+3] and pl[4 + i] = their high bytes (i < 4), so that byte permutes can look up
-// four codes at a time without touching LDS.  v: the code values of the stack.
+// absmax) (the same rounding as nf4_scale_pack) split into byte planes, so that byte permutes
+// can look up four codes at a time without touching LDS.  Codes q < 8 form table A, q >= 8
+// table B; code q sits at position (q + 5) & 7 of its table (the position the decode below
+// reads).  pl[0..1]: low bytes of table A (positions 0-3, 4-7), pl[2..3]: low bytes of
+// table B, pl[4..7]: the high bytes likewise.  v: the code values of the stack.
 __device__ __forceinline__ void nf4_planes(float absmax, const float *v, uint32_t (&pl)[8]) {
-  uint32_t e[8];
+  // the code at table position t: (t + 3) & 7 in table A, 8 + ((t + 3) & 7) in table B
+  auto code_at = [](int t) { return (t & 8) | ((t + 3) & 7); };
+  uint32_t e[8];  // e[k]: positions 2k, 2k + 1 (of A for k < 4, of B for k >= 4)
 #pragma unroll
-  for (int k = 0; k < 8; ++k) e[k] = pack_bf16x2(v[2 * k] * absmax, v[2 * k + 1] * absmax);
+  for (int k = 0; k < 8; ++k) e[k] = pack_bf16x2(v[code_at(2 * k)] * absmax, v[code_at(2 * k + 1)] * absmax);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     pl[i] = __builtin_amdgcn_perm(e[2 * i + 1], e[2 * i], 0x06040200u);
@@ -139,19 +143,20 @@ __device__ __forceinline__ void nf4_planes(float absmax, const float *v, uint32_
   }
 }
 // The 8 codes of one 32-bit word (element 2j in the high nibble of byte j) to 8 bf16 values
-// through the planes of nf4_planes.  v_perm_b32 picks byte s (0..7) of the pair {S0:S1}, so a
-// code q reads entry q & 7 of planes 0-1 or of planes 2-3, chosen per byte by q >= 8.  For the
-// choice, q + 0x78 has bit 7 set exactly when q >= 8, and the selectors 8..11 of v_perm_b32
-// replicate bit 7 of bytes 1, 3, 5, 7 of the pair into a whole byte.
+// through the planes of nf4_planes.  v_perm_b32 picks byte s (0..7) of the pair {S0:S1}; for
+// selector values 8-11 it replicates a sign bit, for 12 it gives 0x00 and for 13 and up 0xFF.
+// With x = q + 5 per byte: x & 7 is the code's table position, and perm(0, 0, x) is 0xFF
+// exactly where q >= 8 (x = 13..20; x = 5..12 gives 0x00 from zero bytes, zero sign bits and
+// the constant 12), the mask that picks table B.
 __device__ __forceinline__ u32x4 nf4_decode_planes(uint32_t w, const uint32_t (&pl)[8]) {
   const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // codes 2j+1, codes 2j
   u32x4 out;
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const uint32_t q = __builtin_amdgcn_perm(lo, hi, p == 0 ? 0x05010400u : 0x07030602u);  // codes 4p..4p+3
-    const uint32_t x = q + 0x78787878u;
-    const uint32_t m = __builtin_amdgcn_perm(x, x << 8, 0x0B090A08u);  // 0xFF in bytes with q >= 8
-    const uint32_t s = q & 0x07070707u;
+    const uint32_t x = q + 0x05050505u;
+    const uint32_t m = __builtin_amdgcn_perm(0u, 0u, x);  // 0xFF in bytes with q >= 8
+    const uint32_t s = x & 0x07070707u;
     const uint32_t L = (__builtin_amdgcn_perm(pl[3], pl[2], s) & m) | (__builtin_amdgcn_perm(pl[1], pl[0], s) & ~m);
     const uint32_t H = (__builtin_amdgcn_perm(pl[7], pl[6], s) & m) | (__builtin_amdgcn_perm(pl[5], pl[4], s) & ~m);
     out[2 * p] = __builtin_amdgcn_perm(H, L, 0x05010400u);
