@@ -65,7 +65,7 @@ bool last_launch_ok() { return hipGetLastError() == hipSuccess; }
 // ------------------------------------------------------------------ workspace layout
 struct Layout {
   size_t cnt, off, perm, inv, z1, z2, G, h, O, dO, u2, dG, u1, dXp, A1T, B1T, A2T, B2T, part, W1x, W2x,
-      zp, ctr, total;
+      zp, ctr, tail, tail_ctr, total;
 };
 static constexpr size_t NONE = ~(size_t)0;
 // Activations and stacks that the 4-bit GEMMs stream with buffer loads must each stay
@@ -141,6 +141,10 @@ static Layout layout(const e4b_moe_desc &d, int r1, int r2) {
     if (r2) { wgrad((int)H, r2); wgrad(r2, (int)I); }
   }
   L.part = part ? take(part) : NONE;
+  // training: the K-split of the last round of the large fp32-epilogue GEMMs (down, gate_up
+  // dgrad): partial tiles and arrival counters (zeroed by the forward's routing launch)
+  L.tail = train ? take(TAIL_BYTES) : NONE;
+  L.tail_ctr = train ? take((size_t)TAIL_CTRS * 4) : NONE;
   if (use_expand(d)) {
     L.W1x = take(E * 2 * I * H * 2);
     L.W2x = take(E * H * I * 2);
@@ -355,7 +359,9 @@ static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, con
   if (M <= SMALL_M_MAX && !fmt_8bit(w_gu->fmt) && !(d.flags & (E4B_TRAIN | E4B_SEPARATE)) && E <= FUSE_E_MAX &&
       r1 <= FUSE_R_MAX && r2 <= FUSE_R_MAX)
     return M == 0 ? E4B_OK : moe_fwd_two_launch(d, w_gu, w_dn, l_gu, l_dn, x, ids, topw, y, ws, L, r1, r2, s);
-  E4B_LAUNCH(launch_route(ids, M, E, cnt, off, perm, inv, s));
+  float *tail = L.tail == NONE ? nullptr : at<float>(ws, L.tail);
+  int32_t *tail_ctr = L.tail_ctr == NONE ? nullptr : at<int32_t>(ws, L.tail_ctr);
+  E4B_LAUNCH(launch_route(ids, M, E, cnt, off, perm, inv, s, tail_ctr, TAIL_CTRS));
   if (M == 0) return E4B_OK;
   if (W1x) {
     E4B_LAUNCH(launch_expand(qstack(w_gu), E, W1x, s));
@@ -421,6 +427,7 @@ static e4b_status moe_fwd(const e4b_moe_desc *desc, const e4b_qweight *w_gu, con
       nsplit = train ? 1 : small_down_splits(M, E, H, I);
       E4B_LAUNCH(launch_small_down(a, nsplit, s));
     } else {
+      a.tail = tail; a.tail_ctr = tail_ctr;
       E4B_LAUNCH(launch_gemm_down(a, s));
     }
   }
@@ -548,6 +555,8 @@ e4b_status e4b_moe_dgrad(const e4b_moe_desc *desc, const e4b_qweight *w_gu, cons
     a.xa = u1; a.ldxa = r1; a.xb = r1 ? A1T : nullptr; a.xb_estride = (int64_t)H * r1;
     a.ldxb = r1; a.r = r1;
     a.C = dXp; a.ldc = H; a.alpha = 1.0f; a.I = I;
+    a.tail = L.tail == NONE ? nullptr : at<float>(ws, L.tail);
+    a.tail_ctr = L.tail_ctr == NONE ? nullptr : at<int32_t>(ws, L.tail_ctr);
     E4B_LAUNCH(launch_gemm_gate_up_dgrad(a, s));
   }
   E4B_LAUNCH(launch_unpermute(dXp, inv, d.T, d.topk, H, dx, s));

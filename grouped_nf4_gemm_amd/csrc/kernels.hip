@@ -27,8 +27,10 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(const int32_t *__r
                                                               int E, int32_t *__restrict__ cnt,
                                                               int32_t *__restrict__ off,
                                                               int32_t *__restrict__ perm,
-                                                              int32_t *__restrict__ inv) {
+                                                              int32_t *__restrict__ inv,
+                                                              int32_t *__restrict__ zero, int nzero) {
   extern __shared__ int32_t sm[];
+  for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero[i] = 0;
   const int KE = E + 1;  // keys 0..E-1 valid, E = dropped
   int32_t *wc = sm;                   // [RT_WAVES][KE]
   int32_t *soff = sm + RT_WAVES * KE;  // [KE]
@@ -100,10 +102,10 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(const int32_t *__r
 }
 
 bool launch_route(const int32_t *ids, int M, int E, int32_t *cnt, int32_t *off, int32_t *perm,
-                  int32_t *inv, hipStream_t s) {
+                  int32_t *inv, hipStream_t s, int32_t *zero, int nzero) {
   LaunchScope ls(FAM_ROUTE, s);
   const size_t shm = (size_t)(RT_WAVES + 1) * (E + 1) * sizeof(int32_t);
-  route_kernel<<<1, RT_WAVES * 64, shm, s>>>(ids, M, E, cnt, off, perm, inv);
+  route_kernel<<<1, RT_WAVES * 64, shm, s>>>(ids, M, E, cnt, off, perm, inv, zero, zero ? nzero : 0);
   return last_launch_ok();
 }
 
@@ -608,6 +610,7 @@ struct WSProducer {
   __amdgpu_buffer_rsrc_t ra, rc, rs, rs2;
   LDirectAN<4> la;
   int v, p;  // producer wave (0..3) and thread (0..255)
+  int sb = 0;  // first 64-wide slab of K this tile reduces over (its part of a K-split tile)
   RowL nk[3];          // NK ring: slab t in nk[t % 3]
   KnL kn[3][KnL::VTS];  // KN ring: K-major loaders of virtual threads p, p + 256
 
@@ -637,9 +640,9 @@ struct WSProducer {
   __device__ __forceinline__ void fetch_b(int slab, int nmain) {
     if constexpr (KN) {
 #pragma unroll
-      for (int h = 0; h < KnL::VTS; ++h) kn[Q][h].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
+      for (int h = 0; h < KnL::VTS; ++h) kn[Q][h].fetch(rc, rs, rs2, (slab + sb) * BK, dead(slab, nmain));
     } else {
-      nk[Q].fetch(rc, rs, rs2, slab * BK, dead(slab, nmain));
+      nk[Q].fetch(rc, rs, rs2, (slab + sb) * BK, dead(slab, nmain));
     }
   }
   template <int Q, int P>
@@ -656,7 +659,7 @@ struct WSProducer {
     }
   }
   __device__ __forceinline__ void issue_a(ATile &t, int slab, int nmain) {
-    la.issue(ra, t, (uint32_t)(slab * BK * 2) | dead(slab, nmain), v);
+    la.issue(ra, t, (uint32_t)((slab + sb) * BK * 2) | dead(slab, nmain), v);
   }
   // The LoRA K-extension as nl = ceil(r / 64) more slabs nmain, nmain + 1: tile rows of
   // the adapter input (xa, sorted rows) and of the adapter's B rows (xb, mapped like the
@@ -706,7 +709,8 @@ struct WSProducer {
     slab_barrier<LOADS>();  // A rows of slab s+1 landed; only the B codes of slab s+3 in flight
   }
   __device__ __forceinline__ void run(const GroupedArgs &g, int e, int n0, const RowMap &map, int Nrows,
-                                      const TileM &tm, int nmain, int nl) {
+                                      const TileM &tm, int kb0, int nmain, int nl) {
+    sb = kb0;
     const LoraCtx ls{nl, g.r, tm.rows, Nrows, tm.row0, g.ldxa, g.ldxb, map,
                      make_rsrc(g.xa, (uint32_t)((int64_t)g.M * g.ldxa * 2)),
                      make_rsrc(g.xb + (int64_t)e * g.xb_estride, (uint32_t)((int64_t)Nrows * g.ldxb * 2))};
@@ -750,6 +754,120 @@ struct WSProducer {
   }
 };
 
+// ---------------------------------------------------------------- K-split of the last round
+// With one workgroup per compute unit, a launch of nt tiles runs in ceil(nt / 256) rounds and
+// its last round keeps only nt % 256 compute units busy.  The fp32-epilogue GEMMs (down,
+// gate_up dgrad) split each tile of that round along K into q parts (q of them fit one round,
+// each part keeps at least TAIL_MIN_SLABS slabs): part 0 runs in the tile's own workgroup,
+// parts 1 .. q-1 in the extra grid rows, which are dispatched last.  Tiles are numbered as
+// the grid deals them, t = row tile * gridDim.x + column tile.
+struct TailPart {
+  int ti = -1;  // index of the split tile among the split tiles, or -1: a whole tile
+  int part = 0, q = 1;
+};
+// Row tiles of BMt rows over all expert segments (the same in every wave).
+__device__ __forceinline__ int count_row_tiles(const int32_t *__restrict__ off, int E, int BMt) {
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+  for (int c = 0; c < E; c += 64) {
+    const int ee = c + lane;
+    int nt = ee < E ? (off[ee + 1] - off[ee] + BMt - 1) / BMt : 0;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) nt += __shfl_xor(nt, d);
+    tot += nt;
+  }
+  return __builtin_amdgcn_readfirstlane(tot);
+}
+// This workgroup's (row tile, column tile) and part; false: nothing to do.
+__device__ __forceinline__ bool tail_split(const GroupedArgs &g, int nall, int &slot, int &col, TailPart &tp) {
+  const int ncol = (int)gridDim.x, nt = count_row_tiles(g.off, g.E, L_BM) * ncol;
+  const int r = nt % TAIL_UNITS;  // tiles of the last, partial round
+  const int q = r ? min(min(TAIL_Q, TAIL_UNITS / r), nall / TAIL_MIN_SLABS) : 1;
+  const int first = nt - r;
+  if (slot >= g.tail_slot0) {  // parts 1 .. q-1 of the split tiles
+    const int x = (slot - g.tail_slot0) * ncol + col;
+    if (q < 2 || x >= r * (q - 1)) return false;
+    tp.ti = x / (q - 1);
+    tp.part = 1 + x % (q - 1);
+    tp.q = q;
+    const int t = first + tp.ti;
+    slot = t / ncol;
+    col = t % ncol;
+    return true;
+  }
+  const int t = slot * ncol + col;
+  if (q > 1 && t >= first && t < nt) {
+    tp.ti = t - first;
+    tp.part = 0;
+    tp.q = q;
+  }
+  return true;
+}
+// Accumulators 4c .. 4c+3 of this lane (c a constant in unrolled loops).
+__device__ __forceinline__ f32x4 acc_piece(const LMma &m, int c) {
+  const f32x16 &a = m.acc[c >> 3][(c >> 2) & 1];
+  const int o = (c & 3) * 4;
+  return f32x4{a[o], a[o + 1], a[o + 2], a[o + 3]};
+}
+// The q parts' partial tiles of this lane added in part order (base(p): the lane's pieces of
+// part p) and stored as the fp32 epilogue stores them: out = alpha * sum + bias[column].
+// Piece c holds accumulators (i, j, 4 (c & 3) .. +3) = rows rl + 32 i + 8 (c & 3) .. +3 of
+// column n0 + col_of(j).  Branch-free over q: all TAIL_Q loads of a piece are issued (parts
+// past q read part q - 1 again) and the sum takes part p only when p < q; one piece's loads
+// are in flight at a time.
+template <class Base>
+__device__ __forceinline__ void tail_sum_store(const GroupedArgs &g, const TileM &tm, int n0, const Base &base,
+                                               int q) {
+  const int lane = threadIdx.x & 63;
+  const int rl = LMma::wm() * 128 + (lane >> 5) * 4;
+  float *C = (float *)g.C;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    f32x4 v[TAIL_Q];
+#pragma unroll
+    for (int p = 0; p < TAIL_Q; ++p) v[p] = *(const f32x4 *)(base(min(p, q - 1)) + c * 64 * 4);
+    f32x4 sum = v[0];
+#pragma unroll
+    for (int p = 1; p < TAIL_Q; ++p) {
+      const f32x4 t = sum + v[p];
+      sum = p < q ? t : sum;
+    }
+    const int i = c >> 3, j = (c >> 2) & 1, r0 = rl + i * 32 + (c & 3) * 8;
+    const int n = n0 + LMma::col_of(j);
+    if (n < g.N) {
+      const float bn = g.bias ? bf2f(g.bias[(int64_t)tm.e * g.bias_estride + n]) : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (r0 + u < tm.rows) C[(int64_t)(tm.row0 + r0 + u) * g.ldc + n] = g.alpha * sum[u] + bn;
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+// The end of one part of a split tile, per consumer wave (no workgroup barrier: the producer
+// waves have ended).  The wave stores its fp32 accumulators as the part's partial tile and
+// counts its arrival on its (tile, wave) counter; the wave that arrives last adds the q
+// partial tiles in part order, which fixes the result bit for bit whatever the arrival
+// order, stores it through the tile epilogue and resets the counter for the next launch.
+// Partial layout per (tile, part, wave): 32 pieces of 4 accumulators x 64 lanes.
+__device__ __forceinline__ void tail_finish(LMma &mma, const GroupedArgs &g, const TileM &tm, int n0,
+                                            const TailPart &tp) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  auto base = [&](int p) { return g.tail + (((int64_t)(tp.ti * tp.q + p) * 8 + w) * 32 * 64 + lane) * 4; };
+  {
+    float *mine = base(tp.part);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) *(f32x4 *)(mine + c * 64 * 4) = acc_piece(mma, c);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the partial tile before the arrival
+  int old = 0;
+  if (lane == 0) old = atomicAdd(&g.tail_ctr[tp.ti * 8 + w], 1);
+  old = __shfl(old, 0);
+  if (old != tp.q - 1) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other parts' partial tiles
+  tail_sum_store(g, tm, n0, base, tp.q);  // the wave's own part is read back like the others
+  if (lane == 0) g.tail_ctr[tp.ti * 8 + w] = 0;
+}
+
 template <int BKIND, int EPI, bool SWIGLU, int FMT>
 __global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
   __shared__ DecodeTables tb;
@@ -759,21 +877,28 @@ __global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
   constexpr bool KN = BKIND == B_QKN;
   init_decode_tables(tb, g.q);
   TileM tm;
-  if (!find_tile(g.off, g.E, L_BM, blockIdx.y, tm, tile_sh)) return;
+  const int nall = g.K / BK;
+  int slot = blockIdx.y, col = blockIdx.x;
+  TailPart tp;
+  if constexpr (EPI == EPI_F32) {
+    if (g.tail && !tail_split(g, nall, slot, col, tp)) return;
+  }
+  if (!find_tile(g.off, g.E, L_BM, slot, tm, tile_sh)) return;
   const int e = tm.e;
-  const int n0 = blockIdx.x * (SWIGLU ? L_BN / 2 : L_BN);
+  const int n0 = col * (SWIGLU ? L_BN / 2 : L_BN);
   const RowMap map{n0, g.I, SWIGLU, SWIGLU && g.act == 1};
   const int Nrows = SWIGLU ? 2 * g.I : g.N;
-  const int nmain = g.K / BK;
-  // the LoRA K-extension: ceil(r / 64) more slabs of the producers' pipeline
-  const int nl = (g.r + BK - 1) / BK;
+  // this tile's slabs of K: all of them, or its part of a split tile
+  const int kb0 = tp.part * nall / tp.q, nmain = (tp.part + 1) * nall / tp.q - kb0;
+  // the LoRA K-extension: ceil(r / 64) more slabs of the producers' pipeline (the last part)
+  const int nl = tp.part == tp.q - 1 ? (g.r + BK - 1) / BK : 0;
   if (threadIdx.x >= WS_CONSUMERS) {
     // The NF4 decode is the heaviest VALU work of a slab: its waves issue first, so the
     // slab is ready sooner (measured 1-1.5% on the input-gradient GEMMs; the light MXFP4
     // decode is better left at the consumers' priority).
     if constexpr (FMT == FMT_NF4 || FMT == FMT_NF4_DQ) __builtin_amdgcn_s_setprio(2);
     WSProducer<BKIND, FMT> pr(tb, A0, A1, B0, B1, g);
-    pr.run(g, e, n0, map, Nrows, tm, nmain, nl);
+    pr.run(g, e, n0, map, Nrows, tm, kb0, nmain, nl);
     return;
   }
   LMma mma;
@@ -811,6 +936,12 @@ __global__ __launch_bounds__(WS_THREADS) void gemm_ws_kernel(GroupedArgs g) {
     mma.step_rows<false>(odd ? A1 : A0, (odd ? B1 : B0).nk, min(4, (g.r - x * BK + 15) / 16), ni);
     if (x + 1 < nl) consumer_barrier();
   }
+  if constexpr (EPI == EPI_F32) {
+    if (tp.ti >= 0) {
+      tail_finish(mma, g, tm, n0, tp);
+      return;
+    }
+  }
   large_epilogue<EPI>(mma, g, tm, n0);
 }
 
@@ -839,11 +970,22 @@ bool launch_gemm_gate_up(const GroupedArgs &a, hipStream_t s) {
   return last_launch_ok();
 }
 
+// Grid of a large fp32-epilogue GEMM: the tile grid, plus rows for the parts of split tiles
+// past the first (tail_split) when the caller gave the partial-tile workspace.
+static dim3 f32_grid(GroupedArgs &b) {
+  const int ncol = cdiv(b.N, L_BN), slots = m_slots(b, L_BM);
+  // the bf16-copy tiles stay whole, and so do tiles too short for two parts
+  if (b.Bx || b.K / BK < 2 * TAIL_MIN_SLABS) b.tail = nullptr;
+  b.tail_slot0 = slots;
+  return dim3(ncol, slots + (b.tail ? cdiv(TAIL_UNITS, ncol) : 0));
+}
+
 bool launch_gemm_down(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_DOWN, s);
-  dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
-  launch_large<B_QNK, EPI_F32, false>(a, grid, s);
+  GroupedArgs b = a;
+  const dim3 grid = f32_grid(b);
+  launch_large<B_QNK, EPI_F32, false>(b, grid, s);
   return last_launch_ok();
 }
 
@@ -858,8 +1000,9 @@ bool launch_gemm_down_dgrad(const GroupedArgs &a, hipStream_t s) {
 bool launch_gemm_gate_up_dgrad(const GroupedArgs &a, hipStream_t s) {
   if (a.M == 0) return true;
   LaunchScope ls(FAM_GATE_UP_DGRAD, s);
-  dim3 grid(cdiv(a.N, L_BN), m_slots(a, L_BM));
-  launch_large<B_QKN, EPI_F32, false>(a, grid, s);
+  GroupedArgs b = a;
+  const dim3 grid = f32_grid(b);
+  launch_large<B_QKN, EPI_F32, false>(b, grid, s);
   return last_launch_ok();
 }
 

@@ -122,14 +122,29 @@ struct GroupedArgs {
   const uint16_t *bias;
   int64_t bias_estride;
   DecodeFuse fz;
+  // large fp32-epilogue tiles (down, gate_up dgrad): with `tail` set, the tiles of the last,
+  // partial round of workgroups are split along K (tail_split); grid rows from tail_slot0 on
+  // run the split parts past the first.  tail: fp32 partial tiles; tail_ctr: one arrival
+  // counter per split tile and consumer wave, zero between launches.
+  float *tail;
+  int32_t *tail_ctr;
+  int tail_slot0;
 };
+
+// K-split of the last round of large fp32-epilogue tiles: at most TAIL_UNITS workgroup units
+// (the compute units of one round), at most TAIL_Q parts per tile and at least TAIL_MIN_SLABS
+// 64-wide slabs per part (shorter parts do not repay their start-up, partial store and
+// fences).  Workspace: TAIL_UNITS partial tiles (256 x 256 fp32) and TAIL_CTRS counters.
+constexpr int TAIL_UNITS = 256, TAIL_Q = 8, TAIL_MIN_SLABS = 64, TAIL_CTRS = TAIL_UNITS * 8;
+constexpr size_t TAIL_BYTES = (size_t)TAIL_UNITS * 256 * 256 * 4;
 
 enum BKind : int { B_QNK = 0, B_QKN = 1, B_DENSE = 2 };
 enum EpiKind : int { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU_FWD = 2, EPI_SWIGLU_BWD = 3 };
 
 // Launchers (return false if the launch failed).
+// zero (nullable): nzero ints set to 0 by the same launch (the tail-split arrival counters)
 bool launch_route(const int32_t *ids, int M, int E, int32_t *cnt, int32_t *off, int32_t *perm,
-                  int32_t *inv, hipStream_t s);
+                  int32_t *inv, hipStream_t s, int32_t *zero = nullptr, int nzero = 0);
 // gate_up forward: h = swiglu(X W1^T + z1 B1^T) (+ G saved)
 bool launch_gemm_gate_up(const GroupedArgs &a, hipStream_t s);
 // down forward: O = h W2^T + z2 B2^T (fp32)

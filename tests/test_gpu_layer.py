@@ -49,6 +49,9 @@ SHAPES = [
     ("int8", 5, 192, 320, 150, 3, 16, 32.0, "int8"),
     ("fp8-few", 4, 256, 192, 20, 2, 8, 16.0, "fp8"),
     ("fp8", 3, 256, 448, 300, 2, 64, 128.0, "fp8"),
+    # one column tile and 3 row tiles, K = 8192 / 16384: the fp32-epilogue GEMMs split every
+    # tile along K (down into 2 parts, gate_up dgrad into 4), summed by the last part
+    ("k-split", 3, 256, 8192, 300, 2, 16, 32.0, "nf4"),
 ]
 
 
