@@ -152,9 +152,12 @@ const char *e4b_status_str(int32_t status);
 
 /* Bytes of caller-owned device workspace that e4b_moe_fwd / e4b_moe_dgrad /
  * e4b_lora_wgrad need for this layer (adapters may be NULL).  Host call, no device work;
- * bad shapes or adapters give E4B_ERR_INVALID_ARG and leave *bytes untouched.  (The
- * workspace is this library's own contract: the pages leave memory management to the
- * caller's framework.) */
+ * bad shapes or adapters give E4B_ERR_INVALID_ARG and leave *bytes untouched.  With
+ * E4B_TRAIN it includes 64 MiB + 8 KiB of partial tiles and arrival counters for the K-split
+ * of the last round of the large down and input-gradient GEMMs (the training forward zeroes
+ * the counters; every call leaves them zero).  Calls on one workspace must be ordered on
+ * one stream.  (The workspace is this library's own contract: the pages leave memory
+ * management to the caller's framework.) */
 e4b_status e4b_moe_workspace_size(const e4b_moe_desc *desc, const e4b_lora *l_gu,
                                   const e4b_lora *l_dn, size_t *bytes);
 
