@@ -322,14 +322,22 @@ __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint16_t v, u
 __device__ __forceinline__ void bstore32(__amdgpu_buffer_rsrc_t r, float v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, 0, 0);
 }
+// Lane pairs: lanes 2m and 2m+1 trade a dword (DPP quad_perm [1,0,3,2]; every lane of the
+// wave is active here, so no lane keeps an old value).
+__device__ __forceinline__ uint32_t lane_swap1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
 // Two bf16 outputs per 4-byte store.  In the MFMA accumulator layout a lane holds one
 // column; lanes 2m and 2m+1 hold columns c and c+1 of the same rows.  x0 and x1 are this
-// lane's values of rows r and r+1: one lane swap (DPP quad_perm [1,0,3,2]) gives the even
-// lane row r at columns (c, c+1) and the odd lane row r+1 at columns (c-1, c).
+// lane's values of rows r and r+1, rounded to bf16 as one dword (row r low); after the swap
+// one byte permute gives the even lane row r at columns (c, c+1) and the odd lane row r+1
+// at columns (c-1, c).  The permute is its own inverse on the pairs (unpair_bf16_f32).
+__device__ __forceinline__ uint32_t pair_perm(uint32_t mine, bool odd) {
+  // v_perm_b32 bytes 0-3 select from the second operand, 4-7 from the first
+  return __builtin_amdgcn_perm(lane_swap1(mine), mine, odd ? 0x03020706u : 0x05040100u);
+}
 __device__ __forceinline__ uint32_t pair_bf16(float x0, float x1, bool odd) {
-  const float send = odd ? x0 : x1;
-  const float recv = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, false));
-  return pack_bf16x2(odd ? recv : x0, odd ? x1 : recv);
+  return pair_perm(pack_bf16x2(x0, x1), odd);
 }
 // The tile epilogues' outputs (h, G, O, dG, dXp) are each larger than the last-level cache
 // and are read back only by later kernels: their stores carry the non-temporal hint (cache
@@ -337,9 +345,6 @@ __device__ __forceinline__ uint32_t pair_bf16(float x0, float x1, bool odd) {
 constexpr int EPI_STORE_CPOL = 2;
 __device__ __forceinline__ void bstore32u(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, 0, EPI_STORE_CPOL);
-}
-__device__ __forceinline__ uint32_t lane_swap1(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
 }
 // The same pairing for fp32 outputs: two columns per 8-byte store.
 __device__ __forceinline__ void bstore_pair_f32(__amdgpu_buffer_rsrc_t r, float x0, float x1, bool odd,
@@ -351,12 +356,11 @@ __device__ __forceinline__ void bstore_pair_f32(__amdgpu_buffer_rsrc_t r, float 
   __builtin_amdgcn_raw_buffer_store_b64(d, r, (int)voff, 0, EPI_STORE_CPOL);
 }
 // The inverse for loads: the even lane loaded row r and the odd lane row r+1, each as the
-// dword of columns (c, c+1) of its pair; returns this lane's column at rows r (lo) and r+1
-// (hi), as bf16 bits.
-__device__ __forceinline__ void unpair_bf16(uint32_t d, bool odd, uint32_t &r0, uint32_t &r1) {
-  const uint32_t recv = lane_swap1(odd ? (d & 0xffffu) : (d >> 16));
-  r0 = odd ? recv : (d & 0xffffu);
-  r1 = odd ? (d >> 16) : recv;
+// dword of columns (c, c+1) of its pair; gives this lane's column at rows r and r+1 as fp32.
+__device__ __forceinline__ void unpair_bf16_f32(uint32_t d, bool odd, float &f0, float &f1) {
+  const uint32_t x = pair_perm(d, odd);  // rows r (low) and r+1 (high) of this lane's column
+  f0 = __uint_as_float(x << 16);
+  f1 = __uint_as_float(x & 0xffff0000u);
 }
 
 // Buffer over rows row0 .. row0 + rows - 1 of a row-major matrix with ld elements of esize

@@ -533,13 +533,13 @@ __device__ __forceinline__ void large_epilogue(LMma &mma, const GroupedArgs &g, 
 #pragma unroll
         for (int v = 0; v < 16; v += 2) {
           const uint32_t o = off + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * pitch;
-          uint32_t g0, g1, u0, u1;
-          unpair_bf16(gd[v / 2], odd, g0, g1);
-          unpair_bf16(ud[v / 2], odd, u0, u1);
+          float g0, g1, u0, u1;
+          unpair_bf16_f32(gd[v / 2], odd, g0, g1);
+          unpair_bf16_f32(ud[v / 2], odd, u0, u1);
           float dg[2], du[2];
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const float dh = mma.acc[i][j][v + q], gt = bf2f((uint16_t)(q ? g1 : g0)), up = bf2f((uint16_t)(q ? u1 : u0));
+            const float dh = mma.acc[i][j][v + q], gt = q ? g1 : g0, up = q ? u1 : u0;
             const float sg = sigmoid_fast(gt);
             dg[q] = dh * up * sg * (1.0f + gt * (1.0f - sg));
             du[q] = dh * gt * sg;
