@@ -69,7 +69,8 @@ __device__ __forceinline__ bool find_tile_wave(const int32_t *__restrict__ off, 
   int base = 0;
   for (int c = 0; c < E; c += 64) {
     const int ee = c + lane;
-    const int cnt = ee < E ? off[ee + 1] - off[ee] : 0;
+    const int o0 = ee < E ? off[ee] : 0;
+    const int cnt = ee < E ? off[ee + 1] - o0 : 0;
     const int nt = (cnt + BMt - 1) / BMt;
     int incl = nt;
 #pragma unroll
@@ -85,7 +86,7 @@ __device__ __forceinline__ bool find_tile_wave(const int32_t *__restrict__ off, 
       const int mt = slot - base - __builtin_amdgcn_readfirstlane(__shfl(excl, src));
       const int n = __builtin_amdgcn_readfirstlane(__shfl(cnt, src));
       t.e = e;
-      t.row0 = __builtin_amdgcn_readfirstlane(off[e]) + mt * BMt;
+      t.row0 = __builtin_amdgcn_readfirstlane(__shfl(o0, src)) + mt * BMt;  // no second load
       t.rows = min(BMt, n - mt * BMt);
       return true;
     }
