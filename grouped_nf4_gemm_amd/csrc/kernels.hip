@@ -21,7 +21,7 @@ __constant__ float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 // walks each range in order, ranking equal expert ids inside a wave64 by the
 // lanes below them (bitwise key match from ballots), which keeps the grouping
 // stable in the flat index t*k + j.
-constexpr int RT_WAVES = 16;
+constexpr int RT_WAVES = 16, RT_BATCH = 8;
 
 __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(const int32_t *__restrict__ ids, int M,
                                                               int E, int32_t *__restrict__ cnt,
@@ -39,9 +39,23 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(const int32_t *__r
   __syncthreads();
   const int S = (((M + RT_WAVES - 1) / RT_WAVES) + 63) & ~63;
   const int f0 = min(M, w * S), f1 = min(M, f0 + S);
-  for (int f = f0 + lane; f < f1; f += 64) {
-    const int e = ids[f];
-    atomicAdd(&wc[w * KE + ((e >= 0 && e < E) ? e : E)], 1);
+  // the ids of RT_BATCH 64-wide chunks are loaded together, so a wave waits for memory
+  // once per batch rather than once per chunk
+  int ev[RT_BATCH];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < RT_BATCH; ++u) {
+      const int f = c0 + 64 * u + lane;
+      ev[u] = f < f1 ? ids[f] : 0;
+    }
+  };
+  for (int c0 = f0; c0 < f1; c0 += 64 * RT_BATCH) {
+    load_batch(c0);
+#pragma unroll
+    for (int u = 0; u < RT_BATCH; ++u) {
+      const int e = ev[u];
+      if (c0 + 64 * u + lane < f1) atomicAdd(&wc[w * KE + ((e >= 0 && e < E) ? e : E)], 1);
+    }
   }
   __syncthreads();
   for (int key = tid; key < KE; key += blockDim.x) {
@@ -75,28 +89,32 @@ __global__ __launch_bounds__(RT_WAVES * 64) void route_kernel(const int32_t *__r
   for (int e = tid; e < KE; e += blockDim.x) off[e] = soff[e];
   const int nbits = 32 - __clz(E);
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = f0; c0 < f1; c0 += 64) {
-    const int f = c0 + lane;
-    const bool act = f < f1;
-    const int e = act ? ids[f] : 0;
-    const bool valid = act && e >= 0 && e < E;
-    const int key = valid ? e : E;
-    uint64_t eq = __ballot(act);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      eq &= bit ? m : ~m;
+  for (int cb = f0; cb < f1; cb += 64 * RT_BATCH) {
+    load_batch(cb);
+#pragma unroll
+    for (int u = 0; u < RT_BATCH; ++u) {
+      const int f = cb + 64 * u + lane;
+      const bool act = f < f1;
+      const int e = ev[u];
+      const bool valid = act && e >= 0 && e < E;
+      const int key = valid ? e : E;
+      uint64_t eq = __ballot(act);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        eq &= bit ? m : ~m;
+      }
+      const int rank = __popcll(eq & lt);
+      const int total = __popcll(eq);
+      if (valid) {
+        const int pos = soff[e] + wc[w * KE + e] + rank;
+        perm[pos] = f;
+        inv[f] = pos;
+      } else if (act) {
+        inv[f] = -1;
+      }
+      if (valid && rank == 0) wc[w * KE + e] += total;
     }
-    const int rank = __popcll(eq & lt);
-    const int total = __popcll(eq);
-    if (valid) {
-      const int pos = soff[e] + wc[w * KE + e] + rank;
-      perm[pos] = f;
-      inv[f] = pos;
-    } else if (act) {
-      inv[f] = -1;
-    }
-    if (valid && rank == 0) wc[w * KE + e] += total;
   }
   for (int p = soff[E] + tid; p < M; p += blockDim.x) perm[p] = -1;
 }
