@@ -213,9 +213,12 @@ static int splits_for(int64_t wgs, int64_t slabs) {
   int sp = (int)std::min<int64_t>(SPLIT_MAX, std::max<int64_t>(1, (SPLIT_TARGET_WGS + wgs - 1) / std::max<int64_t>(1, wgs)));
   return (int)std::max<int64_t>(1, std::min<int64_t>(sp, slabs / 4));
 }
+// LoRA-A: also at most 64 slabs per split, so that a long reduction (K = 2I in the
+// backward) is not left to one workgroup per row tile and split.
 int lora_a_splits(int M, int E, int N, int K) {
   if (M == 0) return 1;
-  return splits_for((int64_t)cdiv(N, 64) * (cdiv(M, 128) + E), K / BK);
+  const int sp = splits_for((int64_t)cdiv(N, 64) * (cdiv(M, 128) + E), K / BK);
+  return std::max(sp, (int)std::min<int64_t>(SPLIT_MAX, std::max(1, cdiv(K / BK, 64))));
 }
 // Upper bound on the splits of one expert's weight-gradient reduction; each expert takes
 // as many as its own rows fill (wgrad_expert_splits).  With many experts the routed rows are
@@ -225,7 +228,10 @@ int lora_a_splits(int M, int E, int N, int K) {
 int wgrad_splits(int M, int E, int Na, int Nb) {
   if (M == 0 || E == 0) return 1;
   const int64_t tiles = Nb <= 64 ? (int64_t)cdiv(Nb, 64) * cdiv(Na, 128) : (int64_t)cdiv(Nb, 128) * cdiv(Na, 64);
-  int sp = splits_for(tiles * E, (int64_t)M / E / BK);
+  // short-wide tiles (rank rows x 128 weight columns) reach the memory rate only with
+  // about three times as many workgroups in flight
+  const int64_t wgs = Nb <= 64 ? tiles * E : tiles * E * SPLIT_TARGET_WGS / 3072;
+  int sp = splits_for(wgs, (int64_t)M / E / BK);
   if (E >= 32) {
     const int64_t per = (int64_t)E * Na * Nb * 4;
     sp = std::max(sp, (int)std::min<int64_t>(SPLIT_MAX, std::max<int64_t>(1, ((int64_t)256 << 20) / per)));
