@@ -113,6 +113,20 @@ def test_deterministic_and_duplicate_rows():
     assert torch.equal(a["dx"][7].view(torch.int16), a["dx"][3].view(torch.int16))
 
 
+def test_split_weight_gradients():
+    """Weight gradients of two heavily routed experts split four ways (fp32 partial sums added
+    in split order) and of two rarely routed ones not split: oracle parity on every row, and
+    the same bits on a second call."""
+    inp = synth.make_inputs(synth.custom(4, 256, 256, 2048, 2, 16, 32.0), seed=21)
+    inp.ids[:1800] = np.array([0, 1], dtype=inp.ids.dtype)
+    case = Case(inp)
+    a = case.run()
+    _check_all(case, a)
+    b = case.run()
+    for k in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
+        assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
+
+
 def test_empty_experts_and_skew():
     """All tokens on one expert of four: the other experts' LoRA grads are exactly 0."""
     inp = synth.make_inputs(synth.custom(4, 128, 128, 90, 2, 8, 16.0), seed=17)
