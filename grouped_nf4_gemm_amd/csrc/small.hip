@@ -281,11 +281,13 @@ __device__ __forceinline__ void z2_reduce(const GroupedArgs &g, int row0, int ro
 // The workgroup barrier orders every thread's stores before thread 0's device-scope release
 // fence, and thread 0's acquire fence before every thread's loads: one fence per workgroup
 // (each one writes back or invalidates caches of the whole cache level).
-__device__ __forceinline__ void arrive_combine(const GroupedArgs &g, int c0, int c1, int *flag) {
+// A workgroup that stored nothing (an empty slot) arrives without the release fence: the
+// counter's read-modify-writes carry the release of the workgroups before it.
+__device__ __forceinline__ void arrive_combine(const GroupedArgs &g, int c0, int c1, int *flag, bool stored = true) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const int total = (int)(gridDim.y * gridDim.z);
-    __threadfence();
+    if (stored) __threadfence();
     const bool last = atomicAdd(&g.fz.ctr[blockIdx.x], 1) == total - 1;
     if (last) __threadfence();
     *flag = last;
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_gemm_kernel(GroupedArgs g, i
   }
   TileM tm;
   if (!find_tile_wave(offp, g.E, SM_BMT, blockIdx.y, tm)) {  // the same for every wave
-    if constexpr (FDN) arrive_combine(g, blockIdx.x * SM_WAVES * 32, (blockIdx.x + 1) * SM_WAVES * 32, (int *)&xs);
+    if constexpr (FDN) arrive_combine(g, blockIdx.x * SM_WAVES * 32, (blockIdx.x + 1) * SM_WAVES * 32, (int *)&xs, false);
     return;
   }
   const int e = tm.e;
@@ -790,7 +792,7 @@ __global__ __launch_bounds__(SM_THREADS) void small_direct_kernel(GroupedArgs g,
   }
   TileM tm;
   if (!find_tile_wave(offp, g.E, XMAX, blockIdx.y, tm)) {  // the same for every wave
-    if constexpr (FDN) arrive_combine(g, blockIdx.x * nseq * SM_WAVES * 32, (blockIdx.x + 1) * nseq * SM_WAVES * 32, (int *)small_lds);
+    if constexpr (FDN) arrive_combine(g, blockIdx.x * nseq * SM_WAVES * 32, (blockIdx.x + 1) * nseq * SM_WAVES * 32, (int *)small_lds, false);
     return;
   }
   const int e = tm.e;
