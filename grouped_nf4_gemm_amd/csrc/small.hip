@@ -278,18 +278,19 @@ __device__ __forceinline__ void z2_reduce(const GroupedArgs &g, int row0, int ro
 // gridDim.z workgroups forms y there, as the combine kernel does: y[t][c] =
 // bf16(sum_j w[t,j] * (sum over splits of O[s][inv[t,j]][c])), splits then choices in order.
 // flag: one int of LDS.  Every wave of the workgroup calls it once.
-// The workgroup barrier orders every thread's stores before thread 0's device-scope release
-// fence, and thread 0's acquire fence before every thread's loads: one fence per workgroup
-// (each one writes back or invalidates caches of the whole cache level).
+// The workgroup barrier orders every thread's stores before thread 0's agent-scope release
+// fence (an L2 writeback), and the last workgroup's acquire fence (an L2 invalidate) before
+// every thread's loads: one fence per workgroup and side, not a full fence (which would do
+// both on every workgroup).
 // A workgroup that stored nothing (an empty slot) arrives without the release fence: the
 // counter's read-modify-writes carry the release of the workgroups before it.
 __device__ __forceinline__ void arrive_combine(const GroupedArgs &g, int c0, int c1, int *flag, bool stored = true) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const int total = (int)(gridDim.y * gridDim.z);
-    if (stored) __threadfence();
+    if (stored) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const bool last = atomicAdd(&g.fz.ctr[blockIdx.x], 1) == total - 1;
-    if (last) __threadfence();
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *flag = last;
   }
   __syncthreads();
