@@ -1085,8 +1085,9 @@ __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
     if (s + 1 < s1) fetch(s + 1);
     mma_ktiles(mma, As, Bs, 4);
   }
-  // every split of the expert writes its (possibly zero) partial sums
-  float *C = g.nsplit > 1 ? g.part + ((int64_t)sp * g.E + e) * g.Na * g.Nb : g.C + (int64_t)e * g.Na * g.Nb;
+  // every split of the expert writes its (possibly zero) partial sums; an expert that takes
+  // one split writes C itself (the reduction leaves it alone)
+  float *C = nsplit_e > 1 ? g.part + ((int64_t)sp * g.E + e) * g.Na * g.Nb : g.C + (int64_t)e * g.Na * g.Nb;
   mma.for_each([&](int row, int col, float v) {
     const int a = a0 + row, b = b0 + col;
     if (a < g.Na && b < g.Nb) C[(int64_t)a * g.Nb + b] = v;
@@ -1094,7 +1095,7 @@ __global__ __launch_bounds__(NTHREADS) void wgrad_kernel(WgradArgs g) {
 }
 
 // C[e] = the sum of expert e's own splits of the partial sums [nsplit][E][Na * Nb], in split
-// order.
+// order, for the experts that take more than one split (the others wrote C directly).
 __global__ void wgrad_reduce_kernel(const float *__restrict__ part, const int32_t *__restrict__ off, int nsplit,
                                     int64_t per_expert, int E, float *__restrict__ C) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1102,6 +1103,7 @@ __global__ void wgrad_reduce_kernel(const float *__restrict__ part, const int32_
   if (i >= n) return;
   const int e = (int)(i / per_expert);
   const int ns = wgrad_expert_splits(off[e + 1] - off[e], nsplit);
+  if (ns == 1) return;
   float acc = part[i];
   for (int s2 = 1; s2 < ns; ++s2) acc += part[s2 * n + i];
   C[i] = acc;
